@@ -1,0 +1,282 @@
+"""Python binding of libagmm (all-gather fused matmul for MI355X / gfx950).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of libagmm.so.  There is no CPU or PyTorch fallback; if the library is
+missing or fails to load, every entry point raises.
+
+The functions below carry the names of the C ABI in include/agmm.h and take
+plain integers (device addresses, sizes, stream handles).  `Plan` is a small
+convenience wrapper that takes torch tensors on the GPU and the current torch
+stream.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libagmm.so")
+
+AGMM_BF16, AGMM_FP16, AGMM_FP32 = 0, 1, 2
+AGMM_OK, AGMM_ERR_INVALID_ARG, AGMM_ERR_UNSUPPORTED, AGMM_ERR_OOM, AGMM_ERR_HIP = 0, 1, 2, 3, 4
+(AGMM_VARIANT_AUTO, AGMM_VARIANT_FUSED, AGMM_VARIANT_STAGED, AGMM_VARIANT_UNFUSED,
+ AGMM_VARIANT_SKINNY) = 0, 1, 2, 3, 4
+VARIANTS = {"auto": 0, "fused": 1, "staged": 2, "unfused": 3, "skinny": 4}
+VARIANT_NAMES = {v: k for k, v in VARIANTS.items()}
+
+# (name, restype, argtypes) of every symbol include/agmm.h declares.
+_vp, _i64, _ci, _cc = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_char_p
+EXPORTS = [
+    ("agmm_plan_validate", _ci, [_ci, _i64, _i64, _i64, _ci, _ci]),
+    ("agmm_plan_create", _vp, [_ci, _i64, _i64, _i64, _ci, _ci]),
+    ("agmm_run", _ci, [_vp, ctypes.POINTER(_vp), _vp, _vp, _vp]),
+    ("agmm_gather", _ci, [_vp, ctypes.POINTER(_vp), _vp, _vp]),
+    ("agmm_run_gathered", _ci, [_vp, _vp, _vp, _vp, _vp]),
+    ("agmm_plan_set_int", _ci, [_vp, _cc, _i64]),
+    ("agmm_plan_get_int", _ci, [_vp, _cc, ctypes.POINTER(_i64)]),
+    ("agmm_plan_workspace_bytes", ctypes.c_size_t, [_vp]),
+    ("agmm_plan_slot_ptr", _vp, [_vp, _ci]),
+    ("agmm_plan_tile_order", _ci, [_vp, _ci, ctypes.POINTER(ctypes.c_int32), _ci]),
+    ("agmm_plan_timing_begin", _ci, [_vp]),
+    ("agmm_plan_timing_read", _ci, [_vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_i64)]),
+    ("agmm_plan_timing_end", _ci, [_vp]),
+    ("agmm_plan_destroy", None, [_vp]),
+    ("agmm_last_status", _ci, []),
+    ("agmm_last_error", _cc, []),
+    ("agmm_version", _cc, []),
+]
+
+_lib = None
+
+
+class AgmmError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"agmm error {status}: {message}")
+        self.status = status
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libagmm.so (raises if it is missing: there is no fallback)."""
+    global _lib
+    if _lib is not None and path == LIB_PATH:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build it with `python -m all_gather_gemm_agmm_amd._build` "
+            "(or __graft_entry__.build()); the all-gather matmul has no CPU fallback")
+    lib = ctypes.CDLL(path)
+    for name, res, args in EXPORTS:
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    if path == LIB_PATH:
+        _lib = lib
+    return lib
+
+
+def _check(status: int) -> int:
+    if status != AGMM_OK:
+        lib = load_library()
+        raise AgmmError(status, lib.agmm_last_error().decode())
+    return status
+
+
+def _ptr_table(ptrs: Sequence[int]):
+    return (ctypes.c_void_p * len(ptrs))(*[ctypes.c_void_p(int(p)) for p in ptrs])
+
+
+# ---------------------------------------------------------------- raw C ABI
+def agmm_plan_validate(num_shards, m_per_shard, k, n_local, dtype, rhs_transpose) -> int:
+    return load_library().agmm_plan_validate(num_shards, m_per_shard, k, n_local, dtype,
+                                             int(bool(rhs_transpose)))
+
+
+def agmm_plan_create(num_shards, m_per_shard, k, n_local, dtype, rhs_transpose) -> int:
+    lib = load_library()
+    h = lib.agmm_plan_create(num_shards, m_per_shard, k, n_local, dtype, int(bool(rhs_transpose)))
+    if not h:
+        raise AgmmError(lib.agmm_last_status(), lib.agmm_last_error().decode())
+    return h
+
+
+def agmm_run(plan, shard_ptrs: Sequence[int], B: int, C: int, stream: int) -> int:
+    return _check(load_library().agmm_run(plan, _ptr_table(shard_ptrs), B, C, stream))
+
+
+def agmm_gather(plan, shard_ptrs: Sequence[int], gathered: int, stream: int) -> int:
+    return _check(load_library().agmm_gather(plan, _ptr_table(shard_ptrs), gathered, stream))
+
+
+def agmm_run_gathered(plan, gathered: int, B: int, C: int, stream: int) -> int:
+    return _check(load_library().agmm_run_gathered(plan, gathered, B, C, stream))
+
+
+def agmm_plan_set_int(plan, key: str, value: int) -> int:
+    return _check(load_library().agmm_plan_set_int(plan, key.encode(), int(value)))
+
+
+def agmm_plan_get_int(plan, key: str) -> int:
+    v = ctypes.c_int64(0)
+    _check(load_library().agmm_plan_get_int(plan, key.encode(), ctypes.byref(v)))
+    return int(v.value)
+
+
+def agmm_plan_workspace_bytes(plan) -> int:
+    return int(load_library().agmm_plan_workspace_bytes(plan))
+
+
+def agmm_plan_slot_ptr(plan, slot: int) -> int:
+    return int(load_library().agmm_plan_slot_ptr(plan, slot) or 0)
+
+
+def agmm_plan_tile_order(plan, chunk: int = 0):
+    # Chunk 0 is never smaller than a later (clamped) chunk.
+    cap = max(agmm_plan_get_int(plan, "num_row_blocks"), 1)
+    buf = (ctypes.c_int32 * cap)()
+    got = load_library().agmm_plan_tile_order(plan, chunk, buf, cap)
+    if got < 0:
+        raise AgmmError(agmm_last_status(), agmm_last_error())
+    return [int(buf[i]) for i in range(got)]
+
+
+def agmm_plan_timing_begin(plan) -> int:
+    return _check(load_library().agmm_plan_timing_begin(plan))
+
+
+def agmm_plan_timing_read(plan):
+    ms, n = ctypes.c_double(0.0), ctypes.c_int64(0)
+    _check(load_library().agmm_plan_timing_read(plan, ctypes.byref(ms), ctypes.byref(n)))
+    return float(ms.value), int(n.value)
+
+
+def agmm_plan_timing_end(plan) -> int:
+    return _check(load_library().agmm_plan_timing_end(plan))
+
+
+def agmm_plan_destroy(plan) -> None:
+    if plan:
+        load_library().agmm_plan_destroy(plan)
+
+
+def agmm_last_status() -> int:
+    return int(load_library().agmm_last_status())
+
+
+def agmm_last_error() -> str:
+    return load_library().agmm_last_error().decode()
+
+
+def agmm_version() -> str:
+    return load_library().agmm_version().decode()
+
+
+# ------------------------------------------------------- torch convenience
+def _torch_dtype(dtype: int):
+    import torch
+    return {AGMM_BF16: torch.bfloat16, AGMM_FP16: torch.float16, AGMM_FP32: torch.float32}[dtype]
+
+
+def _stream_handle(stream) -> int:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream)
+
+
+class Plan:
+    """A plan bound to torch tensors.  All checks here are host-side shape,
+    dtype and device checks; the computation is the library's."""
+
+    def __init__(self, num_shards: int, m_per_shard: int, k: int, n_local: int, dtype: int,
+                 rhs_transpose: bool, **settings):
+        self.num_shards, self.m_per_shard, self.k, self.n_local = num_shards, m_per_shard, k, n_local
+        self.dtype, self.rhs_transpose = dtype, bool(rhs_transpose)
+        self.handle = agmm_plan_create(num_shards, m_per_shard, k, n_local, dtype, rhs_transpose)
+        for key, val in settings.items():
+            if val is not None:
+                self.set(key, VARIANTS[val] if key == "variant" and isinstance(val, str) else val)
+
+    @property
+    def m(self) -> int:
+        return self.num_shards * self.m_per_shard
+
+    def set(self, key: str, value: int) -> None:
+        agmm_plan_set_int(self.handle, key, value)
+
+    def get(self, key: str) -> int:
+        return agmm_plan_get_int(self.handle, key)
+
+    def _check_tensor(self, t, shape, name):
+        import torch
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor")
+        if t.device.type != "cuda":
+            raise ValueError(f"{name} must be on the GPU")
+        if t.dtype != _torch_dtype(self.dtype):
+            raise TypeError(f"{name} has dtype {t.dtype}, plan expects {_torch_dtype(self.dtype)}")
+        if tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous (row-major)")
+
+    def b_shape(self):
+        return (self.n_local, self.k) if self.rhs_transpose else (self.k, self.n_local)
+
+    def run(self, shards, B, C=None, stream=None):
+        import torch
+        if len(shards) != self.num_shards:
+            raise ValueError(f"expected {self.num_shards} shards, got {len(shards)}")
+        for r, s in enumerate(shards):
+            self._check_tensor(s, (self.m_per_shard, self.k), f"shards[{r}]")
+        self._check_tensor(B, self.b_shape(), "B")
+        if C is None:
+            C = torch.empty((self.m, self.n_local), dtype=_torch_dtype(self.dtype), device=B.device)
+        self._check_tensor(C, (self.m, self.n_local), "C")
+        agmm_run(self.handle, [s.data_ptr() for s in shards], B.data_ptr(), C.data_ptr(),
+                 _stream_handle(stream))
+        return C
+
+    def gather(self, shards, out=None, stream=None):
+        import torch
+        for r, s in enumerate(shards):
+            self._check_tensor(s, (self.m_per_shard, self.k), f"shards[{r}]")
+        if out is None:
+            out = torch.empty((self.m, self.k), dtype=_torch_dtype(self.dtype), device=shards[0].device)
+        self._check_tensor(out, (self.m, self.k), "gathered")
+        agmm_gather(self.handle, [s.data_ptr() for s in shards], out.data_ptr(), _stream_handle(stream))
+        return out
+
+    def run_gathered(self, gathered, B, C=None, stream=None):
+        import torch
+        self._check_tensor(gathered, (self.m, self.k), "gathered")
+        self._check_tensor(B, self.b_shape(), "B")
+        if C is None:
+            C = torch.empty((self.m, self.n_local), dtype=_torch_dtype(self.dtype), device=B.device)
+        self._check_tensor(C, (self.m, self.n_local), "C")
+        agmm_run_gathered(self.handle, gathered.data_ptr(), B.data_ptr(), C.data_ptr(),
+                          _stream_handle(stream))
+        return C
+
+    def tile_order(self, chunk: int = 0):
+        return agmm_plan_tile_order(self.handle, chunk)
+
+    def workspace_bytes(self) -> int:
+        return agmm_plan_workspace_bytes(self.handle)
+
+    def close(self) -> None:
+        if getattr(self, "handle", None):
+            agmm_plan_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()

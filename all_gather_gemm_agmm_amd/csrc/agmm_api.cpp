@@ -1,0 +1,751 @@
+// C ABI, plan and scheduler of the all-gather matmul library (host side).
+//
+// The plan validates the problem (the tpu-inference page's `validate_inputs`
+// raises on malformed inputs; here every rejection is a status code plus a
+// message), picks tile shapes and the variant, and owns everything a run
+// needs: the staged ring, split-K scratch, tile-order tables, a second
+// stream and the events that sequence it.
+//
+// Staged pipeline (the single-GPU form of the Ascend tutorial's "Double
+// Buffering" and "pvalue Parameter" sections): chunk c holds rows
+// [c*R, (c+1)*R) of every shard (R = pvalue * tile rows, the last chunk
+// clamped), laid out in slot c % nbuf as [num_shards][R][k].  The copy of
+// chunk c runs on the plan's copy stream once the GEMM that last read its
+// slot has finished (event `free`); the GEMM of chunk c runs on the caller's
+// stream once the copy is done (event `ready`).  These two events per slot
+// take the place of the tutorial's barrier_all per chunk and of the
+// semaphores of the tpu-inference kernel.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "agmm.h"
+#include "agmm_kernels.h"
+
+namespace {
+
+thread_local int g_status = AGMM_OK;
+thread_local std::string g_msg;
+
+int set_err(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_status = status;
+  g_msg = buf;
+  return status;
+}
+
+int ok() {
+  g_status = AGMM_OK;
+  g_msg.clear();
+  return AGMM_OK;
+}
+
+int hip_err(hipError_t e, const char* what) {
+  return set_err(AGMM_ERR_HIP, "%s failed: %s", what, hipGetErrorString(e));
+}
+
+constexpr int64_t kDimLimit = int64_t(1) << 30;
+constexpr int kTimingPairs = 4096;
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+size_t elem_bytes(int dtype) { return dtype == AGMM_FP32 ? 4 : 2; }
+
+int validate(int N, int64_t m_s, int64_t k, int64_t n, int dtype, int rt) {
+  if (N < 1) return set_err(AGMM_ERR_INVALID_ARG, "num_shards must be >= 1 (got %d)", N);
+  if (N > agmm::kMaxGroups)
+    return set_err(AGMM_ERR_UNSUPPORTED, "num_shards %d exceeds the supported maximum %d", N,
+                   agmm::kMaxGroups);
+  if (m_s < 1 || k < 1 || n < 1)
+    return set_err(AGMM_ERR_INVALID_ARG,
+                   "sizes must be >= 1 (m_per_shard=%lld, k=%lld, n_local=%lld)", (long long)m_s,
+                   (long long)k, (long long)n);
+  if (dtype != AGMM_BF16 && dtype != AGMM_FP16 && dtype != AGMM_FP32)
+    return set_err(AGMM_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+  if (rt != 0 && rt != 1) return set_err(AGMM_ERR_INVALID_ARG, "rhs_transpose must be 0 or 1");
+  const int64_t m = (int64_t)N * m_s;
+  if (m >= kDimLimit || k >= kDimLimit || n >= kDimLimit || m * k >= (int64_t(1) << 40) ||
+      k * n >= (int64_t(1) << 40) || m * n >= (int64_t(1) << 40))
+    return set_err(AGMM_ERR_UNSUPPORTED, "problem too large (m=%lld, k=%lld, n=%lld)",
+                   (long long)m, (long long)k, (long long)n);
+  if (dtype != AGMM_FP32) {
+    if (k % 8 != 0)
+      return set_err(AGMM_ERR_UNSUPPORTED,
+                     "bf16/fp16 need k %% 8 == 0 (16-byte rows); got k=%lld", (long long)k);
+    if (!rt && n % 8 != 0)
+      return set_err(AGMM_ERR_UNSUPPORTED,
+                     "bf16/fp16 with B stored k x n need n_local %% 8 == 0; got %lld",
+                     (long long)n);
+  }
+  return ok();
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace
+
+struct agmm_plan {
+  // problem
+  int device = 0;
+  int cu_count = 256;
+  int N = 0;
+  int64_t m_s = 0, k = 0, n = 0, m = 0;
+  int dtype = 0;
+  int rt = 0;
+  // settings
+  int variant = AGMM_VARIANT_AUTO;
+  int pvalue = 2;
+  int nbuf = 2;
+  int tile = -1;  // -1: auto
+  int splits = 0; // 0: auto
+  int local_shard = 0;
+  int order = 0;
+  int group_m = 8;
+  int xcd_remap = 1;
+  int copy_wgs = 0;
+  int debug_keep_slots = 0;
+  // derived
+  int variant_used = AGMM_VARIANT_FUSED;
+  int tile_used = agmm::kTile256x256;
+  int bm = 256, bn = 256;
+  int64_t rows_per_chunk = 0;
+  int num_chunks = 1;
+  int nslots = 0;
+  int splits_used = 1;
+  int64_t k_per_split = 0;
+  // device resources
+  char* ws = nullptr;
+  size_t ws_bytes = 0;
+  char* ring = nullptr;
+  size_t slot_bytes = 0;
+  float* partials = nullptr;
+  int32_t* counters = nullptr;
+  int32_t* d_order = nullptr;
+  std::vector<int32_t> h_order;     // concatenated per-chunk orders
+  std::vector<int64_t> order_off;   // offset of chunk c's table
+  std::vector<int32_t> order_len;
+  hipStream_t copy_stream = nullptr;
+  hipEvent_t ev_entry = nullptr;
+  std::vector<hipEvent_t> ev_ready, ev_free;
+  // timing
+  bool timing = false;
+  std::vector<hipEvent_t> tev;  // 2 * kTimingPairs
+  int tev_used = 0;
+  std::mutex mu;
+};
+
+namespace {
+
+bool is_f32(const agmm_plan* p) { return p->dtype == AGMM_FP32; }
+
+// Tile choice for the MFMA path: fewest "tile waves" weighted by the
+// per-tile efficiency of the larger shapes.
+int choose_tile(const agmm_plan* p, int64_t m) {
+  if (p->tile >= 0) return p->tile;
+  struct Cand { int cfg; double eff; };
+  const Cand cands[] = {{agmm::kTile256x256, 1.0}, {agmm::kTile256x128, 0.9},
+                        {agmm::kTile128x128, 0.8}};
+  int best = agmm::kTile256x256;
+  double best_cost = 1e300;
+  for (const Cand& c : cands) {
+    const int64_t bm = agmm::tile_bm(c.cfg), bn = agmm::tile_bn(c.cfg);
+    const int64_t tiles = cdiv(m, bm) * cdiv(p->n, bn);
+    const int64_t waves = cdiv(tiles, p->cu_count);
+    const double cost = (double)waves * (double)(bm * bn) / c.eff;
+    if (cost < best_cost * 0.999) {
+      best_cost = cost;
+      best = c.cfg;
+    }
+  }
+  return best;
+}
+
+// Row-block visit order for a launch covering `groups` groups of `rpg` rows
+// each, whose position t inside a group is shard row `row_off + t`.
+void ring_order(const agmm_plan* p, int64_t rpg, int64_t row_off, int bm, int order_mode,
+                std::vector<int32_t>& out) {
+  const int64_t rows = rpg * p->N;
+  const int64_t nrb = cdiv(rows, bm);
+  out.resize(nrb);
+  for (int64_t b = 0; b < nrb; ++b) out[b] = (int32_t)b;
+  if (order_mode != 0 || p->N == 1) return;
+  const int64_t half = (p->m_s + 1) / 2;  // first half of a shard: rows [0, half)
+  std::vector<int64_t> key(nrb, 0);
+  const int64_t N = p->N, r0 = p->local_shard;
+  for (int64_t b = 0; b < nrb; ++b) {
+    int64_t kmax = -1;
+    const int64_t lo = b * bm, hi = std::min(rows, lo + bm);
+    for (int64_t i = lo; i < hi; ++i) {
+      const int64_t g = i / rpg;
+      const int64_t t = row_off + (i - g * rpg);
+      const bool top = t < half;
+      const int64_t step = top ? ((g - r0) % N + N) % N : ((r0 - g) % N + N) % N;
+      kmax = std::max(kmax, 2 * step + (top ? 0 : 1));
+    }
+    key[b] = kmax;
+  }
+  std::stable_sort(out.begin(), out.end(), [&](int32_t a, int32_t b) { return key[a] < key[b]; });
+}
+
+void free_resources(agmm_plan* p) {
+  if (p->ws) hipFree(p->ws);
+  p->ws = nullptr;
+  p->ws_bytes = 0;
+  p->ring = nullptr;
+  p->partials = nullptr;
+  p->counters = nullptr;
+  p->d_order = nullptr;
+}
+
+// (Re)derive everything from the settings and (re)allocate the workspace.
+int configure(agmm_plan* p) {
+  const int64_t e = elem_bytes(p->dtype);
+  // variant
+  int v = p->variant;
+  if (v == AGMM_VARIANT_AUTO) {
+    if (is_f32(p)) v = AGMM_VARIANT_FUSED;
+    else if (p->m <= 256) v = AGMM_VARIANT_SKINNY;
+    else v = AGMM_VARIANT_FUSED;
+  }
+  if (is_f32(p) && v == AGMM_VARIANT_SKINNY) v = AGMM_VARIANT_FUSED;
+  if ((v == AGMM_VARIANT_STAGED || v == AGMM_VARIANT_UNFUSED) && (p->k * e) % 16 != 0)
+    return set_err(AGMM_ERR_UNSUPPORTED,
+                   "the gather copy needs 16-byte rows (k * elem_bytes %% 16 == 0)");
+  p->variant_used = v;
+
+  // tiles
+  if (is_f32(p)) {
+    p->tile_used = -1;
+    p->bm = p->bn = 64;
+  } else if (v == AGMM_VARIANT_SKINNY) {
+    p->tile_used = p->tile >= 0 ? p->tile : (p->m <= 128 ? agmm::kTile128x128 : agmm::kTile256x128);
+    p->bm = agmm::tile_bm(p->tile_used);
+    p->bn = agmm::tile_bn(p->tile_used);
+  } else if (v == AGMM_VARIANT_STAGED) {
+    p->tile_used = p->tile >= 0 ? p->tile : agmm::kTile256x256;
+    p->bm = agmm::tile_bm(p->tile_used);
+    p->bn = agmm::tile_bn(p->tile_used);
+  } else {
+    p->tile_used = choose_tile(p, p->m);
+    p->bm = agmm::tile_bm(p->tile_used);
+    p->bn = agmm::tile_bn(p->tile_used);
+  }
+
+  // chunking (staged) / split-K (skinny)
+  p->rows_per_chunk = p->m_s;
+  p->num_chunks = 1;
+  p->nslots = 0;
+  p->splits_used = 1;
+  p->k_per_split = p->k;
+  size_t ring_bytes = 0, part_bytes = 0, counter_bytes = 0;
+  if (v == AGMM_VARIANT_STAGED) {
+    p->rows_per_chunk = std::min<int64_t>(p->m_s, (int64_t)p->pvalue * p->bm);
+    p->num_chunks = (int)cdiv(p->m_s, p->rows_per_chunk);
+    p->nslots = p->debug_keep_slots ? p->num_chunks : std::min(p->nbuf, p->num_chunks);
+    p->slot_bytes = (size_t)p->N * p->rows_per_chunk * p->k * e;
+    ring_bytes = p->slot_bytes * p->nslots;
+  } else if (v == AGMM_VARIANT_UNFUSED) {
+    p->nslots = 1;
+    p->slot_bytes = (size_t)p->m * p->k * e;
+    ring_bytes = p->slot_bytes;
+  } else if (v == AGMM_VARIANT_SKINNY) {
+    const int64_t tiles = cdiv(p->m, p->bm) * cdiv(p->n, p->bn);
+    int64_t want = p->splits > 0 ? p->splits : cdiv(p->cu_count, tiles);
+    want = std::max<int64_t>(1, std::min<int64_t>(want, cdiv(p->k, agmm::kTileBK)));
+    p->k_per_split = cdiv(cdiv(p->k, want), agmm::kTileBK) * agmm::kTileBK;
+    p->splits_used = (int)cdiv(p->k, p->k_per_split);
+    if (p->splits_used > 1) {
+      part_bytes = (size_t)p->splits_used * p->m * p->n * sizeof(float);
+      counter_bytes = (size_t)tiles * sizeof(int32_t);
+    }
+  }
+
+  // tile orders (one table per chunk)
+  p->h_order.clear();
+  p->order_off.clear();
+  p->order_len.clear();
+  std::vector<int32_t> tmp;
+  for (int c = 0; c < p->num_chunks; ++c) {
+    const int64_t rows_c = std::min<int64_t>(p->rows_per_chunk, p->m_s - (int64_t)c * p->rows_per_chunk);
+    ring_order(p, rows_c, (int64_t)c * p->rows_per_chunk, p->bm, p->order, tmp);
+    p->order_off.push_back((int64_t)p->h_order.size());
+    p->order_len.push_back((int32_t)tmp.size());
+    p->h_order.insert(p->h_order.end(), tmp.begin(), tmp.end());
+  }
+  const size_t order_bytes = p->h_order.size() * sizeof(int32_t);
+
+  // one allocation, 256-byte aligned pieces
+  auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
+  const size_t total = up(ring_bytes) + up(part_bytes) + up(counter_bytes) + up(order_bytes);
+  free_resources(p);
+  if (total > 0) {
+    if (std::getenv("AGMM_TEST_FAIL_ALLOC"))
+      return set_err(AGMM_ERR_OOM, "workspace allocation of %zu bytes failed (forced by test hook)",
+                     total);
+    hipError_t err = hipMalloc(&p->ws, total);
+    if (err != hipSuccess) {
+      p->ws = nullptr;
+      (void)hipGetLastError();
+      return set_err(AGMM_ERR_OOM, "workspace allocation of %zu bytes failed: %s", total,
+                     hipGetErrorString(err));
+    }
+    p->ws_bytes = total;
+    char* q = p->ws;
+    if (ring_bytes) { p->ring = q; q += up(ring_bytes); }
+    if (part_bytes) { p->partials = reinterpret_cast<float*>(q); q += up(part_bytes); }
+    if (counter_bytes) {
+      p->counters = reinterpret_cast<int32_t*>(q);
+      err = hipMemset(p->counters, 0, counter_bytes);
+      if (err != hipSuccess) return hip_err(err, "hipMemset(counters)");
+      q += up(counter_bytes);
+    }
+    if (order_bytes) {
+      p->d_order = reinterpret_cast<int32_t*>(q);
+      err = hipMemcpy(p->d_order, p->h_order.data(), order_bytes, hipMemcpyHostToDevice);
+      if (err != hipSuccess) return hip_err(err, "hipMemcpy(tile order)");
+    }
+  }
+
+  // events for the ring
+  const size_t want_ev = (size_t)std::max(p->nslots, 1);
+  while (p->ev_ready.size() < want_ev) {
+    hipEvent_t a, b;
+    hipError_t err = hipEventCreateWithFlags(&a, hipEventDisableTiming);
+    if (err != hipSuccess) return hip_err(err, "hipEventCreate");
+    err = hipEventCreateWithFlags(&b, hipEventDisableTiming);
+    if (err != hipSuccess) { hipEventDestroy(a); return hip_err(err, "hipEventCreate"); }
+    p->ev_ready.push_back(a);
+    p->ev_free.push_back(b);
+  }
+  return ok();
+}
+
+agmm::RowMap shard_rows(const agmm_plan* p, const void* const* shards) {
+  agmm::RowMap r{};
+  for (int g = 0; g < p->N; ++g) r.a_group[g] = shards[g];
+  r.a_ld = p->k;
+  r.rows_per_group = (int32_t)p->m_s;
+  r.num_groups = p->N;
+  r.c_group_rows = p->m_s;
+  r.c_row_off = 0;
+  return r;
+}
+
+agmm::GemmProblem base_problem(const agmm_plan* p, const agmm::RowMap& rows, int64_t m_launch,
+                               const void* B, void* C, int chunk) {
+  agmm::GemmProblem g{};
+  g.rows = rows;
+  g.m = (int32_t)m_launch;
+  g.n = (int32_t)p->n;
+  g.k = (int32_t)p->k;
+  g.b = B;
+  g.ldb = p->rt ? p->k : p->n;
+  g.c = C;
+  g.ldc = p->n;
+  g.order.num_rb = (int32_t)cdiv(m_launch, p->bm);
+  g.order.num_cb = (int32_t)cdiv(p->n, p->bn);
+  g.order.group_m = std::max(1, p->group_m);
+  g.order.xcd_remap = p->xcd_remap;
+  g.order.rb_order = nullptr;
+  if (chunk >= 0 && p->d_order && chunk < (int)p->order_off.size() &&
+      p->order_len[chunk] == g.order.num_rb)
+    g.order.rb_order = p->d_order + p->order_off[chunk];
+  g.splits = 1;
+  g.k_per_split = (int32_t)p->k;
+  return g;
+}
+
+int launch_gemm(agmm_plan* p, agmm::GemmProblem& g, hipStream_t s) {
+  const bool timed = p->timing && p->tev_used + 2 <= (int)p->tev.size();
+  if (timed) hipEventRecord(p->tev[p->tev_used], s);
+  hipError_t err;
+  if (is_f32(p)) err = agmm::launch_gemm_f32(g, p->rt != 0, s);
+  else err = agmm::launch_gemm_mfma(g, p->tile_used, p->dtype, p->rt != 0, s);
+  if (err != hipSuccess) return hip_err(err, "GEMM launch");
+  if (timed) {
+    hipEventRecord(p->tev[p->tev_used + 1], s);
+    p->tev_used += 2;
+  }
+  return AGMM_OK;
+}
+
+int check_ptrs(agmm_plan* p, const void* const* shards, const void* B, const void* C) {
+  if (!p) return set_err(AGMM_ERR_INVALID_ARG, "plan is NULL");
+  if (!shards) return set_err(AGMM_ERR_INVALID_ARG, "shard_ptrs is NULL");
+  for (int r = 0; r < p->N; ++r) {
+    if (!shards[r]) return set_err(AGMM_ERR_INVALID_ARG, "shard_ptrs[%d] is NULL", r);
+    if (!aligned16(shards[r]))
+      return set_err(AGMM_ERR_UNSUPPORTED, "shard_ptrs[%d] is not 16-byte aligned", r);
+  }
+  if (!B) return set_err(AGMM_ERR_INVALID_ARG, "B is NULL");
+  if (!C) return set_err(AGMM_ERR_INVALID_ARG, "C is NULL");
+  if (!aligned16(B)) return set_err(AGMM_ERR_UNSUPPORTED, "B is not 16-byte aligned");
+  if (!aligned16(C)) return set_err(AGMM_ERR_UNSUPPORTED, "C is not 16-byte aligned");
+  return AGMM_OK;
+}
+
+int gather_chunk(agmm_plan* p, const void* const* shards, int64_t row0, int64_t rows, void* dst,
+                 int64_t dst_group_rows, int max_wgs, hipStream_t s) {
+  agmm::GatherProblem g{};
+  for (int r = 0; r < p->N; ++r) g.src_group[r] = shards[r];
+  g.num_groups = p->N;
+  g.src_row0 = row0;
+  g.rows = rows;
+  g.row_bytes = p->k * (int64_t)elem_bytes(p->dtype);
+  g.dst = dst;
+  g.dst_group_rows = dst_group_rows;
+  hipError_t err = agmm::launch_gather(g, max_wgs, s);
+  if (err != hipSuccess) return hip_err(err, "gather launch");
+  return AGMM_OK;
+}
+
+int run_staged(agmm_plan* p, const void* const* shards, const void* B, void* C, hipStream_t s) {
+  hipError_t err = hipEventRecord(p->ev_entry, s);
+  if (err != hipSuccess) return hip_err(err, "hipEventRecord");
+  err = hipStreamWaitEvent(p->copy_stream, p->ev_entry, 0);
+  if (err != hipSuccess) return hip_err(err, "hipStreamWaitEvent");
+  const int64_t e = elem_bytes(p->dtype);
+  const int copy_wgs = p->copy_wgs > 0 ? p->copy_wgs : p->cu_count;
+  for (int c = 0; c < p->num_chunks; ++c) {
+    const int slot = c % p->nslots;
+    const int64_t row0 = (int64_t)c * p->rows_per_chunk;
+    const int64_t rows_c = std::min<int64_t>(p->rows_per_chunk, p->m_s - row0);
+    char* slot_ptr = p->ring + (size_t)slot * p->slot_bytes;
+    if (c >= p->nslots) {
+      err = hipStreamWaitEvent(p->copy_stream, p->ev_free[slot], 0);
+      if (err != hipSuccess) return hip_err(err, "hipStreamWaitEvent(free)");
+    }
+    int rc = gather_chunk(p, shards, row0, rows_c, slot_ptr, rows_c, copy_wgs, p->copy_stream);
+    if (rc != AGMM_OK) return rc;
+    if ((err = hipEventRecord(p->ev_ready[slot], p->copy_stream)) != hipSuccess)
+      return hip_err(err, "hipEventRecord(ready)");
+    if ((err = hipStreamWaitEvent(s, p->ev_ready[slot], 0)) != hipSuccess)
+      return hip_err(err, "hipStreamWaitEvent(ready)");
+    agmm::RowMap rm{};
+    for (int g = 0; g < p->N; ++g) rm.a_group[g] = slot_ptr + (size_t)g * rows_c * p->k * e;
+    rm.a_ld = p->k;
+    rm.rows_per_group = (int32_t)rows_c;
+    rm.num_groups = p->N;
+    rm.c_group_rows = p->m_s;
+    rm.c_row_off = row0;
+    agmm::GemmProblem g = base_problem(p, rm, rows_c * p->N, B, C, c);
+    rc = launch_gemm(p, g, s);
+    if (rc != AGMM_OK) return rc;
+    if ((err = hipEventRecord(p->ev_free[slot], s)) != hipSuccess)
+      return hip_err(err, "hipEventRecord(free)");
+  }
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int agmm_plan_validate(int num_shards, int64_t m_per_shard, int64_t k, int64_t n_local, int dtype,
+                       int rhs_transpose) {
+  return validate(num_shards, m_per_shard, k, n_local, dtype, rhs_transpose);
+}
+
+agmm_plan_t agmm_plan_create(int num_shards, int64_t m_per_shard, int64_t k, int64_t n_local,
+                             int dtype, int rhs_transpose) {
+  if (validate(num_shards, m_per_shard, k, n_local, dtype, rhs_transpose) != AGMM_OK)
+    return nullptr;
+  agmm_plan* p = new (std::nothrow) agmm_plan();
+  if (!p) {
+    set_err(AGMM_ERR_OOM, "out of host memory");
+    return nullptr;
+  }
+  p->N = num_shards;
+  p->m_s = m_per_shard;
+  p->k = k;
+  p->n = n_local;
+  p->m = (int64_t)num_shards * m_per_shard;
+  p->dtype = dtype;
+  p->rt = rhs_transpose;
+  hipError_t err = hipGetDevice(&p->device);
+  if (err != hipSuccess) {
+    hip_err(err, "hipGetDevice");
+    delete p;
+    return nullptr;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, p->device) == hipSuccess &&
+      cus > 0)
+    p->cu_count = cus;
+  err = hipStreamCreateWithFlags(&p->copy_stream, hipStreamNonBlocking);
+  if (err != hipSuccess) {
+    hip_err(err, "hipStreamCreate");
+    delete p;
+    return nullptr;
+  }
+  err = hipEventCreateWithFlags(&p->ev_entry, hipEventDisableTiming);
+  if (err != hipSuccess) {
+    hip_err(err, "hipEventCreate");
+    hipStreamDestroy(p->copy_stream);
+    delete p;
+    return nullptr;
+  }
+  if (configure(p) != AGMM_OK) {
+    const int st = g_status;
+    const std::string msg = g_msg;
+    agmm_plan_destroy(p);
+    set_err(st, "%s", msg.c_str());
+    return nullptr;
+  }
+  ok();
+  return p;
+}
+
+int agmm_plan_set_int(agmm_plan_t p, const char* key, int64_t v) {
+  if (!p) return set_err(AGMM_ERR_INVALID_ARG, "plan is NULL");
+  if (!key) return set_err(AGMM_ERR_INVALID_ARG, "key is NULL");
+  std::lock_guard<std::mutex> lk(p->mu);
+  const std::string k(key);
+  auto bad = [&]() {
+    return set_err(AGMM_ERR_INVALID_ARG, "value %lld out of range for key '%s'", (long long)v, key);
+  };
+  if (k == "variant") {
+    if (v < AGMM_VARIANT_AUTO || v > AGMM_VARIANT_SKINNY) return bad();
+    p->variant = (int)v;
+  } else if (k == "pvalue") {
+    if (v < 1 || v > (1 << 20)) return bad();
+    p->pvalue = (int)v;
+  } else if (k == "nbuf") {
+    if (v < 1 || v > 64) return bad();
+    p->nbuf = (int)v;
+  } else if (k == "tile") {
+    if (v < -1 || v >= agmm::kTileCount) return bad();
+    p->tile = (int)v;
+  } else if (k == "splits") {
+    if (v < 0 || v > 4096) return bad();
+    p->splits = (int)v;
+  } else if (k == "local_shard") {
+    if (v < 0 || v >= p->N) return bad();
+    p->local_shard = (int)v;
+  } else if (k == "order") {
+    if (v != 0 && v != 1) return bad();
+    p->order = (int)v;
+  } else if (k == "group_m") {
+    if (v < 1 || v > 1 << 20) return bad();
+    p->group_m = (int)v;
+  } else if (k == "xcd_remap") {
+    if (v != 0 && v != 1) return bad();
+    p->xcd_remap = (int)v;
+  } else if (k == "copy_wgs") {
+    if (v < 0 || v > 1 << 20) return bad();
+    p->copy_wgs = (int)v;
+  } else if (k == "debug_keep_slots") {
+    if (v != 0 && v != 1) return bad();
+    p->debug_keep_slots = (int)v;
+  } else {
+    return set_err(AGMM_ERR_INVALID_ARG, "unknown key '%s'", key);
+  }
+  // Wait for in-flight work that may use the current workspace.
+  hipError_t err = hipDeviceSynchronize();
+  if (err != hipSuccess) return hip_err(err, "hipDeviceSynchronize");
+  return configure(p);
+}
+
+int agmm_plan_get_int(agmm_plan_t p, const char* key, int64_t* value) {
+  if (!p || !key || !value) return set_err(AGMM_ERR_INVALID_ARG, "NULL argument");
+  const std::string k(key);
+  int64_t v;
+  if (k == "variant") v = p->variant;
+  else if (k == "variant_used") v = p->variant_used;
+  else if (k == "pvalue") v = p->pvalue;
+  else if (k == "nbuf") v = p->nbuf;
+  else if (k == "tile") v = p->tile_used;
+  else if (k == "splits") v = p->splits_used;
+  else if (k == "local_shard") v = p->local_shard;
+  else if (k == "order") v = p->order;
+  else if (k == "group_m") v = p->group_m;
+  else if (k == "xcd_remap") v = p->xcd_remap;
+  else if (k == "copy_wgs") v = p->copy_wgs;
+  else if (k == "debug_keep_slots") v = p->debug_keep_slots;
+  else if (k == "num_chunks") v = p->num_chunks;
+  else if (k == "rows_per_chunk") v = p->rows_per_chunk;
+  else if (k == "num_slots") v = p->nslots;
+  else if (k == "tile_bm") v = p->bm;
+  else if (k == "tile_bn") v = p->bn;
+  else if (k == "k_per_split") v = p->k_per_split;
+  else if (k == "num_row_blocks") v = p->order_len.empty() ? 0 : p->order_len[0];
+  else if (k == "cu_count") v = p->cu_count;
+  else return set_err(AGMM_ERR_INVALID_ARG, "unknown key '%s'", key);
+  *value = v;
+  return ok();
+}
+
+size_t agmm_plan_workspace_bytes(agmm_plan_t p) { return p ? p->ws_bytes : 0; }
+
+const void* agmm_plan_slot_ptr(agmm_plan_t p, int slot) {
+  if (!p || !p->ring || slot < 0 || slot >= p->nslots) return nullptr;
+  return p->ring + (size_t)slot * p->slot_bytes;
+}
+
+int agmm_plan_tile_order(agmm_plan_t p, int chunk, int32_t* out, int capacity) {
+  if (!p || !out || chunk < 0 || chunk >= (int)p->order_len.size()) {
+    set_err(AGMM_ERR_INVALID_ARG, "bad arguments to agmm_plan_tile_order");
+    return -1;
+  }
+  const int len = p->order_len[chunk];
+  if (capacity < len) {
+    set_err(AGMM_ERR_INVALID_ARG, "capacity %d < %d row blocks", capacity, len);
+    return -1;
+  }
+  std::memcpy(out, p->h_order.data() + p->order_off[chunk], sizeof(int32_t) * len);
+  ok();
+  return len;
+}
+
+int agmm_run(agmm_plan_t p, const void* const* shard_ptrs, const void* B, void* C, void* stream) {
+  int rc = check_ptrs(p, shard_ptrs, B, C);
+  if (rc != AGMM_OK) return rc;
+  std::lock_guard<std::mutex> lk(p->mu);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  switch (p->variant_used) {
+    case AGMM_VARIANT_FUSED: {
+      agmm::GemmProblem g = base_problem(p, shard_rows(p, shard_ptrs), p->m, B, C, 0);
+      rc = launch_gemm(p, g, s);
+      return rc == AGMM_OK ? ok() : rc;
+    }
+    case AGMM_VARIANT_SKINNY: {
+      agmm::GemmProblem g = base_problem(p, shard_rows(p, shard_ptrs), p->m, B, C, 0);
+      g.splits = p->splits_used;
+      g.k_per_split = (int32_t)p->k_per_split;
+      g.partials = p->partials;
+      g.counters = p->counters;
+      rc = launch_gemm(p, g, s);
+      return rc == AGMM_OK ? ok() : rc;
+    }
+    case AGMM_VARIANT_UNFUSED: {
+      rc = gather_chunk(p, shard_ptrs, 0, p->m_s, p->ring, p->m_s, 0, s);
+      if (rc != AGMM_OK) return rc;
+      agmm::RowMap rm{};
+      rm.a_group[0] = p->ring;
+      rm.a_ld = p->k;
+      rm.rows_per_group = (int32_t)p->m;
+      rm.num_groups = 1;
+      rm.c_group_rows = 0;
+      rm.c_row_off = 0;
+      agmm::GemmProblem g = base_problem(p, rm, p->m, B, C, -1);
+      rc = launch_gemm(p, g, s);
+      return rc == AGMM_OK ? ok() : rc;
+    }
+    case AGMM_VARIANT_STAGED:
+      return run_staged(p, shard_ptrs, B, C, s);
+    default:
+      return set_err(AGMM_ERR_INVALID_ARG, "plan has no valid variant");
+  }
+}
+
+int agmm_gather(agmm_plan_t p, const void* const* shard_ptrs, void* gathered, void* stream) {
+  if (!p) return set_err(AGMM_ERR_INVALID_ARG, "plan is NULL");
+  if (!shard_ptrs) return set_err(AGMM_ERR_INVALID_ARG, "shard_ptrs is NULL");
+  if (!gathered) return set_err(AGMM_ERR_INVALID_ARG, "gathered is NULL");
+  if (!aligned16(gathered)) return set_err(AGMM_ERR_UNSUPPORTED, "gathered is not 16-byte aligned");
+  for (int r = 0; r < p->N; ++r) {
+    if (!shard_ptrs[r]) return set_err(AGMM_ERR_INVALID_ARG, "shard_ptrs[%d] is NULL", r);
+    if (!aligned16(shard_ptrs[r]))
+      return set_err(AGMM_ERR_UNSUPPORTED, "shard_ptrs[%d] is not 16-byte aligned", r);
+  }
+  if ((p->k * (int64_t)elem_bytes(p->dtype)) % 16 != 0)
+    return set_err(AGMM_ERR_UNSUPPORTED, "the gather copy needs 16-byte rows");
+  std::lock_guard<std::mutex> lk(p->mu);
+  const int rc = gather_chunk(p, shard_ptrs, 0, p->m_s, gathered, p->m_s, 0,
+                              static_cast<hipStream_t>(stream));
+  return rc == AGMM_OK ? ok() : rc;
+}
+
+int agmm_run_gathered(agmm_plan_t p, const void* gathered, const void* B, void* C, void* stream) {
+  if (!p) return set_err(AGMM_ERR_INVALID_ARG, "plan is NULL");
+  if (!gathered || !B || !C) return set_err(AGMM_ERR_INVALID_ARG, "NULL pointer argument");
+  if (!aligned16(gathered) || !aligned16(B) || !aligned16(C))
+    return set_err(AGMM_ERR_UNSUPPORTED, "pointers must be 16-byte aligned");
+  std::lock_guard<std::mutex> lk(p->mu);
+  agmm::RowMap rm{};
+  rm.a_group[0] = gathered;
+  rm.a_ld = p->k;
+  rm.rows_per_group = (int32_t)p->m;
+  rm.num_groups = 1;
+  rm.c_group_rows = 0;
+  rm.c_row_off = 0;
+  agmm::GemmProblem g = base_problem(p, rm, p->m, B, C, -1);
+  if (p->variant_used == AGMM_VARIANT_SKINNY && p->splits_used > 1) {
+    g.splits = p->splits_used;
+    g.k_per_split = (int32_t)p->k_per_split;
+    g.partials = p->partials;
+    g.counters = p->counters;
+  }
+  const int rc = launch_gemm(p, g, static_cast<hipStream_t>(stream));
+  return rc == AGMM_OK ? ok() : rc;
+}
+
+int agmm_plan_timing_begin(agmm_plan_t p) {
+  if (!p) return set_err(AGMM_ERR_INVALID_ARG, "plan is NULL");
+  std::lock_guard<std::mutex> lk(p->mu);
+  while (p->tev.size() < 2 * (size_t)kTimingPairs) {
+    hipEvent_t e;
+    hipError_t err = hipEventCreate(&e);
+    if (err != hipSuccess) return hip_err(err, "hipEventCreate");
+    p->tev.push_back(e);
+  }
+  p->tev_used = 0;
+  p->timing = true;
+  return ok();
+}
+
+int agmm_plan_timing_read(agmm_plan_t p, double* total_ms, int64_t* launches) {
+  if (!p || !total_ms || !launches) return set_err(AGMM_ERR_INVALID_ARG, "NULL argument");
+  std::lock_guard<std::mutex> lk(p->mu);
+  double sum = 0.0;
+  for (int i = 0; i + 1 < p->tev_used; i += 2) {
+    hipError_t err = hipEventSynchronize(p->tev[i + 1]);
+    if (err != hipSuccess) return hip_err(err, "hipEventSynchronize");
+    float ms = 0.0f;
+    err = hipEventElapsedTime(&ms, p->tev[i], p->tev[i + 1]);
+    if (err != hipSuccess) return hip_err(err, "hipEventElapsedTime");
+    sum += ms;
+  }
+  *total_ms = sum;
+  *launches = p->tev_used / 2;
+  return ok();
+}
+
+int agmm_plan_timing_end(agmm_plan_t p) {
+  if (!p) return set_err(AGMM_ERR_INVALID_ARG, "plan is NULL");
+  std::lock_guard<std::mutex> lk(p->mu);
+  p->timing = false;
+  return ok();
+}
+
+void agmm_plan_destroy(agmm_plan_t p) {
+  if (!p) return;
+  if (p->copy_stream) hipStreamSynchronize(p->copy_stream);
+  hipDeviceSynchronize();
+  free_resources(p);
+  for (hipEvent_t e : p->ev_ready) hipEventDestroy(e);
+  for (hipEvent_t e : p->ev_free) hipEventDestroy(e);
+  for (hipEvent_t e : p->tev) hipEventDestroy(e);
+  if (p->ev_entry) hipEventDestroy(p->ev_entry);
+  if (p->copy_stream) hipStreamDestroy(p->copy_stream);
+  delete p;
+}
+
+int agmm_last_status(void) { return g_status; }
+
+const char* agmm_last_error(void) { return g_msg.c_str(); }
+
+const char* agmm_version(void) { return "agmm 0.1.0 (gfx950)"; }
+
+}  // extern "C"

@@ -1,0 +1,91 @@
+// Internal interface between the plan/scheduler (agmm_api.cpp) and the HIP
+// kernels.  Not installed; the public interface is include/agmm.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace agmm {
+
+// Largest number of shard buffers one call can name.  The pointer table
+// travels in the kernel arguments (8 bytes per entry).
+constexpr int kMaxGroups = 64;
+
+constexpr int kDtypeBf16 = 0;
+constexpr int kDtypeFp16 = 1;
+constexpr int kDtypeFp32 = 2;
+
+// Row mapping shared by every kernel that reads the gathered operand.
+//
+// A launch covers m = num_groups * rows_per_group logical rows.  Logical row
+// i belongs to group g = i / rows_per_group at position t = i % rows_per_group:
+//   its A row starts at  a_group[g] + t * a_ld            (elements)
+//   its C row is         g * c_group_rows + c_row_off + t
+// The fused path passes the shard pointers themselves (one group per shard);
+// a ring slot or the fully gathered buffer is described the same way.
+struct RowMap {
+  const void* a_group[kMaxGroups];
+  int64_t a_ld;            // elements between consecutive rows of one group
+  int32_t rows_per_group;  // rows of each group covered by this launch
+  int32_t num_groups;
+  int64_t c_group_rows;    // C rows between the starts of consecutive groups
+  int64_t c_row_off;       // C row of position t = 0 inside each group
+};
+
+// Order in which workgroups visit output tiles.
+struct TileOrder {
+  const int32_t* rb_order;  // device table: visit order of row blocks (nullptr = natural)
+  int32_t num_rb;           // row blocks  (ceil(m / BM))
+  int32_t num_cb;           // column blocks (ceil(n / BN))
+  int32_t group_m;          // row blocks walked together for L2 reuse
+  int32_t xcd_remap;        // 1: keep consecutive tiles on one XCD
+};
+
+struct GemmProblem {
+  RowMap rows;
+  TileOrder order;
+  int32_t m, n, k;
+  const void* b;
+  int64_t ldb;             // elements between rows of B as stored
+  void* c;
+  int64_t ldc;             // elements between rows of C
+  // split-K (used when splits > 1)
+  int32_t splits;
+  int32_t k_per_split;     // multiple of the kernel's BK
+  float* partials;         // [splits][m][n] fp32
+  int32_t* counters;       // [num_rb * num_cb], zero between calls
+};
+
+// Tile shapes compiled for the MFMA kernels.
+enum TileCfg : int {
+  kTile256x256 = 0,   // 4 waves, 128x128 per wave
+  kTile128x128 = 1,   // 4 waves, 64x64 per wave
+  kTile256x128 = 2,   // 4 waves, 128x64 per wave
+  kTileCount = 3,
+};
+int tile_bm(int cfg);
+int tile_bn(int cfg);
+constexpr int kTileBK = 64;
+
+// bf16/fp16 MFMA GEMM (16-bit inputs, fp32 accumulate, output in the input dtype).
+hipError_t launch_gemm_mfma(const GemmProblem& p, int tile_cfg, int dtype, bool rhs_transpose,
+                            hipStream_t stream);
+
+// fp32 inputs, fp64 accumulate, fp32 output (any shape).
+hipError_t launch_gemm_f32(const GemmProblem& p, bool rhs_transpose, hipStream_t stream);
+
+// Bit copy of rows into a dense destination:
+//   dst[(g * dst_group_rows + t) * row_bytes ...] = src_group[g][(src_row0 + t) * row_bytes ...]
+// for g < num_groups, t < rows.  row_bytes % 16 == 0, all pointers 16-byte aligned.
+struct GatherProblem {
+  const void* src_group[kMaxGroups];
+  int32_t num_groups;
+  int64_t src_row0;
+  int64_t rows;
+  int64_t row_bytes;
+  void* dst;
+  int64_t dst_group_rows;
+};
+hipError_t launch_gather(const GatherProblem& p, int max_workgroups, hipStream_t stream);
+
+}  // namespace agmm

@@ -1,0 +1,171 @@
+// Gather copy and the fp32-input GEMM of the all-gather matmul (gfx950).
+//
+// Gather: the staged path first copies each shard's rows into a dense buffer
+// (a ring slot, or the whole gathered operand for the unfused path).  This is
+// the single-GPU stand-in for the pages' data movement: the tpu-inference
+// kernel's HBM->VMEM x copies per received shard (`_all_gather_kernel`, the
+// local x copies), and the Ascend tutorial's phase-2 local copy of A into the
+// symmetric buffer in COMM_BLOCK tiles ("Two-Phase Pipeline").  Here it is a
+// plain bit copy with 16-byte vector loads/stores, several in flight per lane.
+//
+// fp32 GEMM: the same contraction for fp32 inputs.  The products of two fp32
+// values are exact in fp64 and the sum runs in fp64, then the result is
+// rounded once to fp32; an fp32 accumulator cannot meet a 1e-5 relative bound
+// on outputs near zero.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "agmm_kernels.h"
+
+namespace agmm {
+
+namespace {
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kCopyThreads = 256;
+constexpr int kCopyUnroll = 4;
+
+__global__ __launch_bounds__(kCopyThreads) void gather_kernel(GatherProblem p) {
+  const int64_t chunks_per_row = p.row_bytes >> 4;
+  const int64_t chunks_per_group = chunks_per_row * p.rows;
+  const int64_t total = chunks_per_group * p.num_groups;
+  const int64_t stride = (int64_t)gridDim.x * kCopyThreads;
+  int64_t u = (int64_t)blockIdx.x * kCopyThreads + threadIdx.x;
+
+  for (; u < total; u += stride * kCopyUnroll) {
+    u32x4_t v[kCopyUnroll];
+    int64_t dst_off[kCopyUnroll];
+#pragma unroll
+    for (int q = 0; q < kCopyUnroll; ++q) {
+      const int64_t w = u + q * stride;
+      dst_off[q] = -1;
+      if (w < total) {
+        const int64_t g = w / chunks_per_group;
+        const int64_t rem = w - g * chunks_per_group;
+        const int64_t t = rem / chunks_per_row;
+        const int64_t c = rem - t * chunks_per_row;
+        const char* src = static_cast<const char*>(p.src_group[g]) +
+                          (p.src_row0 + t) * p.row_bytes + (c << 4);
+        v[q] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(src));
+        dst_off[q] = (g * p.dst_group_rows + t) * p.row_bytes + (c << 4);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < kCopyUnroll; ++q)
+      if (dst_off[q] >= 0)
+        *reinterpret_cast<u32x4_t*>(static_cast<char*>(p.dst) + dst_off[q]) = v[q];
+  }
+}
+
+// fp32 GEMM: 64x64 output tile per workgroup, 256 threads, each thread a 4x4
+// block; 16-deep k slices staged in LDS as double.
+constexpr int kF32Tile = 64;
+constexpr int kF32K = 16;
+
+template <bool BT>
+__global__ __launch_bounds__(256) void gemm_f32_kernel(GemmProblem p) {
+  __shared__ double sa[kF32K][kF32Tile + 1];
+  __shared__ double sb[kF32K][kF32Tile + 1];
+  const int tid = threadIdx.x;
+  const int M = p.m, N = p.n, K = p.k;
+  const int num_cb = p.order.num_cb;
+  const int tile = blockIdx.x;
+  const int rbi = tile / num_cb;
+  const int cb = tile - rbi * num_cb;
+  const int rb = p.order.rb_order ? p.order.rb_order[rbi] : rbi;
+  const int m0 = rb * kF32Tile, n0 = cb * kF32Tile;
+  const int tr = tid / 16, tc = tid % 16;  // this thread: rows tr*4.., cols tc*4..
+
+  // Row sources for the A loads: thread loads A rows m0 + (tid / 16) * 4 + i.
+  double acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = 0.0;
+
+  for (int k0 = 0; k0 < K; k0 += kF32K) {
+    // A tile: 64 rows x 16 k -> 1024 values, 4 per thread.
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int idx = tid + q * 256;
+      const int r = idx / kF32K, kk = idx % kF32K;
+      const int gi = m0 + r, gk = k0 + kk;
+      double v = 0.0;
+      if (gi < M && gk < K) {
+        const int g = gi / p.rows.rows_per_group;
+        const int t = gi - g * p.rows.rows_per_group;
+        v = (double)static_cast<const float*>(p.rows.a_group[g])[(int64_t)t * p.rows.a_ld + gk];
+      }
+      sa[kk][r] = v;
+    }
+    // B tile: 16 k x 64 n.
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int idx = tid + q * 256;
+      int kk, c;
+      if (BT) { c = idx / kF32K; kk = idx % kF32K; }
+      else { kk = idx / kF32Tile; c = idx % kF32Tile; }
+      const int gk = k0 + kk, gn = n0 + c;
+      double v = 0.0;
+      if (gk < K && gn < N) {
+        const float* b = static_cast<const float*>(p.b);
+        v = BT ? (double)b[(int64_t)gn * p.ldb + gk] : (double)b[(int64_t)gk * p.ldb + gn];
+      }
+      sb[kk][c] = v;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < kF32K; ++kk) {
+      double a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = sa[kk][tr * 4 + i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b[j] = sb[kk][tc * 4 + j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_fma(a[i], b[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int gi = m0 + tr * 4 + i;
+    if (gi >= M) continue;
+    const int g = gi / p.rows.rows_per_group;
+    const int t = gi - g * p.rows.rows_per_group;
+    const int64_t crow = (int64_t)g * p.rows.c_group_rows + p.rows.c_row_off + t;
+    float* cp = static_cast<float*>(p.c) + crow * p.ldc;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int gn = n0 + tc * 4 + j;
+      if (gn < N) cp[gn] = (float)acc[i][j];
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_gather(const GatherProblem& p, int max_workgroups, hipStream_t stream) {
+  const int64_t total = (p.row_bytes >> 4) * p.rows * p.num_groups;
+  if (total == 0) return hipSuccess;
+  int64_t wgs = (total + (int64_t)kCopyThreads * kCopyUnroll - 1) / ((int64_t)kCopyThreads * kCopyUnroll);
+  if (max_workgroups > 0 && wgs > max_workgroups) wgs = max_workgroups;
+  if (wgs < 1) wgs = 1;
+  hipLaunchKernelGGL(gather_kernel, dim3((unsigned)wgs), dim3(kCopyThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_f32(const GemmProblem& p, bool rhs_transpose, hipStream_t stream) {
+  const int ntiles = p.order.num_rb * p.order.num_cb;
+  if (ntiles == 0) return hipSuccess;
+  if (rhs_transpose)
+    hipLaunchKernelGGL(gemm_f32_kernel<true>, dim3(ntiles), dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL(gemm_f32_kernel<false>, dim3(ntiles), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace agmm

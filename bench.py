@@ -1,0 +1,261 @@
+#!/usr/bin/env python3
+"""Benchmark of the all-gather matmul on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload 5] [--variant auto]
+
+One step = one agmm_run (the whole hot path: gather/slot sync/tile schedule/
+MFMA GEMM/epilogue, as the chosen variant does them) over one batch of seeded
+synthetic inputs already resident in HBM.  Prints ONE JSON line.
+
+value      : 2*m*k*n_local / (wall time per step), TFLOP/s, timed with events
+             on the caller's stream around exactly K steps.
+roofline   : the dominant kernel (the MFMA GEMM) timed per launch with HIP
+             events on the stream it is launched on, against the MI355X dense
+             bf16/fp16 MFMA peak (2.5 PFLOP/s).
+gather     : the gather copy alone (agmm_gather) on the same shards, GB/s of
+             payload (m*k*elem) and of HBM traffic (read + write).
+variants_ms: the same problem through the fused, staged and unfused paths.
+cpu_baseline: the CPU oracle on a bounded sample of output rows (rank 0).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "TFLOP/s of gather(A)@B (frac of bf16 MFMA peak) + gather GB/s, 1 MI355X"
+PEAK_TFLOPS = {0: 2500.0, 1: 2500.0, 2: 157.3}   # bf16, fp16 dense MFMA; fp32 vector
+PEAK_HBM_GBS = 8000.0
+MALL_BYTES = 256 << 20
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=5)
+    ap.add_argument("--variant", default=None, help="auto|fused|staged|unfused|skinny")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-compare", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--only-run", action="store_true",
+                    help="warmup + K steps of the main path only (for profilers)")
+    return ap.parse_args()
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    for f in ("gemm_mfma.hip", "gather_f32.hip", "agmm_kernels.h"):
+        with open(os.path.join(ROOT, "all_gather_gemm_agmm_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(workload_name: str, variant: str):
+    """HBM bytes per launch of the dominant kernel, from committed rocprofv3
+    PMC summaries; None if absent or taken on different kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload_name}_{variant}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("kernel_sha") != kernel_source_sha():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one MI355X only: the all-gather matmul here runs each "
+              "peer's shard as a local HBM buffer, so --gpus must be 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import all_gather_gemm_agmm_amd as agmm
+    from all_gather_gemm_agmm_amd import inputs as I
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    agmm.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    w = I.WORKLOADS[args.workload]
+    variant = args.variant or w.variant
+    t0 = time.time()
+    shards_np, B_np = I.make_inputs(w)
+    tdt = {0: torch.bfloat16, 1: torch.float16, 2: torch.float32}[w.dtype]
+    itype = {0: np.int16, 1: np.int16, 2: np.int32}[w.dtype]
+
+    def up(bits):
+        return torch.from_numpy(bits.view(itype)).view(tdt).to(dev)
+
+    # Enough independent buffer sets that a step never finds its operands in
+    # the 256 MB MALL from the previous step.
+    ws_bytes = w.algorithmic_bytes()
+    nsets = max(1, min(32, math.ceil(2 * MALL_BYTES / ws_bytes)))
+    base_shards = [up(s) for s in shards_np]
+    base_B = up(B_np)
+    sets = []
+    for i in range(nsets):
+        sh = base_shards if i == 0 else [s.clone() for s in base_shards]
+        Bt = base_B if i == 0 else base_B.clone()
+        C = torch.empty((w.m, w.n_local), dtype=tdt, device=dev)
+        sets.append((sh, Bt, C))
+    gen_s = time.time() - t0
+
+    settings = {}
+    if variant == "staged":
+        settings = {"pvalue": w.pvalue or 2, "nbuf": w.nbuf or 2}
+    plan = agmm.Plan(w.num_shards, w.m_per_shard, w.k, w.n_local, w.dtype, w.rhs_transpose,
+                     variant=variant, **settings)
+    used = agmm.VARIANT_NAMES[plan.get("variant_used")]
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        sh, Bt, C = sets[i % nsets]
+        plan.run(sh, Bt, C, stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    agmm.agmm_plan_timing_begin(plan.handle)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(args.steps):
+        step(i)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms_total = start.elapsed_time(end)
+    k_ms, k_launches = agmm.agmm_plan_timing_read(plan.handle)
+    agmm.agmm_plan_timing_end(plan.handle)
+    ms_per_step = ms_total / args.steps
+    flops = w.flops()
+    value = flops / (ms_per_step * 1e-3) / 1e12
+
+    if args.only_run:
+        print(json.dumps({"workload": w.name, "variant": used, "ms_per_step": ms_per_step}),
+              flush=True)
+        plan.close()
+        return
+
+    # dominant kernel: the GEMM launches (one per step, or one per chunk when staged)
+    launches_per_step = max(1, k_launches // max(args.steps, 1))
+    avg_launch_ms = k_ms / max(k_launches, 1)
+    flops_per_launch = flops / launches_per_step
+    achieved = flops_per_launch / (avg_launch_ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+    traffic = traffic_from_profiles(w.name, used)
+    roofline = {"bound": "mfma" if w.dtype != 2 else "alu", "achieved": round(achieved, 2),
+                "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                "traffic": traffic, "kernel_ms": round(avg_launch_ms, 5),
+                "launches_per_step": launches_per_step}
+
+    # gather copy alone
+    gather = None
+    if (w.k * w.elem_bytes) % 16 == 0:
+        G = torch.empty((w.m, w.k), dtype=tdt, device=dev)
+        gplan = agmm.Plan(w.num_shards, w.m_per_shard, w.k, w.n_local, w.dtype, w.rhs_transpose)
+        for i in range(3):
+            gplan.gather(sets[i % nsets][0], G, stream=stream)
+        torch.cuda.synchronize()
+        gs, ge = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        gsteps = max(10, args.steps)
+        gs.record(stream)
+        for i in range(gsteps):
+            gplan.gather(sets[i % nsets][0], G, stream=stream)
+        ge.record(stream)
+        torch.cuda.synchronize()
+        g_ms = gs.elapsed_time(ge) / gsteps
+        payload = w.gather_bytes()
+        gather = {"ms": round(g_ms, 5), "payload_GB_s": round(payload / (g_ms * 1e-3) / 1e9, 1),
+                  "traffic_GB_s": round(2 * payload / (g_ms * 1e-3) / 1e9, 1),
+                  "frac_hbm": round(2 * payload / (g_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+        gplan.close()
+        del G
+
+    # the same problem through the other paths (overlap accounting)
+    variants_ms = None
+    if not args.no_compare:
+        variants_ms = {}
+        for v in ("fused", "staged", "unfused", "skinny"):
+            if v == "skinny" and (w.dtype == 2 or w.m > 1024):
+                continue
+            if v in ("staged", "unfused") and (w.k * w.elem_bytes) % 16:
+                continue
+            st = {"pvalue": w.pvalue or 2, "nbuf": w.nbuf or 2} if v == "staged" else {}
+            vp = agmm.Plan(w.num_shards, w.m_per_shard, w.k, w.n_local, w.dtype,
+                           w.rhs_transpose, variant=v, **st)
+            for i in range(2):
+                sh, Bt, C = sets[i % nsets]
+                vp.run(sh, Bt, C, stream=stream)
+            torch.cuda.synchronize()
+            vs, ve = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            nst = max(5, args.steps // 2)
+            vs.record(stream)
+            for i in range(nst):
+                sh, Bt, C = sets[i % nsets]
+                vp.run(sh, Bt, C, stream=stream)
+            ve.record(stream)
+            torch.cuda.synchronize()
+            variants_ms[v] = round(vs.elapsed_time(ve) / nst, 5)
+            vp.close()
+        if "unfused" in variants_ms and "staged" in variants_ms:
+            variants_ms["unfused_over_staged"] = round(variants_ms["unfused"] / variants_ms["staged"], 4)
+        if gather and "unfused" in variants_ms and "staged" in variants_ms:
+            variants_ms["hidden_gather_frac"] = round(
+                (variants_ms["unfused"] - variants_ms["staged"]) / gather["ms"], 4)
+
+    plan.close()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        # bounded sample: whole output rows (all n_local columns, full k),
+        # grown until about --cpu-seconds of oracle work.
+        rows = [0]
+        t_cpu = 0.0
+        nrows = 1
+        while True:
+            sel = [int(r) for r in np.linspace(0, w.m - 1, nrows)]
+            t1 = time.time()
+            oracle.agmm_f64(shards_np, B_np, w.dtype, w.rhs_transpose, rows=sel)
+            t_cpu = time.time() - t1
+            rows = sel
+            if t_cpu > args.cpu_seconds / 4 or nrows >= w.m:
+                break
+            nrows = min(w.m, max(nrows * 2, int(nrows * (args.cpu_seconds / 4) / max(t_cpu, 1e-3))))
+        cpu_flops = 2.0 * len(rows) * w.k * w.n_local
+        cpu = {"value": round(cpu_flops / t_cpu / 1e12, 6), "unit": "TFLOP/s",
+               "cores": oracle.num_threads(), "kind": "oracle",
+               "sample": f"{len(rows)} of {w.m} output rows (all {w.n_local} columns, full k={w.k}), "
+                         f"{t_cpu:.2f} s incl. decoding B"}
+
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": I.DTYPE_NAMES[w.dtype], "data": "synthetic (seeded, N(0,1/sqrt(k)) or U[-1,1])",
+        "config": {**w.describe(), "variant": used, "buffer_sets": nsets},
+        "frac_of_peak": round(value / PEAK_TFLOPS[w.dtype], 4),
+        "roofline": roofline, "gather": gather, "variants_ms": variants_ms,
+        "cpu_baseline": cpu, "input_gen_s": round(gen_s, 1),
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

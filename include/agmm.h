@@ -1,0 +1,219 @@
+/*
+ * agmm — all-gather fused matmul for AMD Instinct MI355X (gfx950).
+ *
+ * One GPU's share of the all-gather matmul
+ *
+ *     C[m, n_local] = concat_r(A_r[m_per_shard, k]) @ B[k, n_local]
+ *     m = num_shards * m_per_shard
+ *
+ * as the tpu-inference page defines it ("all_gather_matmul.py",
+ * `all_gather_matmul`: the result is all-gather(x, axis=0) @ y, x sharded by
+ * rows over the ring, y sharded by columns so each device owns n_local of
+ * them and produces C[:, n_local]) and as the Triton-distributed-Ascend
+ * tutorial "AllGather-GEMM" checks it (golden `torch_allgather_gemm`:
+ * all-gather, concatenate along dim 0, matmul).  With rhs_transpose, B is
+ * stored [n_local, k] and contracted on its second dimension (tpu-inference
+ * `_do_mxu`, dot_general over dims ((1,),(1,))).
+ *
+ * On one GPU the peers' shards are separate device buffers; the caller
+ * passes their addresses as a table (the role the per-peer pointer table
+ * plays in the Mosaic-GPU launch_context page).
+ *
+ * Conventions for every entry point:
+ *   - Device pointers are HIP device addresses (hipMalloc / torch CUDA
+ *     tensors).  Host pointers are marked "host".
+ *   - Layouts are dense row-major: shard r is [m_per_shard, k] (leading
+ *     dimension k); B is [k, n_local] (ld n_local) or, with rhs_transpose,
+ *     [n_local, k] (ld k); C is [m, n_local] (ld n_local), and row
+ *     r*m_per_shard + i of C is row i of shard r.
+ *   - Element type: every operand has the plan's dtype; C too (the cast
+ *     rounds to nearest even).  bf16/fp16 accumulate in fp32; fp32 inputs
+ *     accumulate in fp64 and round once to fp32.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the legacy default
+ *     stream).  Work is enqueued asynchronously: it starts after everything
+ *     earlier on `stream`, and later work on `stream` sees its results.
+ *   - Errors: functions return an agmm_status (or NULL for plan creation)
+ *     and record a thread-local status and message readable with
+ *     agmm_last_status() / agmm_last_error().  No entry point aborts the
+ *     process.  Invalid input is reported, never silently computed.
+ *   - Ownership: the caller owns every buffer it passes and the stream; it
+ *     must keep buffers alive until the enqueued work has finished.  The plan
+ *     owns its workspace, its internal streams and events.
+ */
+#ifndef AGMM_H
+#define AGMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct agmm_plan agmm_plan;
+typedef agmm_plan *agmm_plan_t;
+
+typedef enum {
+  AGMM_BF16 = 0,
+  AGMM_FP16 = 1,
+  AGMM_FP32 = 2
+} agmm_dtype;
+
+typedef enum {
+  AGMM_OK = 0,
+  AGMM_ERR_INVALID_ARG = 1, /* NULL pointer, size < 1, unknown key or dtype */
+  AGMM_ERR_UNSUPPORTED = 2, /* valid request this build does not implement
+                               (alignment, shape rule, too many shards) */
+  AGMM_ERR_OOM = 3,         /* device allocation failed */
+  AGMM_ERR_HIP = 4          /* a HIP runtime call or launch failed */
+} agmm_status;
+
+/* Paths an agmm_run can take (key "variant" of agmm_plan_set_int). */
+typedef enum {
+  AGMM_VARIANT_AUTO = 0,    /* plan picks: fused, or split-K for skinny m */
+  AGMM_VARIANT_FUSED = 1,   /* GEMM reads A rows straight from the shard
+                               buffers; no gathered copy (Ascend tutorial,
+                               "AllGather + GEMM (Fused Distributed Kernel)":
+                               no intermediate write between the phases) */
+  AGMM_VARIANT_STAGED = 2,  /* chunked gather into a ring of nbuf slots on a
+                               second stream, overlapped with the GEMM of the
+                               previous chunk (Ascend tutorial, "Double
+                               Buffering" and "pvalue Parameter") */
+  AGMM_VARIANT_UNFUSED = 3, /* gather all of A, then one GEMM, one stream (the
+                               decomposed approach the tutorial compares to) */
+  AGMM_VARIANT_SKINNY = 4   /* split-K GEMM from the shard buffers with an
+                               in-kernel fixed-order reduction (small m) */
+} agmm_variant;
+
+/*
+ * Check a problem description without touching the GPU.
+ * Returns AGMM_OK if agmm_plan_create would accept it, otherwise the status
+ * it would fail with (and sets agmm_last_error()).
+ *   num_shards    1 .. 64
+ *   m_per_shard, k, n_local >= 1, with m*k, k*n_local, m*n_local < 2^31
+ *   dtype         agmm_dtype
+ *   rhs_transpose 0: B is [k, n_local]; 1: B is [n_local, k]
+ * bf16/fp16 additionally need k % 8 == 0 (16-byte rows for vector loads) and,
+ * without rhs_transpose, n_local % 8 == 0; fp32 needs k % 4 == 0 for the
+ * gather copy used by the staged/unfused variants.  (The tpu-inference
+ * page's own `validate_inputs` rules — 2-D inputs, equal dtypes, matching k —
+ * are implied by this signature; its TPU tiling rules are not imposed.)
+ */
+int agmm_plan_validate(int num_shards, int64_t m_per_shard, int64_t k, int64_t n_local,
+                       int dtype, int rhs_transpose);
+
+/*
+ * Create a plan on the current HIP device.  Validates as above, picks tiles
+ * and the default variant, and allocates everything a run needs (ring
+ * workspace, split-K partials, tile-order tables, internal stream and
+ * events), so agmm_run itself never allocates.
+ * Returns NULL on failure (see agmm_last_status / agmm_last_error).
+ */
+agmm_plan_t agmm_plan_create(int num_shards, int64_t m_per_shard, int64_t k, int64_t n_local,
+                             int dtype, int rhs_transpose);
+
+/*
+ * Enqueue C = concat(A_r) @ B (or @ B^T) on `stream`.
+ *   shard_ptrs  host array of num_shards device pointers, shard r = [m_per_shard, k];
+ *               read during the call only (may be freed on return)
+ *   B           device, [k, n_local] or [n_local, k] (rhs_transpose)
+ *   C           device, [m, n_local]; must not overlap any input
+ *   stream      hipStream_t as void*
+ * All device pointers must be 16-byte aligned.
+ * Not safe to call concurrently on one plan from two host threads or on two
+ * streams at once (the ring and split-K scratch are shared); serial calls on
+ * different streams are safe (the plan orders them with its events).
+ * Returns AGMM_OK, AGMM_ERR_INVALID_ARG (NULL plan/pointer),
+ * AGMM_ERR_UNSUPPORTED (misaligned pointer) or AGMM_ERR_HIP (launch failed).
+ */
+int agmm_run(agmm_plan_t plan, const void *const *shard_ptrs, const void *B, void *C,
+             void *stream);
+
+/*
+ * Enqueue only the all-gather: gathered[r*m_per_shard + i, :] = shard r row i,
+ * a bit-exact copy.  gathered is a device buffer [m, k] of the plan's dtype,
+ * 16-byte aligned.  (The gathered operand the tpu-inference kernel returns as
+ * its second output, `x_hbm_scratch`.)  Same stream rules as agmm_run.
+ */
+int agmm_gather(agmm_plan_t plan, const void *const *shard_ptrs, void *gathered, void *stream);
+
+/*
+ * Enqueue C = G @ B for an already gathered operand G [m, k] (device), e.g.
+ * the output of agmm_gather or a staged run — the second half of the
+ * tpu-inference page's "split n" idea (matmul the gathered x against another
+ * column block of y without gathering again).  Shapes and dtype are the
+ * plan's.  Same rules as agmm_run.
+ */
+int agmm_run_gathered(agmm_plan_t plan, const void *gathered, const void *B, void *C,
+                      void *stream);
+
+/*
+ * Tune a plan.  Keys (value ranges):
+ *   "variant"       agmm_variant
+ *   "pvalue"        >= 1: tile-rows of each shard per staged chunk
+ *   "nbuf"          >= 1: ring slots for the staged variant
+ *   "tile"          0: 256x256, 1: 128x128, 2: 256x128 output tile (bf16/fp16)
+ *   "splits"        >= 1: k-splits for the skinny variant
+ *   "local_shard"   0 .. num_shards-1: where the ring order starts
+ *   "order"         0: ring order from local_shard, 1: natural order
+ *   "group_m"       >= 1: row blocks walked together (L2 reuse)
+ *   "xcd_remap"     0/1: keep consecutive tiles on one XCD
+ *   "copy_wgs"      >= 0: workgroups of the staged gather copy (0 = auto)
+ *   "debug_keep_slots" 0/1: staged variant uses one slot per chunk (nothing
+ *                   is overwritten; for inspection by agmm_plan_slot_ptr)
+ * Changing a key that affects the workspace reallocates it (synchronously).
+ * Returns AGMM_OK, AGMM_ERR_INVALID_ARG (unknown key / out of range) or
+ * AGMM_ERR_OOM.
+ */
+int agmm_plan_set_int(agmm_plan_t plan, const char *key, int64_t value);
+
+/* Read a plan setting (keys above, plus "num_chunks", "rows_per_chunk",
+ * "tile_bm", "tile_bn", "num_row_blocks" and the resolved "variant_used").
+ * value: host pointer.  Returns AGMM_OK or AGMM_ERR_INVALID_ARG. */
+int agmm_plan_get_int(agmm_plan_t plan, const char *key, int64_t *value);
+
+/* Bytes of device workspace the plan holds (ring, partials, tables). */
+size_t agmm_plan_workspace_bytes(agmm_plan_t plan);
+
+/* Device address of ring slot `slot` ([num_shards][rows_per_chunk][k]) or
+ * NULL; for tests of the staged gather. */
+const void *agmm_plan_slot_ptr(agmm_plan_t plan, int slot);
+
+/*
+ * Row-block visit order the plan's GEMM uses (host array `out` of at least
+ * "num_row_blocks" entries for chunk `chunk`; chunk 0 for non-staged).
+ * Ring order from local shard r0: step s takes the first half of shard
+ * (r0+s) mod N and then the second half of shard (r0-s) mod N (tpu-inference
+ * `_all_gather_kernel`: the bidirectional ring sends the top half of a shard
+ * left and the bottom half right, so at step s a device holds the top half of
+ * shard d+s and the bottom half of shard d-s; `_do_o_local_copy` writes them
+ * to those rows).  A row block waits for the latest of its rows.
+ * Returns the number of entries written, or -1 on error.
+ */
+int agmm_plan_tile_order(agmm_plan_t plan, int chunk, int32_t *out, int capacity);
+
+/*
+ * Per-launch timing of the plan's main GEMM kernel with HIP events recorded
+ * on the stream that kernel is launched on.  begin: clear and enable;
+ * read: wait for the recorded events and return the summed kernel time (ms)
+ * and the number of launches timed; end: disable.
+ */
+int agmm_plan_timing_begin(agmm_plan_t plan);
+int agmm_plan_timing_read(agmm_plan_t plan, double *total_ms, int64_t *launches);
+int agmm_plan_timing_end(agmm_plan_t plan);
+
+/* Wait for the plan's internal streams, free its workspace. NULL is a no-op. */
+void agmm_plan_destroy(agmm_plan_t plan);
+
+/* Thread-local status / message of the last failing call (AGMM_OK / "" if none). */
+int agmm_last_status(void);
+const char *agmm_last_error(void);
+
+/* Library version string. */
+const char *agmm_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* AGMM_H */

@@ -1,0 +1,86 @@
+"""Host-only checks of the C ABI (no GPU): the library loads, exports every
+symbol include/agmm.h declares, and rejects malformed problems with the
+documented status codes and messages."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import all_gather_gemm_agmm_amd as agmm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "agmm.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(agmm_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = agmm.load_library()
+    names = declared_functions()
+    assert len(names) >= 15
+    for name in names:
+        assert hasattr(lib, name), f"{name} declared in agmm.h but not exported"
+    # ...and the Python binding covers exactly the declared set
+    assert sorted(n for n, _, _ in agmm.EXPORTS) == names
+
+
+def test_version():
+    assert "gfx950" in agmm.agmm_version()
+
+
+def test_validate_accepts_the_workloads():
+    from all_gather_gemm_agmm_amd import inputs as I
+    for w in I.WORKLOADS.values():
+        assert agmm.agmm_plan_validate(w.num_shards, w.m_per_shard, w.k, w.n_local, w.dtype,
+                                       w.rhs_transpose) == agmm.AGMM_OK
+
+
+@pytest.mark.parametrize("args,status,fragment", [
+    ((0, 4, 8, 8, 0, 0), agmm.AGMM_ERR_INVALID_ARG, "num_shards"),
+    ((65, 4, 8, 8, 0, 0), agmm.AGMM_ERR_UNSUPPORTED, "maximum"),
+    ((2, 0, 8, 8, 0, 0), agmm.AGMM_ERR_INVALID_ARG, "sizes"),
+    ((2, 4, 0, 8, 0, 0), agmm.AGMM_ERR_INVALID_ARG, "sizes"),
+    ((2, 4, 8, -1, 0, 0), agmm.AGMM_ERR_INVALID_ARG, "sizes"),
+    ((2, 4, 8, 8, 7, 0), agmm.AGMM_ERR_INVALID_ARG, "dtype"),
+    ((2, 4, 8, 8, 0, 2), agmm.AGMM_ERR_INVALID_ARG, "rhs_transpose"),
+    ((2, 4, 12, 8, 0, 1), agmm.AGMM_ERR_UNSUPPORTED, "k % 8"),
+    ((2, 4, 16, 12, 1, 0), agmm.AGMM_ERR_UNSUPPORTED, "n_local % 8"),
+    ((2, 1 << 29, 8, 8, 0, 0), agmm.AGMM_ERR_UNSUPPORTED, "too large"),
+])
+def test_validate_rejects(args, status, fragment):
+    assert agmm.load_library().agmm_plan_validate(*args) == status
+    assert agmm.agmm_last_status() == status
+    assert fragment in agmm.agmm_last_error()
+
+
+def test_validate_accepts_ragged_and_fp32_odd_shapes():
+    assert agmm.agmm_plan_validate(3, 100, 200, 136, 0, 0) == agmm.AGMM_OK
+    assert agmm.agmm_plan_validate(3, 100, 200, 130, 1, 1) == agmm.AGMM_OK  # n free with B^T
+    assert agmm.agmm_plan_validate(2, 5, 7, 3, 2, 0) == agmm.AGMM_OK        # fp32: any shape
+    assert agmm.agmm_last_status() == agmm.AGMM_OK and agmm.agmm_last_error() == ""
+
+
+def test_null_handles_are_rejected_without_touching_the_gpu():
+    lib = agmm.load_library()
+    assert lib.agmm_run(None, None, None, None, None) == agmm.AGMM_ERR_INVALID_ARG
+    assert "plan is NULL" in agmm.agmm_last_error()
+    assert lib.agmm_gather(None, None, None, None) == agmm.AGMM_ERR_INVALID_ARG
+    assert lib.agmm_run_gathered(None, None, None, None, None) == agmm.AGMM_ERR_INVALID_ARG
+    assert lib.agmm_plan_set_int(None, b"pvalue", 2) == agmm.AGMM_ERR_INVALID_ARG
+    v = ctypes.c_int64(0)
+    assert lib.agmm_plan_get_int(None, b"pvalue", ctypes.byref(v)) == agmm.AGMM_ERR_INVALID_ARG
+    assert lib.agmm_plan_workspace_bytes(None) == 0
+    assert not lib.agmm_plan_slot_ptr(None, 0)
+    assert lib.agmm_plan_tile_order(None, 0, None, 0) == -1
+    assert lib.agmm_plan_timing_begin(None) == agmm.AGMM_ERR_INVALID_ARG
+    lib.agmm_plan_destroy(None)  # no-op
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    with pytest.raises(RuntimeError, match="no CPU fallback"):
+        agmm.load_library(str(tmp_path / "libagmm.so"))

@@ -1,0 +1,305 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Tolerance (stated for the all-gather matmul workloads): per element
+|C_gpu - C_ref| / (|C_ref| + 1e-3) <= 2e-2 for bf16/fp16 inputs and <= 1e-5
+for fp32 inputs, C_ref being the oracle's float64 result.  Gathered operands
+and schedule-invariance checks are bit-exact.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import all_gather_gemm_agmm_amd as agmm
+from all_gather_gemm_agmm_amd import inputs as I
+from gpu_util import BOUND, rel_err, sample_rows, to_bits, to_device, torch_dtype
+
+pytestmark = pytest.mark.gpu
+
+BF16, FP16, FP32 = I.DTYPE_BF16, I.DTYPE_FP16, I.DTYPE_FP32
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    agmm.load_library()
+
+
+def make_case(N, m_s, k, n, dtype, rt, seed, dist="normal"):
+    w = I.custom_workload(N, m_s, k, n, dtype, rt, dist=dist, wid=seed)
+    shards, B = I.make_inputs(w)
+    return w, shards, B
+
+
+def run_variant(w, shards_d, B_d, variant, **settings):
+    plan = agmm.Plan(w.num_shards, w.m_per_shard, w.k, w.n_local, w.dtype, w.rhs_transpose,
+                     variant=variant, **settings)
+    try:
+        C = plan.run(shards_d, B_d)
+        torch.cuda.synchronize()
+        return C, plan.get("variant_used")
+    finally:
+        plan.close()
+
+
+def check_against_oracle(w, shards, B, C_d, rows=None):
+    ref = oracle.agmm_f64(shards, B, w.dtype, w.rhs_transpose, rows=rows)
+    Cb = to_bits(C_d if rows is None else C_d[torch.tensor(rows, device=C_d.device)])
+    got = oracle.decode(Cb, w.dtype)
+    err = rel_err(got, ref)
+    assert np.all(np.isfinite(got))
+    assert err <= BOUND[w.dtype], f"max rel err {err:.3e} > {BOUND[w.dtype]}"
+    return err
+
+
+# ---------------------------------------------------------------- small and ragged
+SMALL = [
+    # N, m_s, k, n, dtype, rhs_transpose
+    (2, 64, 256, 128, FP32, False),
+    (3, 100, 200, 136, BF16, False),
+    (3, 100, 200, 130, FP16, True),
+    (2, 300, 136, 264, BF16, True),
+    (4, 77, 520, 96, FP16, False),
+    (1, 513, 64, 257, BF16, True),
+    (5, 1, 8, 8, BF16, False),
+    (2, 33, 36, 5, FP32, True),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: "x".join(map(str, c[:4])) + f"_{I.DTYPE_NAMES[c[4]]}_rt{int(c[5])}")
+@pytest.mark.parametrize("variant", ["fused", "staged", "unfused", "skinny"])
+def test_small_ragged(case, variant):
+    N, m_s, k, n, dtype, rt = case
+    if variant in ("staged", "unfused") and (k * (4 if dtype == FP32 else 2)) % 16:
+        pytest.skip("gather copy needs 16-byte rows")
+    w, shards, B = make_case(N, m_s, k, n, dtype, rt, seed=17 + N + m_s)
+    shards_d = [to_device(s, dtype) for s in shards]
+    B_d = to_device(B, dtype)
+    settings = {"pvalue": 1} if variant == "staged" else {}
+    C, used = run_variant(w, shards_d, B_d, variant, **settings)
+    check_against_oracle(w, shards, B, C)
+
+
+@pytest.mark.parametrize("tile", [0, 1, 2])
+@pytest.mark.parametrize("dtype,rt", [(BF16, False), (BF16, True), (FP16, False), (FP16, True)])
+def test_tiles_ragged(tile, dtype, rt):
+    w, shards, B = make_case(3, 200, 328, 392, dtype, rt, seed=900 + tile)
+    shards_d = [to_device(s, dtype) for s in shards]
+    B_d = to_device(B, dtype)
+    C, _ = run_variant(w, shards_d, B_d, "fused", tile=tile)
+    check_against_oracle(w, shards, B, C)
+
+
+# ------------------------------------------------------------- the five workloads
+def workload_inputs(wid):
+    w = I.WORKLOADS[wid]
+    shards, B = I.make_inputs(w)
+    return w, shards, B, [to_device(s, w.dtype) for s in shards], to_device(B, w.dtype)
+
+
+@pytest.mark.parametrize("variant", ["auto", "fused", "staged", "unfused"])
+def test_workload1_fp32(variant):
+    w, shards, B, sd, bd = workload_inputs(1)
+    C, _ = run_variant(w, sd, bd, variant)
+    check_against_oracle(w, shards, B, C)
+
+
+@pytest.mark.parametrize("variant", ["auto", "fused", "staged", "unfused", "skinny"])
+def test_workload2(variant):
+    w, shards, B, sd, bd = workload_inputs(2)
+    C, _ = run_variant(w, sd, bd, variant)
+    check_against_oracle(w, shards, B, C)
+
+
+@pytest.mark.parametrize("variant", ["auto", "fused", "skinny", "unfused"])
+def test_workload3_skinny(variant):
+    w, shards, B, sd, bd = workload_inputs(3)
+    C, used = run_variant(w, sd, bd, variant)
+    if variant == "auto":
+        assert used == agmm.AGMM_VARIANT_SKINNY
+    check_against_oracle(w, shards, B, C)
+
+
+@pytest.mark.parametrize("variant", ["staged", "fused", "unfused"])
+def test_workload4_sampled(variant):
+    w, shards, B, sd, bd = workload_inputs(4)
+    settings = {"pvalue": w.pvalue, "nbuf": w.nbuf} if variant == "staged" else {}
+    C, _ = run_variant(w, sd, bd, variant, **settings)
+    rows = sample_rows(w.num_shards, w.m_per_shard, per_shard=3, seed=4)
+    check_against_oracle(w, shards, B, C, rows=rows)
+
+
+def test_workload5_fused_sampled():
+    w, shards, B, sd, bd = workload_inputs(5)
+    C, used = run_variant(w, sd, bd, "fused")
+    rows = sample_rows(w.num_shards, w.m_per_shard, per_shard=2, seed=5)
+    check_against_oracle(w, shards, B, C, rows=rows)
+    # a property that holds at any size: every output finite and C not all zero
+    assert torch.isfinite(C.float()).all().item()
+
+
+# ---------------------------------------------------------------- gather, exact
+@pytest.mark.parametrize("dtype", [BF16, FP16, FP32])
+def test_gather_bit_exact(dtype):
+    w, shards, B = make_case(5, 37, 264, 8, dtype, False, seed=77)
+    sd = [to_device(s, dtype) for s in shards]
+    plan = agmm.Plan(w.num_shards, w.m_per_shard, w.k, w.n_local, dtype, False)
+    try:
+        G = plan.gather(sd)
+        torch.cuda.synchronize()
+    finally:
+        plan.close()
+    assert np.array_equal(to_bits(G), oracle.gather(shards, dtype))
+
+
+def test_staged_slots_bit_exact():
+    """debug_keep_slots: every chunk keeps its own slot; each equals the
+    oracle gather's rows of that chunk."""
+    w, shards, B = make_case(3, 300, 128, 64, BF16, True, seed=78)
+    sd = [to_device(s, BF16) for s in shards]
+    bd = to_device(B, BF16)
+    plan = agmm.Plan(3, 300, 128, 64, BF16, True, variant="staged", pvalue=1, tile=1,
+                     debug_keep_slots=1)
+    try:
+        C = plan.run(sd, bd)
+        torch.cuda.synchronize()
+        R = plan.get("rows_per_chunk")
+        nch = plan.get("num_chunks")
+        assert R == 128 and nch == 3
+        G = oracle.gather(shards, BF16)
+        for c in range(nch):
+            ptr = agmm.agmm_plan_slot_ptr(plan.handle, c)
+            rows_c = min(R, 300 - c * R)
+            nbytes = 3 * rows_c * 128 * 2
+            host = np.empty(nbytes // 2, dtype=np.uint16)
+            import ctypes
+            hip = ctypes.CDLL("libamdhip64.so")
+            hip.hipMemcpy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int]
+            assert hip.hipMemcpy(host.ctypes.data, ptr, nbytes, 2) == 0  # device -> host
+            host = host.reshape(3, rows_c, 128)
+            for r in range(3):
+                want = G[r * 300 + c * R: r * 300 + c * R + rows_c]
+                assert np.array_equal(host[r], want), (c, r)
+    finally:
+        plan.close()
+    check_against_oracle(w, shards, B, C)
+
+
+# -------------------------------------------------- schedule invariance, exact
+def test_schedule_orders_bit_identical():
+    w, shards, B = make_case(4, 384, 256, 512, BF16, False, seed=79)
+    sd = [to_device(s, BF16) for s in shards]
+    bd = to_device(B, BF16)
+    outs = []
+    for order, r0 in [(1, 0), (0, 0), (0, 1), (0, 3)]:
+        C, _ = run_variant(w, sd, bd, "fused", order=order, local_shard=r0, tile=0)
+        outs.append(to_bits(C))
+    for o in outs[1:]:
+        assert np.array_equal(outs[0], o)
+    # same microkernel and tile: fused, staged and unfused agree bit for bit
+    Cs, _ = run_variant(w, sd, bd, "staged", pvalue=1, tile=0)
+    Cu, _ = run_variant(w, sd, bd, "unfused", tile=0)
+    assert np.array_equal(outs[0], to_bits(Cs))
+    assert np.array_equal(outs[0], to_bits(Cu))
+    check_against_oracle(w, shards, B, Cs)
+
+
+def test_ring_order_table():
+    plan = agmm.Plan(4, 512, 64, 128, BF16, False, variant="fused", tile=0, local_shard=1)
+    try:
+        order = plan.tile_order()
+    finally:
+        plan.close()
+    # 4 shards x 2 row blocks of 256: top halves are row blocks 2r, bottom 2r+1.
+    # step 0: top of shard 1, bottom of shard 1; step 1: top of 2, bottom of 0;
+    # step 2: top of 3, bottom of 3; step 3: top of 0, bottom of 2.
+    assert order == [2, 3, 4, 1, 6, 7, 0, 5]
+
+
+def test_identity_returns_gathered_exactly():
+    for dtype, rt in [(BF16, False), (FP16, True), (FP32, False)]:
+        N, m_s, k = 3, 70, 64
+        w, shards, _ = make_case(N, m_s, k, k, dtype, rt, seed=80)
+        eye = I.to_storage_bits(np.eye(k, dtype=np.float32), dtype)
+        sd = [to_device(s, dtype) for s in shards]
+        C, _ = run_variant(w, sd, to_device(eye, dtype), "fused")
+        assert np.array_equal(to_bits(C), oracle.gather(shards, dtype))
+
+
+def test_fp16_subnormal_outputs():
+    """Outputs deep in the fp16 subnormal range must not be flushed."""
+    N, m_s, k, n = 2, 64, 64, 64
+    rng = np.random.default_rng(81)
+    shards = [I.to_storage_bits((rng.standard_normal((m_s, k)) * 2e-3).astype(np.float32), FP16)
+              for _ in range(N)]
+    B = I.to_storage_bits((rng.standard_normal((k, n)) * 2e-3).astype(np.float32), FP16)
+    w = I.custom_workload(N, m_s, k, n, FP16, False)
+    C, _ = run_variant(w, [to_device(s, FP16) for s in shards], to_device(B, FP16), "fused")
+    ref = oracle.agmm_f64(shards, B, FP16, False)
+    got = oracle.decode(to_bits(C), FP16)
+    assert (np.abs(ref) < 2.0 ** -14).mean() > 0.5      # mostly subnormal outputs
+    assert (np.abs(got) > 0).mean() > 0.9                # and they survived
+    assert rel_err(got, ref) <= BOUND[FP16]
+
+
+def test_repeated_runs_fresh_inputs():
+    """Back-to-back runs with new inputs (staged ring reuse, split-K counters
+    reset): every run matches its own oracle."""
+    for variant, settings in [("staged", {"pvalue": 1, "tile": 1, "nbuf": 2}), ("skinny", {})]:
+        plan = None
+        try:
+            for it in range(3):
+                w, shards, B = make_case(4, 160 if variant == "staged" else 24, 192, 256, BF16,
+                                         True, seed=300 + it)
+                if plan is None:
+                    plan = agmm.Plan(w.num_shards, w.m_per_shard, w.k, w.n_local, BF16, True,
+                                     variant=variant, **settings)
+                C = plan.run([to_device(s, BF16) for s in shards], to_device(B, BF16))
+                torch.cuda.synchronize()
+                check_against_oracle(w, shards, B, C)
+        finally:
+            if plan is not None:
+                plan.close()
+
+
+def test_run_gathered_matches_fused():
+    w, shards, B = make_case(2, 256, 512, 256, FP16, True, seed=82)
+    sd = [to_device(s, FP16) for s in shards]
+    bd = to_device(B, FP16)
+    plan = agmm.Plan(2, 256, 512, 256, FP16, True, variant="fused", tile=1)
+    try:
+        G = plan.gather(sd)
+        C1 = plan.run_gathered(G, bd)
+        C2 = plan.run(sd, bd)
+        torch.cuda.synchronize()
+    finally:
+        plan.close()
+    assert np.array_equal(to_bits(C1), to_bits(C2))
+    check_against_oracle(w, shards, B, C1)
+
+
+def test_run_rejects_misaligned_pointer():
+    w, shards, B = make_case(2, 8, 64, 64, BF16, False, seed=83)
+    sd = [to_device(s, BF16) for s in shards]
+    bd = to_device(B, BF16)
+    C = torch.empty((16, 64), dtype=torch.bfloat16, device="cuda")
+    plan = agmm.Plan(2, 8, 64, 64, BF16, False)
+    try:
+        with pytest.raises(agmm.AgmmError) as ei:
+            agmm.agmm_run(plan.handle, [sd[0].data_ptr() + 2, sd[1].data_ptr()], bd.data_ptr(),
+                          C.data_ptr(), torch.cuda.current_stream().cuda_stream)
+        assert ei.value.status == agmm.AGMM_ERR_UNSUPPORTED
+        with pytest.raises(agmm.AgmmError) as ei:
+            agmm.agmm_run(plan.handle, [sd[0].data_ptr(), 0], bd.data_ptr(), C.data_ptr(),
+                          torch.cuda.current_stream().cuda_stream)
+        assert ei.value.status == agmm.AGMM_ERR_INVALID_ARG
+    finally:
+        plan.close()
+
+
+def test_oom_hook_reports_status(monkeypatch):
+    monkeypatch.setenv("AGMM_TEST_FAIL_ALLOC", "1")
+    with pytest.raises(agmm.AgmmError) as ei:
+        agmm.Plan(2, 512, 256, 256, BF16, False, variant="unfused")
+    assert ei.value.status == agmm.AGMM_ERR_OOM
