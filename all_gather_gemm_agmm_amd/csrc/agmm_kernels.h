@@ -65,7 +65,7 @@ enum TileCfg : int {
 };
 int tile_bm(int cfg);
 int tile_bn(int cfg);
-constexpr int kTileBK = 64;
+constexpr int kTileBK = 32;
 
 // bf16/fp16 MFMA GEMM (16-bit inputs, fp32 accumulate, output in the input dtype).
 hipError_t launch_gemm_mfma(const GemmProblem& p, int tile_cfg, int dtype, bool rhs_transpose,

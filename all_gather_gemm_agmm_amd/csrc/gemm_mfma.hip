@@ -16,15 +16,20 @@
 //  * v_mfma_f32_32x32x16_{bf16,f16}: the B tile is the MFMA's first operand
 //    and the A tile its second, so each lane ends up owning 4 consecutive
 //    output columns of one row (8-byte packed stores in the epilogue).
-//  * A and k-contiguous B tiles go global -> LDS directly
-//    (global_load_lds_dwordx4, no register staging).  B stored k x n is
-//    loaded to registers in 8x8 blocks, transposed in registers and written
-//    to LDS in the same k-contiguous layout.
-//  * LDS rows are 64 elements (128 bytes, 8 chunks of 16 bytes); chunk c of
-//    row r sits at position c ^ ((r ^ (r >> 3)) & 7), which keeps both the
-//    MFMA fragment reads and the transposed B writes free of bank conflicts.
-//  * Two LDS stages: the loads of k-tile i+1 are in flight while the MFMAs of
-//    k-tile i run.
+//  * Every operand tile goes global -> LDS directly (global_load_lds_dwordx4:
+//    lane i of a wave writes bytes [16i, 16i+16) of a 1 KiB LDS block, so the
+//    LDS swizzle is chosen by which global chunk each lane fetches).
+//  * k-tiles of 32 elements in a ring of 3-4 LDS stages: the loads of the
+//    next 2-3 tiles are in flight while tile i is multiplied; each wave waits
+//    only for the tile it needs next (partial vmcnt), one barrier per k-tile
+//    placed between the two k16 halves, and the LDS reads and global->LDS
+//    loads are interleaved one by one with the MFMAs (sched_group_barrier).
+//  * k-contiguous tiles (A, and B when stored n x k): rows of 64 bytes, chunk
+//    c of row r at position c ^ ((r >> 2) & 3).  B stored k x n
+//    keeps its n-contiguous rows in LDS (chunk c of k-row r at c ^ f(r & 3),
+//    f = {0, 4, 10, 14}) and is transposed on the way out by
+//    ds_read_b64_tr_b16.  Both layouts are free of LDS bank conflicts for
+//    the fragment reads.
 //  * Rows past m, columns past n and k past the end are fed from a zero
 //    block, so ragged tails need no masking inside the main loop.
 //  * Tile order: XCD-aware remap of the workgroup id, grouped row blocks for
@@ -42,20 +47,27 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
 
 typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+typedef __attribute__((address_space(3))) char lds_char_t;
 
 // 16 zero bytes: the source of every out-of-range 16-byte chunk.
 __device__ __attribute__((aligned(64))) const uint32_t g_zero_chunk[16] = {0};
 
 constexpr int kThreads = 256;
-constexpr int kBK = kTileBK;        // 64 elements = 128 bytes per LDS row
-constexpr int kRowBytes = kBK * 2;
+constexpr int kBK = kTileBK;         // 32 elements
+constexpr int kKRow = kBK * 2;       // bytes of a k-contiguous LDS row (64)
 
-__device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
+__device__ __forceinline__ int swz_k(int row) { return (row >> 2) & 3; }
+__device__ __forceinline__ int swz_n(int krow) {
+  // 0, 4, 10, 14 for krow % 4 = 0..3
+  const int r = krow & 3;
+  return (r << 2) ^ ((r >> 1) << 1);
+}
 
 template <int DT>
 __device__ __forceinline__ f32x16_t mfma32(u32x4_t a, u32x4_t b, f32x16_t c) {
@@ -91,8 +103,44 @@ __device__ __forceinline__ uint16_t cvt1(float v) {
   }
 }
 
-__device__ __forceinline__ void load_lds16(const void* gsrc, char* lds_base_uniform) {
-  __builtin_amdgcn_global_load_lds(gsrc, (lds_void_t*)lds_base_uniform, 16, 0, 0);
+// One 16-byte-per-lane global -> LDS load: lane i of the wave writes bytes
+// [16i, 16i+16) of the 1 KiB LDS block at `lds_block` (wave-uniform).
+// Issued as inline assembly on purpose: the compiler cannot tell which LDS
+// bytes such a load writes, so it would otherwise wait for every one of
+// them (vmcnt(0)) before the next LDS read anywhere in the kernel, which
+// defeats the multi-stage pipeline.  The kernel instead waits explicitly for
+// exactly the k-tile it is about to read (wait_vmcnt + barrier).
+__device__ __forceinline__ void load_lds16(const void* gsrc, char* lds_block) {
+  const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_char_t*)lds_block);
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(gsrc), "s"(lds)
+               : "m0");
+}
+
+__device__ __forceinline__ u32x2_t read_tr(const char* p) {
+  i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(lds_char_t*)p);
+  return __builtin_bit_cast(u32x2_t, v);
+}
+
+// vmcnt(n) with the other counters left alone (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Workgroup barrier without the release/acquire fence of __syncthreads():
+// that fence would also wait for the in-flight global->LDS loads of the
+// next k-tiles.  Completion of the loads a k-tile needs is awaited
+// explicitly (wait_vmcnt) before this barrier; the empty asm statements keep
+// the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void block_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 // Logical tile visited by this workgroup.
@@ -114,26 +162,32 @@ __device__ __forceinline__ void tile_coords(const TileOrder& o, int wg, int nwg,
   rb = o.rb_order ? o.rb_order[rbi] : rbi;
 }
 
-template <int BM, int BN, int DT, bool BT>
+template <int BM, int BN, int DT, bool BT, int NST>
 struct GemmTile {
+  static constexpr int kStages = NST;
   static constexpr int WM = 2, WN = 2;
   static constexpr int TM = BM / WM, TN = BN / WN;     // per-wave tile
   static constexpr int FM = TM / 32, FN = TN / 32;     // 32x32 MFMA blocks per wave
-  static constexpr int A_BYTES = BM * kRowBytes;
-  static constexpr int B_BYTES = BN * kRowBytes;
+  static constexpr int A_BYTES = BM * kKRow;
+  static constexpr int B_BYTES = BN * kKRow;           // same size in both B layouts
   static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
-  static constexpr int LDS_BYTES = 2 * STAGE_BYTES;
-  static constexpr int A_IPW = BM / 32;                // 8-row load instructions per wave for A
-  static constexpr int B_IPW = BN / 32;                // same for k-contiguous B
-  static constexpr int NN_BLOCKS = 8 * (BN / 8);       // 8x8 blocks of a k x n B tile
-  static constexpr int NN_PER_THREAD = (NN_BLOCKS + kThreads - 1) / kThreads;
+  static constexpr int LDS_BYTES = kStages * STAGE_BYTES;
+  static constexpr int A_IPW = A_BYTES / 1024 / 4;     // 1 KiB load instructions per wave
+  static constexpr int B_IPW = B_BYTES / 1024 / 4;
+  static constexpr int LOADS = A_IPW + B_IPW;          // per wave per k-tile
+  static constexpr int B_ROW = BN * 2;                 // bytes of an n-contiguous k-row
   static_assert(FM >= 1 && FN >= 1, "tile too small");
+  static_assert(A_IPW >= 1 && B_IPW >= 1, "tile too small for the load split");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+  static_assert((NST - 2) * LOADS < 64, "vmcnt range");
+  static_assert(NST >= 3 && NST <= 4, "stages");
 };
 
-template <int BM, int BN, int DT, bool BT, bool SPLIT>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_mfma_kernel(GemmProblem p) {
-  using T = GemmTile<BM, BN, DT, BT>;
+template <int BM, int BN, int DT, bool BT, bool SPLIT, int NST, int OCC>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
+void gemm_mfma_kernel(GemmProblem p) {
+  using T = GemmTile<BM, BN, DT, BT, NST>;
+  constexpr int kStages = T::kStages;
   __shared__ __attribute__((aligned(1024))) char smem[T::LDS_BYTES];
 
   const int tid = threadIdx.x;
@@ -162,17 +216,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 
   const char* zero = reinterpret_cast<const char*>(g_zero_chunk);
 
-  // ---- per-lane global sources for the direct-to-LDS loads -------------------
-  // Load instruction j of this wave fills LDS rows (wave*IPW + j)*8 + lane/8,
-  // position lane%8, which holds logical chunk (lane%8) ^ swz(row).
-  const int lrow8 = lane >> 3, lpos = lane & 7;
+  // ---- per-lane global sources of the direct-to-LDS loads -------------------
+  // k-contiguous tiles: instruction j of this wave fills LDS rows
+  // (wave*IPW + j)*16 + lane/4, position lane%4 = chunk (lane%4) ^ swz_k(row).
   const char* a_src[T::A_IPW];
-  int a_kc[T::A_IPW];  // element offset of this lane's chunk inside a k-tile
+  int a_kc[T::A_IPW];
   uint32_t a_ok = 0;
 #pragma unroll
   for (int j = 0; j < T::A_IPW; ++j) {
-    const int r = (wave * T::A_IPW + j) * 8 + lrow8;
-    const int c = lpos ^ swz(r);
+    const int r = (wave * T::A_IPW + j) * 16 + (lane >> 2);
+    const int c = (lane & 3) ^ swz_k(r);
     a_kc[j] = c * 8;
     const int gi = m0 + r;
     a_src[j] = zero;
@@ -183,103 +236,85 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
       a_ok |= 1u << j;
     }
   }
-  const char* b_src[BT ? T::B_IPW : 1];
-  int b_kc[BT ? T::B_IPW : 1];
+  const char* b_src[T::B_IPW];
+  int b_kc[T::B_IPW];   // BT: element offset in k; !BT: k-row inside the tile
   uint32_t b_ok = 0;
-  if constexpr (BT) {
 #pragma unroll
-    for (int j = 0; j < T::B_IPW; ++j) {
-      const int r = (wave * T::B_IPW + j) * 8 + lrow8;
-      const int c = lpos ^ swz(r);
+  for (int j = 0; j < T::B_IPW; ++j) {
+    b_src[j] = zero;
+    if constexpr (BT) {
+      const int r = (wave * T::B_IPW + j) * 16 + (lane >> 2);
+      const int c = (lane & 3) ^ swz_k(r);
       b_kc[j] = c * 8;
       const int gn = n0 + r;
-      b_src[j] = zero;
       if (gn < N) {
         b_src[j] = static_cast<const char*>(p.b) + ((int64_t)gn * p.ldb + c * 8) * 2;
+        b_ok |= 1u << j;
+      }
+    } else {
+      // n-contiguous k-rows of BN*2 bytes: byte (wave*IPW + j)*1024 + lane*16
+      const int byte = (wave * T::B_IPW + j) * 1024 + lane * 16;
+      const int kr = byte / T::B_ROW;
+      const int pos = (byte % T::B_ROW) >> 4;
+      const int c = pos ^ swz_n(kr);
+      b_kc[j] = kr;
+      const int gn = n0 + c * 8;
+      if (gn < N) {
+        b_src[j] = static_cast<const char*>(p.b) + ((int64_t)kr * p.ldb + gn) * 2;
         b_ok |= 1u << j;
       }
     }
   }
 
-  // B stored k x n: each thread owns 8x8 blocks (8 k rows x 8 n columns).
-  u32x4_t nn_regs[T::NN_PER_THREAD][8];
-
-  auto issue_a = [&](char* stage, int k0) {
-    const bool full = (k0 + kBK <= k_end);
+  // Branch-free issue of one k-tile: lanes whose row/column is out of range,
+  // or whose chunk lies past k_end (ragged k, or a k-tile past the end that
+  // the uniform pipeline still issues), fetch the zero block instead.
+  auto issue = [&](int stage, int k0) {
+    char* sa = smem + stage * T::STAGE_BYTES;
+    char* sb = sa + T::A_BYTES;
+    const int64_t a_step = (int64_t)k0 * 2;
+    const int64_t b_step = BT ? (int64_t)k0 * 2 : (int64_t)k0 * p.ldb * 2;
 #pragma unroll
     for (int j = 0; j < T::A_IPW; ++j) {
-      const bool ok = ((a_ok >> j) & 1) && (full || (k0 + a_kc[j] < k_end));
-      const char* src = ok ? a_src[j] + (int64_t)k0 * 2 : zero;
-      load_lds16(src, stage + (wave * T::A_IPW + j) * 1024);
+      const bool ok = ((a_ok >> j) & 1) && (k0 + a_kc[j] < k_end);
+      load_lds16(ok ? a_src[j] + a_step : zero, sa + (wave * T::A_IPW + j) * 1024);
     }
-  };
-  auto issue_b_direct = [&](char* stage, int k0) {
-    const bool full = (k0 + kBK <= k_end);
 #pragma unroll
     for (int j = 0; j < T::B_IPW; ++j) {
-      const bool ok = ((b_ok >> j) & 1) && (full || (k0 + b_kc[j] < k_end));
-      const char* src = ok ? b_src[j] + (int64_t)k0 * 2 : zero;
-      load_lds16(src, stage + T::A_BYTES + (wave * T::B_IPW + j) * 1024);
-    }
-  };
-  auto load_b_nn = [&](int k0) {
-#pragma unroll
-    for (int q = 0; q < T::NN_PER_THREAD; ++q) {
-      const int blk = tid + q * kThreads;
-      const int nb = blk % (BN / 8), kb = blk / (BN / 8);
-      const int gn = n0 + nb * 8;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int gk = k0 + kb * 8 + i;
-        u32x4_t v = {0u, 0u, 0u, 0u};
-        if (blk < T::NN_BLOCKS && gk < k_end && gn < N)
-          v = *reinterpret_cast<const u32x4_t*>(static_cast<const char*>(p.b) +
-                                                ((int64_t)gk * p.ldb + gn) * 2);
-        nn_regs[q][i] = v;
-      }
-    }
-  };
-  auto store_b_nn = [&](char* stage) {
-    char* bs = stage + T::A_BYTES;
-#pragma unroll
-    for (int q = 0; q < T::NN_PER_THREAD; ++q) {
-      const int blk = tid + q * kThreads;
-      if (blk < T::NN_BLOCKS) {
-        const int nb = blk % (BN / 8), kb = blk / (BN / 8);
-        // Transpose the 8x8 block of 16-bit values: out[j] gathers element j
-        // of rows 0..7 (8 consecutive k of column n0 + nb*8 + j).
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int w = j >> 1, sh = (j & 1) * 16;
-          u32x4_t o;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const uint32_t lo = (nn_regs[q][2 * e][w] >> sh) & 0xFFFFu;
-            const uint32_t hi = (nn_regs[q][2 * e + 1][w] >> sh) & 0xFFFFu;
-            o[e] = lo | (hi << 16);
-          }
-          const int r = nb * 8 + j;
-          *reinterpret_cast<u32x4_t*>(bs + r * kRowBytes + ((kb ^ swz(r)) << 4)) = o;
-        }
-      }
+      const bool ok = ((b_ok >> j) & 1) && (k0 + b_kc[j] < k_end);
+      load_lds16(ok ? b_src[j] + b_step : zero, sb + (wave * T::B_IPW + j) * 1024);
     }
   };
 
   // ---- LDS fragment read offsets -------------------------------------------
   const int hi = lane >> 5, l32 = lane & 31;
-  int a_off[T::FM], a_x[T::FM], b_off[T::FN], b_x[T::FN];
+  int a_off[T::FM], a_x[T::FM];
 #pragma unroll
   for (int f = 0; f < T::FM; ++f) {
     const int r = wm * T::TM + f * 32 + l32;
-    a_off[f] = r * kRowBytes;
-    a_x[f] = hi ^ swz(r);
+    a_off[f] = r * kKRow;
+    a_x[f] = hi ^ swz_k(r);
   }
+  // BT: k-contiguous rows like A.  !BT: ds_read_b64_tr_b16 source lanes.
+  // Lane i of 16-lane group G reads k-row 16s + 8*(G/2) + 4*half + i/4 at
+  // columns nb + 16*(G%2) + 4*(i%4) .. +3; the instruction hands lane
+  // 16G + j element e of the 16x4 block read by lanes 4e + j/4, i.e.
+  // B[16s + 8*(G/2) + 4*half + e][nb + 16*(G%2) + j].
+  int b_off[T::FN], b_x[T::FN];
+  if constexpr (BT) {
 #pragma unroll
-  for (int f = 0; f < T::FN; ++f) {
-    const int r = wn * T::TN + f * 32 + l32;
-    b_off[f] = T::A_BYTES + r * kRowBytes;
-    b_x[f] = hi ^ swz(r);
+    for (int f = 0; f < T::FN; ++f) {
+      const int r = wn * T::TN + f * 32 + l32;
+      b_off[f] = T::A_BYTES + r * kKRow;
+      b_x[f] = hi ^ swz_k(r);
+    }
   }
+  const int tr_g = lane >> 4, tr_i = lane & 15;
+  const int tr_krow = 8 * (tr_g >> 1) + (tr_i >> 2);        // + 16s + 4*half
+  const int tr_swz = swz_n(tr_krow);                        // k-row % 4 is the same for every s/half
+  int tr_n[T::FN];
+#pragma unroll
+  for (int f = 0; f < T::FN; ++f) tr_n[f] = wn * T::TN + f * 32 + 16 * (tr_g & 1) + 4 * (tr_i & 3);
 
   f32x16_t acc[T::FM][T::FN];
 #pragma unroll
@@ -289,61 +324,98 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-  // Fragments for k-substep s+1 are read from LDS while the MFMAs of
-  // substep s run (two register sets).
   auto read_frags = [&](const char* stage, int s, u32x4_t* af, u32x4_t* bfr) {
 #pragma unroll
     for (int f = 0; f < T::FM; ++f)
       af[f] = *reinterpret_cast<const u32x4_t*>(stage + a_off[f] + (((2 * s) ^ a_x[f]) << 4));
-#pragma unroll
-    for (int f = 0; f < T::FN; ++f)
-      bfr[f] = *reinterpret_cast<const u32x4_t*>(stage + b_off[f] + (((2 * s) ^ b_x[f]) << 4));
-  };
-  auto compute = [&](const char* stage) {
-    u32x4_t af[2][T::FM], bfr[2][T::FN];
-    read_frags(stage, 0, af[0], bfr[0]);
-#pragma unroll
-    for (int s = 0; s < kBK / 16; ++s) {
-      if (s + 1 < kBK / 16) read_frags(stage, s + 1, af[(s + 1) & 1], bfr[(s + 1) & 1]);
-#pragma unroll
-      for (int i = 0; i < T::FM; ++i)
-#pragma unroll
-        for (int j = 0; j < T::FN; ++j)
-          acc[i][j] = mfma32<DT>(bfr[s & 1][j], af[s & 1][i], acc[i][j]);
-    }
-  };
-
-  // ---- main loop -------------------------------------------------------------
-  char* stage0 = smem;
-  char* stage1 = smem + T::STAGE_BYTES;
-  if (nk > 0) {
-    issue_a(stage0, k_begin);
     if constexpr (BT) {
-      issue_b_direct(stage0, k_begin);
+#pragma unroll
+      for (int f = 0; f < T::FN; ++f)
+        bfr[f] = *reinterpret_cast<const u32x4_t*>(stage + b_off[f] + (((2 * s) ^ b_x[f]) << 4));
     } else {
-      load_b_nn(k_begin);
-      store_b_nn(stage0);
+      const char* sb = stage + T::A_BYTES;
+#pragma unroll
+      for (int f = 0; f < T::FN; ++f) {
+        const int n = tr_n[f];
+        const int pos = (n >> 3) ^ tr_swz;
+        const int within = (n & 7) * 2;
+        const char* p0 = sb + (16 * s + tr_krow) * T::B_ROW + (pos << 4) + within;
+        const u32x2_t lo = read_tr(p0);
+        const u32x2_t hi2 = read_tr(p0 + 4 * T::B_ROW);
+        bfr[f] = u32x4_t{lo[0], lo[1], hi2[0], hi2[1]};
+      }
     }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+  };
+  auto mfma_block = [&](const u32x4_t* af, const u32x4_t* bfr) {
+#pragma unroll
+    for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < T::FN; ++j) acc[i][j] = mfma32<DT>(bfr[j], af[i], acc[i][j]);
+  };
+  constexpr int kMfmaPerSub = T::FM * T::FN;
+  constexpr int kReadsPerSub = T::FM + (BT ? T::FN : 2 * T::FN);
+
+  // ---- main loop ---------------------------------------------------------------
+  // A k-tile (32 deep) is two k16 substeps.  Per iteration `it`:
+  //   region 1: MFMAs of substep 0 (fragments f0), LDS reads of substep 1 (f1)
+  //   sync    : this wave's loads of tile it+1 done (vmcnt), then barrier --
+  //             tile it+1 is complete in LDS, and every wave has finished
+  //             reading tile it-1, whose stage is reused next
+  //   region 2: MFMAs of substep 1 (f1), loads of tile it+NST-1 into the
+  //             stage of tile it-1, LDS reads of tile it+1 substep 0 (f0)
+  // Every iteration issues exactly one k-tile of loads (past the end they
+  // fetch zeros into a stage nobody reads again), so the vmcnt arithmetic is
+  // the same in every iteration and the loop body has no branches.
+  u32x4_t f0a[T::FM], f0b[T::FN], f1a[T::FM], f1b[T::FN];
+#pragma unroll
+  for (int t = 0; t < kStages - 1; ++t) issue(t, k_begin + t * kBK);
+  wait_vmcnt<(kStages - 2) * T::LOADS>();
+  block_barrier();
+  read_frags(smem, 0, f0a, f0b);
+  int st_cur = 0;                 // stage of tile it
+  int st_new = kStages - 1;       // stage that receives tile it + NST - 1
+  for (int it = 0; it < nk; ++it) {
+    const char* cur = smem + st_cur * T::STAGE_BYTES;
+    const int st_next = (st_cur + 1 == kStages) ? 0 : st_cur + 1;
+    read_frags(cur, 1, f1a, f1b);
+    mfma_block(f0a, f0b);
+    // interleave: MFMA, LDS read, MFMA, LDS read, ...
+    constexpr int kPairs1 = kReadsPerSub < kMfmaPerSub ? kReadsPerSub : kMfmaPerSub;
+#pragma unroll
+    for (int q = 0; q < kPairs1; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    if constexpr (kMfmaPerSub > kPairs1)
+      __builtin_amdgcn_sched_group_barrier(0x008, kMfmaPerSub - kPairs1, 0);
+
+    wait_vmcnt<(kStages - 3) * T::LOADS>();
+    block_barrier();
+
+    issue(st_new, k_begin + (it + kStages - 1) * kBK);
+    read_frags(smem + st_next * T::STAGE_BYTES, 0, f0a, f0b);
+    mfma_block(f1a, f1b);
+    // interleave: MFMA, global->LDS load, ..., then MFMA, LDS read, ...
+    constexpr int kPairsV = T::LOADS < kMfmaPerSub ? T::LOADS : kMfmaPerSub;
+    constexpr int kLeft = kMfmaPerSub - kPairsV;
+    constexpr int kPairsR = kReadsPerSub < kLeft ? kReadsPerSub : kLeft;
+#pragma unroll
+    for (int q = 0; q < kPairsV; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 1);
+    }
+#pragma unroll
+    for (int q = 0; q < kPairsR; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+    }
+    if constexpr (kLeft > kPairsR)
+      __builtin_amdgcn_sched_group_barrier(0x008, kLeft - kPairsR, 1);
+    st_cur = st_next;
+    st_new = (st_new + 1 == kStages) ? 0 : st_new + 1;
   }
-  for (int kt = 0; kt < nk; ++kt) {
-    char* cur = (kt & 1) ? stage1 : stage0;
-    char* nxt = (kt & 1) ? stage0 : stage1;
-    const bool more = (kt + 1 < nk);
-    const int k1 = k_begin + (kt + 1) * kBK;
-    if (more) {
-      issue_a(nxt, k1);
-      if constexpr (BT) issue_b_direct(nxt, k1);
-      else load_b_nn(k1);
-    }
-    compute(cur);
-    if constexpr (!BT) {
-      if (more) store_b_nn(nxt);
-    }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-  }
+  // No LDS-bound load may still be in flight when the workgroup retires.
+  wait_vmcnt<0>();
 
   // ---- epilogue --------------------------------------------------------------
   // acc[i][j][4q + e] holds C[m0 + wm*TM + i*32 + l32][n0 + wn*TN + j*32 + 8q + 4hi + e].
@@ -424,24 +496,26 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   }
 }
 
-template <int BM, int BN, int DT, bool BT>
+template <int BM, int BN, int DT, bool BT, int NST, int OCC>
 hipError_t launch_one(const GemmProblem& p, hipStream_t stream) {
   const int ntiles = p.order.num_rb * p.order.num_cb;
   if (p.splits > 1) {
-    hipLaunchKernelGGL((gemm_mfma_kernel<BM, BN, DT, BT, true>), dim3(ntiles * p.splits),
+    hipLaunchKernelGGL((gemm_mfma_kernel<BM, BN, DT, BT, true, NST, OCC>), dim3(ntiles * p.splits),
                        dim3(kThreads), 0, stream, p);
   } else {
-    hipLaunchKernelGGL((gemm_mfma_kernel<BM, BN, DT, BT, false>), dim3(ntiles), dim3(kThreads), 0,
-                       stream, p);
+    hipLaunchKernelGGL((gemm_mfma_kernel<BM, BN, DT, BT, false, NST, OCC>), dim3(ntiles),
+                       dim3(kThreads), 0, stream, p);
   }
   return hipGetLastError();
 }
 
-template <int BM, int BN>
+template <int BM, int BN, int NST, int OCC>
 hipError_t launch_tile(const GemmProblem& p, int dtype, bool bt, hipStream_t s) {
   if (dtype == kDtypeBf16)
-    return bt ? launch_one<BM, BN, kDtypeBf16, true>(p, s) : launch_one<BM, BN, kDtypeBf16, false>(p, s);
-  return bt ? launch_one<BM, BN, kDtypeFp16, true>(p, s) : launch_one<BM, BN, kDtypeFp16, false>(p, s);
+    return bt ? launch_one<BM, BN, kDtypeBf16, true, NST, OCC>(p, s)
+              : launch_one<BM, BN, kDtypeBf16, false, NST, OCC>(p, s);
+  return bt ? launch_one<BM, BN, kDtypeFp16, true, NST, OCC>(p, s)
+            : launch_one<BM, BN, kDtypeFp16, false, NST, OCC>(p, s);
 }
 
 }  // namespace
@@ -453,9 +527,11 @@ hipError_t launch_gemm_mfma(const GemmProblem& p, int tile_cfg, int dtype, bool 
                             hipStream_t stream) {
   if (dtype != kDtypeBf16 && dtype != kDtypeFp16) return hipErrorInvalidValue;
   switch (tile_cfg) {
-    case kTile256x256: return launch_tile<256, 256>(p, dtype, rhs_transpose, stream);
-    case kTile128x128: return launch_tile<128, 128>(p, dtype, rhs_transpose, stream);
-    case kTile256x128: return launch_tile<256, 128>(p, dtype, rhs_transpose, stream);
+    // 256x256: one workgroup per CU, 4-stage ring (128 KiB LDS)
+    case kTile256x256: return launch_tile<256, 256, 4, 1>(p, dtype, rhs_transpose, stream);
+    // 128x128 and 256x128: two workgroups per CU (<= 80 KiB LDS, <= 256 VGPRs each)
+    case kTile128x128: return launch_tile<128, 128, 4, 2>(p, dtype, rhs_transpose, stream);
+    case kTile256x128: return launch_tile<256, 128, 3, 2>(p, dtype, rhs_transpose, stream);
     default: return hipErrorInvalidValue;
   }
 }
