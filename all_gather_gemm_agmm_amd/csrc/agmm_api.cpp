@@ -111,7 +111,7 @@ struct agmm_plan {
   int splits = 0; // 0: auto
   int local_shard = 0;
   int order = 0;
-  int group_m = 8;
+  int group_m = 4;
   int xcd_remap = 1;
   int copy_wgs = 0;
   int debug_keep_slots = 0;
@@ -130,7 +130,6 @@ struct agmm_plan {
   char* ring = nullptr;
   size_t slot_bytes = 0;
   float* partials = nullptr;
-  int32_t* counters = nullptr;
   int32_t* d_order = nullptr;
   std::vector<int32_t> h_order;     // concatenated per-chunk orders
   std::vector<int64_t> order_off;   // offset of chunk c's table
@@ -204,7 +203,6 @@ void free_resources(agmm_plan* p) {
   p->ws_bytes = 0;
   p->ring = nullptr;
   p->partials = nullptr;
-  p->counters = nullptr;
   p->d_order = nullptr;
 }
 
@@ -229,7 +227,11 @@ int configure(agmm_plan* p) {
     p->tile_used = -1;
     p->bm = p->bn = 64;
   } else if (v == AGMM_VARIANT_SKINNY) {
-    p->tile_used = p->tile >= 0 ? p->tile : (p->m <= 128 ? agmm::kTile128x128 : agmm::kTile256x128);
+    // all of m in one row block; narrow column blocks so that enough
+    // workgroups stream B (the 64-wide tile needs B stored n x k)
+    p->tile_used = p->tile >= 0 ? p->tile
+                   : (p->m <= 128 ? (p->rt ? agmm::kTile128x64 : agmm::kTile128x128)
+                                  : agmm::kTile256x128);
     p->bm = agmm::tile_bm(p->tile_used);
     p->bn = agmm::tile_bn(p->tile_used);
   } else if (v == AGMM_VARIANT_STAGED) {
@@ -248,7 +250,7 @@ int configure(agmm_plan* p) {
   p->nslots = 0;
   p->splits_used = 1;
   p->k_per_split = p->k;
-  size_t ring_bytes = 0, part_bytes = 0, counter_bytes = 0;
+  size_t ring_bytes = 0, part_bytes = 0;
   if (v == AGMM_VARIANT_STAGED) {
     p->rows_per_chunk = std::min<int64_t>(p->m_s, (int64_t)p->pvalue * p->bm);
     p->num_chunks = (int)cdiv(p->m_s, p->rows_per_chunk);
@@ -261,14 +263,17 @@ int configure(agmm_plan* p) {
     ring_bytes = p->slot_bytes;
   } else if (v == AGMM_VARIANT_SKINNY) {
     const int64_t tiles = cdiv(p->m, p->bm) * cdiv(p->n, p->bn);
-    int64_t want = p->splits > 0 ? p->splits : cdiv(p->cu_count, tiles);
+    // enough k-splits to give every CU a workgroup, rounded down to a power
+    // of two so the k ranges stay even
+    int64_t want = p->splits;
+    if (want <= 0) {
+      want = 1;
+      while (want * 2 * tiles <= p->cu_count) want *= 2;
+    }
     want = std::max<int64_t>(1, std::min<int64_t>(want, cdiv(p->k, agmm::kTileBK)));
     p->k_per_split = cdiv(cdiv(p->k, want), agmm::kTileBK) * agmm::kTileBK;
     p->splits_used = (int)cdiv(p->k, p->k_per_split);
-    if (p->splits_used > 1) {
-      part_bytes = (size_t)p->splits_used * p->m * p->n * sizeof(float);
-      counter_bytes = (size_t)tiles * sizeof(int32_t);
-    }
+    if (p->splits_used > 1) part_bytes = (size_t)p->splits_used * p->m * p->n * sizeof(float);
   }
 
   // tile orders (one table per chunk)
@@ -287,7 +292,7 @@ int configure(agmm_plan* p) {
 
   // one allocation, 256-byte aligned pieces
   auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
-  const size_t total = up(ring_bytes) + up(part_bytes) + up(counter_bytes) + up(order_bytes);
+  const size_t total = up(ring_bytes) + up(part_bytes) + up(order_bytes);
   free_resources(p);
   if (total > 0) {
     if (std::getenv("AGMM_TEST_FAIL_ALLOC"))
@@ -304,12 +309,6 @@ int configure(agmm_plan* p) {
     char* q = p->ws;
     if (ring_bytes) { p->ring = q; q += up(ring_bytes); }
     if (part_bytes) { p->partials = reinterpret_cast<float*>(q); q += up(part_bytes); }
-    if (counter_bytes) {
-      p->counters = reinterpret_cast<int32_t*>(q);
-      err = hipMemset(p->counters, 0, counter_bytes);
-      if (err != hipSuccess) return hip_err(err, "hipMemset(counters)");
-      q += up(counter_bytes);
-    }
     if (order_bytes) {
       p->d_order = reinterpret_cast<int32_t*>(q);
       err = hipMemcpy(p->d_order, p->h_order.data(), order_bytes, hipMemcpyHostToDevice);
@@ -624,7 +623,6 @@ int agmm_run(agmm_plan_t p, const void* const* shard_ptrs, const void* B, void* 
       g.splits = p->splits_used;
       g.k_per_split = (int32_t)p->k_per_split;
       g.partials = p->partials;
-      g.counters = p->counters;
       rc = launch_gemm(p, g, s);
       return rc == AGMM_OK ? ok() : rc;
     }
@@ -685,7 +683,6 @@ int agmm_run_gathered(agmm_plan_t p, const void* gathered, const void* B, void* 
     g.splits = p->splits_used;
     g.k_per_split = (int32_t)p->k_per_split;
     g.partials = p->partials;
-    g.counters = p->counters;
   }
   const int rc = launch_gemm(p, g, static_cast<hipStream_t>(stream));
   return rc == AGMM_OK ? ok() : rc;

@@ -49,25 +49,34 @@ struct GemmProblem {
   int64_t ldb;             // elements between rows of B as stored
   void* c;
   int64_t ldc;             // elements between rows of C
-  // split-K (used when splits > 1)
+  // split-K (used when splits > 1): partial sums, then a reduction kernel
   int32_t splits;
-  int32_t k_per_split;     // multiple of the kernel's BK
-  float* partials;         // [splits][m][n] fp32
-  int32_t* counters;       // [num_rb * num_cb], zero between calls
+  int32_t k_per_split;     // multiple of kTileBK
+  float* partials;         // [splits][m][n] fp32 scratch
 };
 
 // Tile shapes compiled for the MFMA kernels.
 enum TileCfg : int {
-  kTile256x256 = 0,   // 4 waves, 128x128 per wave
-  kTile128x128 = 1,   // 4 waves, 64x64 per wave
-  kTile256x128 = 2,   // 4 waves, 128x64 per wave
-  kTileCount = 3,
+  kTile256x256 = 0,      // 4 waves, 128x128 per wave, 32-deep k-tiles
+  kTile128x128 = 1,      // 64x64 per wave
+  kTile256x128 = 2,      // 128x64 per wave
+  kTile256x256k64 = 3,   // as kTile256x256 with 64-deep k-tiles
+  kTile256x128k64 = 4,
+  kTile128x128k64 = 5,
+  kTile256x256w8 = 6,    // 8 waves (two per SIMD), 128x64 per wave
+  kTile256x128w8 = 7,    // 8 waves, 128x32 per wave
+  kTile128x64 = 8,       // 4 waves, 64x32 per wave; B stored n x k only
+  kTileCount = 9,
 };
 int tile_bm(int cfg);
 int tile_bn(int cfg);
-constexpr int kTileBK = 32;
+int tile_bk(int cfg);
+// k granularity of split-K ranges (a multiple of every configuration's depth)
+constexpr int kTileBK = 64;
 
 // bf16/fp16 MFMA GEMM (16-bit inputs, fp32 accumulate, output in the input dtype).
+// With p.splits > 1 this is two launches on `stream`: fp32 partial sums per
+// k range, then their fixed-order sum and cast.
 hipError_t launch_gemm_mfma(const GemmProblem& p, int tile_cfg, int dtype, bool rhs_transpose,
                             hipStream_t stream);
 

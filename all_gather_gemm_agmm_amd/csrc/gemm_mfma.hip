@@ -12,7 +12,7 @@
 // store).
 //
 // Design (MI355X-native, not a translation of either page):
-//  * 256 threads = 4 waves of 64 lanes, 2x2 waves per output tile.
+//  * 4 or 8 waves of 64 lanes per workgroup, 2 x (waves/2) over the tile.
 //  * v_mfma_f32_32x32x16_{bf16,f16}: the B tile is the MFMA's first operand
 //    and the A tile its second, so each lane ends up owning 4 consecutive
 //    output columns of one row (8-byte packed stores in the epilogue).
@@ -48,6 +48,7 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 
@@ -58,11 +59,16 @@ typedef __attribute__((address_space(3))) char lds_char_t;
 // 16 zero bytes: the source of every out-of-range 16-byte chunk.
 __device__ __attribute__((aligned(64))) const uint32_t g_zero_chunk[16] = {0};
 
-constexpr int kThreads = 256;
-constexpr int kBK = kTileBK;         // 32 elements
-constexpr int kKRow = kBK * 2;       // bytes of a k-contiguous LDS row (64)
 
-__device__ __forceinline__ int swz_k(int row) { return (row >> 2) & 3; }
+// Position of 16-byte chunk groups in a k-contiguous LDS row (BK elements,
+// 2*BK bytes).  Both choices were measured free of LDS bank conflicts for
+// the MFMA fragment reads on gfx950 (64 banks, 16 lanes per ds_read_b128
+// cycle).
+template <int BK>
+__device__ __forceinline__ int swz_k(int row) {
+  if constexpr (BK == 32) return (row >> 2) & 3;
+  else return (row ^ (row >> 3)) & 7;
+}
 __device__ __forceinline__ int swz_n(int krow) {
   // 0, 4, 10, 14 for krow % 4 = 0..3
   const int r = krow & 3;
@@ -162,31 +168,43 @@ __device__ __forceinline__ void tile_coords(const TileOrder& o, int wg, int nwg,
   rb = o.rb_order ? o.rb_order[rbi] : rbi;
 }
 
-template <int BM, int BN, int DT, bool BT, int NST>
+template <int BM, int BN, int BK, int DT, bool BT, int NST, int WAVES>
 struct GemmTile {
   static constexpr int kStages = NST;
-  static constexpr int WM = 2, WN = 2;
+  static constexpr int THREADS = 64 * WAVES;
+  static constexpr int WM = 2, WN = WAVES / 2;      // wave grid over the output tile
   static constexpr int TM = BM / WM, TN = BN / WN;     // per-wave tile
   static constexpr int FM = TM / 32, FN = TN / 32;     // 32x32 MFMA blocks per wave
-  static constexpr int A_BYTES = BM * kKRow;
-  static constexpr int B_BYTES = BN * kKRow;           // same size in both B layouts
+  static constexpr int KROW = BK * 2;                  // bytes of a k-contiguous LDS row
+  static constexpr int CPR = BK / 8;                   // 16-byte chunks per such row
+  static constexpr int RPI = 1024 / KROW;              // rows one 1 KiB load instruction fills
+  static constexpr int SUB = BK / 16;                  // k16 MFMA substeps per k-tile
+  static constexpr int A_BYTES = BM * KROW;
+  static constexpr int B_BYTES = BN * KROW;            // same size in both B layouts
   static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
   static constexpr int LDS_BYTES = kStages * STAGE_BYTES;
-  static constexpr int A_IPW = A_BYTES / 1024 / 4;     // 1 KiB load instructions per wave
-  static constexpr int B_IPW = B_BYTES / 1024 / 4;
+  static constexpr int A_IPW = A_BYTES / 1024 / WAVES; // 1 KiB load instructions per wave
+  static constexpr int B_IPW = B_BYTES / 1024 / WAVES;
   static constexpr int LOADS = A_IPW + B_IPW;          // per wave per k-tile
   static constexpr int B_ROW = BN * 2;                 // bytes of an n-contiguous k-row
+  // Where in a k-tile the workgroup synchronises: in the middle when at
+  // least 3 stages leave a tile of slack, else at the end of the tile.
+  static constexpr bool MID_SYNC = NST >= 3;
+  static constexpr int SYNC_SUB = MID_SYNC ? SUB / 2 : SUB;
+  static_assert(BK == 32 || BK == 64, "BK");
+  static_assert(WAVES == 4 || WAVES == 8, "waves");
   static_assert(FM >= 1 && FN >= 1, "tile too small");
   static_assert(A_IPW >= 1 && B_IPW >= 1, "tile too small for the load split");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
-  static_assert((NST - 2) * LOADS < 64, "vmcnt range");
-  static_assert(NST >= 3 && NST <= 4, "stages");
+  static_assert((NST - 1) * LOADS < 64, "vmcnt range");
+  static_assert(NST >= 2 && NST <= 4, "stages");
 };
 
-template <int BM, int BN, int DT, bool BT, bool SPLIT, int NST, int OCC>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
+template <int BM, int BN, int BK, int DT, bool BT, bool SPLIT, int NST, int WAVES, int OCC>
+__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 void gemm_mfma_kernel(GemmProblem p) {
-  using T = GemmTile<BM, BN, DT, BT, NST>;
+  using T = GemmTile<BM, BN, BK, DT, BT, NST, WAVES>;
+  constexpr int kBK = BK;
   constexpr int kStages = T::kStages;
   __shared__ __attribute__((aligned(1024))) char smem[T::LDS_BYTES];
 
@@ -218,14 +236,15 @@ void gemm_mfma_kernel(GemmProblem p) {
 
   // ---- per-lane global sources of the direct-to-LDS loads -------------------
   // k-contiguous tiles: instruction j of this wave fills LDS rows
-  // (wave*IPW + j)*16 + lane/4, position lane%4 = chunk (lane%4) ^ swz_k(row).
+  // (wave*IPW + j)*RPI + lane/CPR, position lane%CPR, which holds chunk
+  // (lane%CPR) ^ swz_k(row).
   const char* a_src[T::A_IPW];
   int a_kc[T::A_IPW];
   uint32_t a_ok = 0;
 #pragma unroll
   for (int j = 0; j < T::A_IPW; ++j) {
-    const int r = (wave * T::A_IPW + j) * 16 + (lane >> 2);
-    const int c = (lane & 3) ^ swz_k(r);
+    const int r = (wave * T::A_IPW + j) * T::RPI + lane / T::CPR;
+    const int c = (lane % T::CPR) ^ swz_k<BK>(r);
     a_kc[j] = c * 8;
     const int gi = m0 + r;
     a_src[j] = zero;
@@ -243,8 +262,8 @@ void gemm_mfma_kernel(GemmProblem p) {
   for (int j = 0; j < T::B_IPW; ++j) {
     b_src[j] = zero;
     if constexpr (BT) {
-      const int r = (wave * T::B_IPW + j) * 16 + (lane >> 2);
-      const int c = (lane & 3) ^ swz_k(r);
+      const int r = (wave * T::B_IPW + j) * T::RPI + lane / T::CPR;
+      const int c = (lane % T::CPR) ^ swz_k<BK>(r);
       b_kc[j] = c * 8;
       const int gn = n0 + r;
       if (gn < N) {
@@ -292,8 +311,8 @@ void gemm_mfma_kernel(GemmProblem p) {
 #pragma unroll
   for (int f = 0; f < T::FM; ++f) {
     const int r = wm * T::TM + f * 32 + l32;
-    a_off[f] = r * kKRow;
-    a_x[f] = hi ^ swz_k(r);
+    a_off[f] = r * T::KROW;
+    a_x[f] = hi ^ swz_k<BK>(r);
   }
   // BT: k-contiguous rows like A.  !BT: ds_read_b64_tr_b16 source lanes.
   // Lane i of 16-lane group G reads k-row 16s + 8*(G/2) + 4*half + i/4 at
@@ -305,8 +324,8 @@ void gemm_mfma_kernel(GemmProblem p) {
 #pragma unroll
     for (int f = 0; f < T::FN; ++f) {
       const int r = wn * T::TN + f * 32 + l32;
-      b_off[f] = T::A_BYTES + r * kKRow;
-      b_x[f] = hi ^ swz_k(r);
+      b_off[f] = T::A_BYTES + r * T::KROW;
+      b_x[f] = hi ^ swz_k<BK>(r);
     }
   }
   const int tr_g = lane >> 4, tr_i = lane & 15;
@@ -356,63 +375,70 @@ void gemm_mfma_kernel(GemmProblem p) {
   constexpr int kReadsPerSub = T::FM + (BT ? T::FN : 2 * T::FN);
 
   // ---- main loop ---------------------------------------------------------------
-  // A k-tile (32 deep) is two k16 substeps.  Per iteration `it`:
-  //   region 1: MFMAs of substep 0 (fragments f0), LDS reads of substep 1 (f1)
-  //   sync    : this wave's loads of tile it+1 done (vmcnt), then barrier --
-  //             tile it+1 is complete in LDS, and every wave has finished
-  //             reading tile it-1, whose stage is reused next
-  //   region 2: MFMAs of substep 1 (f1), loads of tile it+NST-1 into the
-  //             stage of tile it-1, LDS reads of tile it+1 substep 0 (f0)
+  // Fragment registers alternate between two sets: the LDS reads of substep
+  // s+1 are in flight while the MFMAs of substep s run.  Once per k-tile the
+  // workgroup synchronises ("sync"): each wave waits for its own loads of
+  // the next k-tile (vmcnt), then a barrier makes that tile complete in LDS
+  // and guarantees every wave is done with the stage the next issue reuses;
+  // right after it the loads of a further k-tile are issued.
+  //   MID_SYNC (>= 3 stages): sync in the middle of tile `it`, issue tile
+  //     it+NST-1 into the stage of tile it-1; the reads of tile it+1 start
+  //     during the last substep of tile it.
+  //   2 stages: sync at the end of tile `it`, issue tile it+2 into the stage
+  //     of tile it.
   // Every iteration issues exactly one k-tile of loads (past the end they
   // fetch zeros into a stage nobody reads again), so the vmcnt arithmetic is
   // the same in every iteration and the loop body has no branches.
-  u32x4_t f0a[T::FM], f0b[T::FN], f1a[T::FM], f1b[T::FN];
+  u32x4_t fa[2][T::FM], fb[2][T::FN];
+  constexpr int kPre = T::MID_SYNC ? kStages - 1 : kStages;   // tiles issued up front
 #pragma unroll
-  for (int t = 0; t < kStages - 1; ++t) issue(t, k_begin + t * kBK);
-  wait_vmcnt<(kStages - 2) * T::LOADS>();
+  for (int t = 0; t < kPre; ++t) issue(t, k_begin + t * kBK);
+  wait_vmcnt<(kPre - 1) * T::LOADS>();
   block_barrier();
-  read_frags(smem, 0, f0a, f0b);
-  int st_cur = 0;                 // stage of tile it
-  int st_new = kStages - 1;       // stage that receives tile it + NST - 1
+  read_frags(smem, 0, fa[0], fb[0]);
+  int st_cur = 0;                              // stage of tile it
+  int st_new = T::MID_SYNC ? kStages - 1 : 0;  // stage the next issue fills
+  int t_new = kPre;                            // k-tile the next issue loads
   for (int it = 0; it < nk; ++it) {
     const char* cur = smem + st_cur * T::STAGE_BYTES;
     const int st_next = (st_cur + 1 == kStages) ? 0 : st_cur + 1;
-    read_frags(cur, 1, f1a, f1b);
-    mfma_block(f0a, f0b);
-    // interleave: MFMA, LDS read, MFMA, LDS read, ...
-    constexpr int kPairs1 = kReadsPerSub < kMfmaPerSub ? kReadsPerSub : kMfmaPerSub;
 #pragma unroll
-    for (int q = 0; q < kPairs1; ++q) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-    if constexpr (kMfmaPerSub > kPairs1)
-      __builtin_amdgcn_sched_group_barrier(0x008, kMfmaPerSub - kPairs1, 0);
-
-    wait_vmcnt<(kStages - 3) * T::LOADS>();
-    block_barrier();
-
-    issue(st_new, k_begin + (it + kStages - 1) * kBK);
-    read_frags(smem + st_next * T::STAGE_BYTES, 0, f0a, f0b);
-    mfma_block(f1a, f1b);
-    // interleave: MFMA, global->LDS load, ..., then MFMA, LDS read, ...
-    constexpr int kPairsV = T::LOADS < kMfmaPerSub ? T::LOADS : kMfmaPerSub;
-    constexpr int kLeft = kMfmaPerSub - kPairsV;
-    constexpr int kPairsR = kReadsPerSub < kLeft ? kReadsPerSub : kLeft;
+    for (int s = 0; s < T::SUB; ++s) {
+      if (s == T::SYNC_SUB) {
+        wait_vmcnt<(kStages - 3 > 0 ? kStages - 3 : 0) * T::LOADS>();
+        block_barrier();
+        issue(st_new, k_begin + t_new * kBK);
+      }
+      if (s + 1 < T::SUB) read_frags(cur, s + 1, fa[(s + 1) & 1], fb[(s + 1) & 1]);
+      else if (T::MID_SYNC) read_frags(smem + st_next * T::STAGE_BYTES, 0, fa[0], fb[0]);
+      mfma_block(fa[s & 1], fb[s & 1]);
+      // interleave: MFMA, global->LDS load (right after a sync), ...,
+      // then MFMA, LDS read, MFMA, LDS read, ..., then the remaining MFMAs
+      const int nv = (s == T::SYNC_SUB) ? (T::LOADS < kMfmaPerSub ? T::LOADS : kMfmaPerSub) : 0;
+      const int left = kMfmaPerSub - nv;
+      const int nr = kReadsPerSub < left ? kReadsPerSub : left;
 #pragma unroll
-    for (int q = 0; q < kPairsV; ++q) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 1);
-    }
+      for (int q = 0; q < nv; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      }
 #pragma unroll
-    for (int q = 0; q < kPairsR; ++q) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+      for (int q = 0; q < nr; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+#pragma unroll
+      for (int q = 0; q < left - nr; ++q) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     }
-    if constexpr (kLeft > kPairsR)
-      __builtin_amdgcn_sched_group_barrier(0x008, kLeft - kPairsR, 1);
+    if constexpr (!T::MID_SYNC) {
+      wait_vmcnt<0>();
+      block_barrier();
+      issue(st_new, k_begin + t_new * kBK);
+      read_frags(smem + st_next * T::STAGE_BYTES, 0, fa[0], fb[0]);
+    }
     st_cur = st_next;
     st_new = (st_new + 1 == kStages) ? 0 : st_new + 1;
+    ++t_new;
   }
   // No LDS-bound load may still be in flight when the workgroup retires.
   wait_vmcnt<0>();
@@ -449,89 +475,138 @@ void gemm_mfma_kernel(GemmProblem p) {
       }
     }
   } else {
-    // Split-K: fp32 partial tile, then the last workgroup of this tile sums
-    // the partials in split order (fixed, so results are reproducible) and
-    // writes the cast result.
+    // Split-K: this workgroup's fp32 partial tile goes to partials[split];
+    // splitk_reduce_kernel sums the splits afterwards.
     float* part = p.partials + (int64_t)split * M * N;
+    const bool vec_ok = (N % 4) == 0;
 #pragma unroll
     for (int i = 0; i < T::FM; ++i) {
       const int gi = m0 + wm * T::TM + i * 32 + l32;
       if (gi >= M) continue;
+      float* prow = part + (int64_t)gi * N;
 #pragma unroll
       for (int j = 0; j < T::FN; ++j) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int gn = n0 + wn * T::TN + j * 32 + 8 * q + 4 * hi;
+          const f32x16_t& a = acc[i][j];
+          if (vec_ok && gn + 3 < N) {
+            *reinterpret_cast<f32x4_t*>(prow + gn) =
+                f32x4_t{a[4 * q + 0], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]};
+          } else {
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (gn + e < N) part[(int64_t)gi * N + gn + e] = acc[i][j][4 * q + e];
+            for (int e = 0; e < 4; ++e)
+              if (gn + e < N) prow[gn + e] = a[4 * q + e];
+          }
         }
       }
-    }
-    __threadfence();
-    __syncthreads();
-    __shared__ int s_last;
-    const int tile = rb * p.order.num_cb + cb;
-    if (tid == 0) {
-      const int prev = atomicAdd(&p.counters[tile], 1);
-      s_last = (prev == p.splits - 1);
-    }
-    __syncthreads();
-    if (s_last) {
-      __threadfence();
-      const int rows = min(BM, M - m0), cols = min(BN, N - n0);
-      for (int idx = tid; idx < rows * cols; idx += kThreads) {
-        const int r = idx / cols, cc = idx - r * cols;
-        const int gi = m0 + r, gn = n0 + cc;
-        float s = 0.0f;
-        for (int sp = 0; sp < p.splits; ++sp)
-          s += __builtin_nontemporal_load(p.partials + ((int64_t)sp * M + gi) * N + gn);
-        const int g = gi / p.rows.rows_per_group;
-        const int t = gi - g * p.rows.rows_per_group;
-        const int64_t crow = (int64_t)g * p.rows.c_group_rows + p.rows.c_row_off + t;
-        static_cast<uint16_t*>(p.c)[crow * p.ldc + gn] = cvt1<DT>(s);
-      }
-      if (tid == 0) p.counters[tile] = 0;
     }
   }
 }
 
-template <int BM, int BN, int DT, bool BT, int NST, int OCC>
+// Sum of the split-K partials in split order 0, 1, ..., S-1 (fixed, so the
+// result does not depend on which workgroup finished first), cast to the
+// output dtype, scattered to C rows through the row map.  Four consecutive
+// columns per thread.
+template <int DT>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmProblem p) {
+  const int M = p.m, N = p.n;
+  const int n4 = (N + 3) / 4;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (int64_t)M * n4) return;
+  const int row = (int)(idx / n4);
+  const int col = (int)(idx - (int64_t)row * n4) * 4;
+  const int g = row / p.rows.rows_per_group;
+  const int t = row - g * p.rows.rows_per_group;
+  const int64_t crow = (int64_t)g * p.rows.c_group_rows + p.rows.c_row_off + t;
+  uint16_t* cp = static_cast<uint16_t*>(p.c) + crow * p.ldc;
+  const int64_t plane = (int64_t)M * N;
+  const float* src = p.partials + (int64_t)row * N + col;
+  if ((N % 4) == 0) {
+    f32x4_t s = *reinterpret_cast<const f32x4_t*>(src);
+    for (int sp = 1; sp < p.splits; ++sp) s += *reinterpret_cast<const f32x4_t*>(src + sp * plane);
+    u32x2_t v;
+    v[0] = pack2<DT>(s[0], s[1]);
+    v[1] = pack2<DT>(s[2], s[3]);
+    if ((p.ldc % 4) == 0) {
+      *reinterpret_cast<u32x2_t*>(cp + col) = v;
+    } else {
+      for (int e = 0; e < 4; ++e) cp[col + e] = cvt1<DT>(s[e]);
+    }
+  } else {
+    for (int e = 0; e < 4 && col + e < N; ++e) {
+      float s = src[e];
+      for (int sp = 1; sp < p.splits; ++sp) s += src[sp * plane + e];
+      cp[col + e] = cvt1<DT>(s);
+    }
+  }
+}
+
+template <int BM, int BN, int BK, int DT, bool BT, int NST, int WAVES, int OCC>
 hipError_t launch_one(const GemmProblem& p, hipStream_t stream) {
   const int ntiles = p.order.num_rb * p.order.num_cb;
   if (p.splits > 1) {
-    hipLaunchKernelGGL((gemm_mfma_kernel<BM, BN, DT, BT, true, NST, OCC>), dim3(ntiles * p.splits),
-                       dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((gemm_mfma_kernel<BM, BN, BK, DT, BT, true, NST, WAVES, OCC>),
+                       dim3(ntiles * p.splits), dim3(64 * WAVES), 0, stream, p);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    const int64_t work = (int64_t)p.m * ((p.n + 3) / 4);
+    hipLaunchKernelGGL((splitk_reduce_kernel<DT>), dim3((unsigned)((work + 255) / 256)), dim3(256),
+                       0, stream, p);
   } else {
-    hipLaunchKernelGGL((gemm_mfma_kernel<BM, BN, DT, BT, false, NST, OCC>), dim3(ntiles),
-                       dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((gemm_mfma_kernel<BM, BN, BK, DT, BT, false, NST, WAVES, OCC>),
+                       dim3(ntiles), dim3(64 * WAVES), 0, stream, p);
   }
   return hipGetLastError();
 }
 
-template <int BM, int BN, int NST, int OCC>
+template <int BM, int BN, int BK, int NST, int WAVES, int OCC>
 hipError_t launch_tile(const GemmProblem& p, int dtype, bool bt, hipStream_t s) {
   if (dtype == kDtypeBf16)
-    return bt ? launch_one<BM, BN, kDtypeBf16, true, NST, OCC>(p, s)
-              : launch_one<BM, BN, kDtypeBf16, false, NST, OCC>(p, s);
-  return bt ? launch_one<BM, BN, kDtypeFp16, true, NST, OCC>(p, s)
-            : launch_one<BM, BN, kDtypeFp16, false, NST, OCC>(p, s);
+    return bt ? launch_one<BM, BN, BK, kDtypeBf16, true, NST, WAVES, OCC>(p, s)
+              : launch_one<BM, BN, BK, kDtypeBf16, false, NST, WAVES, OCC>(p, s);
+  return bt ? launch_one<BM, BN, BK, kDtypeFp16, true, NST, WAVES, OCC>(p, s)
+            : launch_one<BM, BN, BK, kDtypeFp16, false, NST, WAVES, OCC>(p, s);
 }
 
 }  // namespace
 
-int tile_bm(int cfg) { return cfg == kTile128x128 ? 128 : 256; }
-int tile_bn(int cfg) { return cfg == kTile256x256 ? 256 : 128; }
+// Compiled tile configurations: output tile, k-depth of an LDS stage,
+// stages in the LDS ring, waves per workgroup, waves per SIMD.
+struct TileInfo { int bm, bn, bk, stages, waves, occ; };
+constexpr TileInfo kTiles[kTileCount] = {
+    {256, 256, 32, 4, 4, 1},   // kTile256x256:      128 KiB LDS, 3 k-tiles in flight
+    {128, 128, 32, 4, 4, 2},   // kTile128x128:      64 KiB, two workgroups per CU
+    {256, 128, 32, 3, 4, 2},   // kTile256x128:      72 KiB, two workgroups per CU
+    {256, 256, 64, 2, 4, 1},   // kTile256x256k64:   128 KiB, 128-byte rows per load
+    {256, 128, 64, 3, 4, 1},   // kTile256x128k64:   144 KiB
+    {128, 128, 64, 2, 4, 2},   // kTile128x128k64:   64 KiB, two workgroups per CU
+    {256, 256, 32, 4, 8, 2},   // kTile256x256w8:    8 waves (2 per SIMD), 128x64 per wave
+    {256, 128, 32, 4, 8, 2},   // kTile256x128w8:    8 waves, 128x32 per wave
+    {128, 64, 32, 4, 4, 1},    // kTile128x64:       48 KiB; B stored n x k only (skinny m)
+};
+
+int tile_bm(int cfg) { return kTiles[cfg].bm; }
+int tile_bn(int cfg) { return kTiles[cfg].bn; }
+int tile_bk(int cfg) { return kTiles[cfg].bk; }
 
 hipError_t launch_gemm_mfma(const GemmProblem& p, int tile_cfg, int dtype, bool rhs_transpose,
                             hipStream_t stream) {
   if (dtype != kDtypeBf16 && dtype != kDtypeFp16) return hipErrorInvalidValue;
   switch (tile_cfg) {
-    // 256x256: one workgroup per CU, 4-stage ring (128 KiB LDS)
-    case kTile256x256: return launch_tile<256, 256, 4, 1>(p, dtype, rhs_transpose, stream);
-    // 128x128 and 256x128: two workgroups per CU (<= 80 KiB LDS, <= 256 VGPRs each)
-    case kTile128x128: return launch_tile<128, 128, 4, 2>(p, dtype, rhs_transpose, stream);
-    case kTile256x128: return launch_tile<256, 128, 3, 2>(p, dtype, rhs_transpose, stream);
+    case kTile256x256: return launch_tile<256, 256, 32, 4, 4, 1>(p, dtype, rhs_transpose, stream);
+    case kTile128x128: return launch_tile<128, 128, 32, 4, 4, 2>(p, dtype, rhs_transpose, stream);
+    case kTile256x128: return launch_tile<256, 128, 32, 3, 4, 2>(p, dtype, rhs_transpose, stream);
+    case kTile256x256k64: return launch_tile<256, 256, 64, 2, 4, 1>(p, dtype, rhs_transpose, stream);
+    case kTile256x128k64: return launch_tile<256, 128, 64, 3, 4, 1>(p, dtype, rhs_transpose, stream);
+    case kTile128x128k64: return launch_tile<128, 128, 64, 2, 4, 2>(p, dtype, rhs_transpose, stream);
+    case kTile256x256w8: return launch_tile<256, 256, 32, 4, 8, 2>(p, dtype, rhs_transpose, stream);
+    case kTile256x128w8: return launch_tile<256, 128, 32, 4, 8, 2>(p, dtype, rhs_transpose, stream);
+    case kTile128x64:
+      // an n-contiguous B tile of 64 columns is too narrow for its LDS swizzle
+      if (!rhs_transpose) return hipErrorInvalidValue;
+      return dtype == kDtypeBf16 ? launch_one<128, 64, 32, kDtypeBf16, true, 4, 4, 1>(p, stream)
+                                 : launch_one<128, 64, 32, kDtypeFp16, true, 4, 4, 1>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }
