@@ -48,7 +48,14 @@ def parse():
     ap.add_argument("--no-compare", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--only-run", action="store_true",
-                    help="warmup + K steps of the main path only (for profilers)")
+                    help="warmup + K steps of the main path, then 3 gather copies of the same "
+                         "shards (the known-size copy that calibrates HBM counters); for profilers")
+    ap.add_argument("--summarize-trace", metavar="DIR",
+                    help="write profiles/ summary of a rocprofv3 --kernel-trace --stats CSV run")
+    ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/ traffic summary from rocprofv3 --pmc FETCH_SIZE and "
+                         "--pmc WRITE_SIZE CSV runs of --only-run")
+    ap.add_argument("--command", default="", help="profiler command line, recorded in summaries")
     return ap.parse_args()
 
 
@@ -73,8 +80,113 @@ def traffic_from_profiles(workload_name: str, variant: str):
     return d.get("hbm_bytes_per_launch")
 
 
+# ------------------------------------------------------------ profile summaries
+def _csv_rows(d, suffix):
+    import csv
+    import glob
+    files = sorted(glob.glob(os.path.join(d, "**", "*" + suffix), recursive=True))
+    if not files:
+        raise SystemExit(f"no *{suffix} under {d}")
+    rows = []
+    for f in files:
+        with open(f) as fh:
+            rows.extend(csv.DictReader(fh))
+    return rows
+
+
+def _short(name: str) -> str:
+    for key in ("gemm_mfma_kernel", "splitk_reduce_kernel", "gather_kernel", "gemm_f32_kernel"):
+        if key in name:
+            return key
+    return name[:48]
+
+
+def summarize_trace(args, w, variant):
+    rows = _csv_rows(args.summarize_trace, "kernel_stats.csv")
+    name = f"kernel_trace_{w.name}_{variant}"
+    lines = [f"# rocprofv3 kernel trace: {w.name}, {variant} path", "",
+             f"command: `{args.command}`", "",
+             "| kernel | calls | avg us | min us | max us | total % |", "|---|---|---|---|---|---|"]
+    out = []
+    for r in rows:
+        calls = int(r.get("Calls", 0) or 0)
+        avg_ns = float(r.get("AverageNs", 0) or 0)
+        out.append({"kernel": r.get("Name", ""), "calls": calls, "avg_us": avg_ns / 1e3,
+                    "min_us": float(r.get("MinNs", 0) or 0) / 1e3,
+                    "max_us": float(r.get("MaxNs", 0) or 0) / 1e3,
+                    "pct": float(r.get("Percentage", 0) or 0)})
+    for o in sorted(out, key=lambda o: -o["pct"]):
+        lines.append(f"| {_short(o['kernel'])} | {o['calls']} | {o['avg_us']:.2f} | "
+                     f"{o['min_us']:.2f} | {o['max_us']:.2f} | {o['pct']:.1f} |")
+    lines += ["", "Full kernel symbols:", ""] + [f"- `{o['kernel']}`" for o in out]
+    path = os.path.join(ROOT, "profiles", name + ".md")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(path)
+
+
+def summarize_traffic(args, w, variant):
+    fetch_rows = _csv_rows(args.summarize_traffic[0], "counter_collection.csv")
+    write_rows = _csv_rows(args.summarize_traffic[1], "counter_collection.csv")
+
+    def per_kernel(rows, counter):
+        acc = {}
+        for r in rows:
+            if r.get("Counter_Name") != counter:
+                continue
+            k = _short(r.get("Kernel_Name", ""))
+            disp = r.get("Dispatch_Id")
+            acc.setdefault(k, {}).setdefault(disp, 0.0)
+            acc[k][disp] += float(r.get("Counter_Value", 0) or 0)
+        out = {}
+        for k, v in acc.items():
+            ids = sorted(v, key=lambda x: int(x))
+            if k == "gather_kernel":
+                ids = ids[-3:]   # the 3 calibration copies run last
+            out[k] = sum(v[i] for i in ids) / len(ids)   # KiB per dispatch
+        return out
+
+    fetch = per_kernel(fetch_rows, "FETCH_SIZE")
+    write = per_kernel(write_rows, "WRITE_SIZE")
+    copy_bytes = w.gather_bytes()
+    # the gather copy reads and writes exactly m*k*elem bytes
+    f_scale = copy_bytes / (fetch["gather_kernel"] * 1024.0)
+    w_scale = copy_bytes / (write["gather_kernel"] * 1024.0)
+    main = "gemm_mfma_kernel" if "gemm_mfma_kernel" in fetch else "gemm_f32_kernel"
+    fb = fetch[main] * 1024.0 * f_scale
+    wb = write[main] * 1024.0 * w_scale
+    extra = {}
+    if "splitk_reduce_kernel" in fetch:
+        extra = {"reduce_fetch_bytes": fetch["splitk_reduce_kernel"] * 1024.0 * f_scale,
+                 "reduce_write_bytes": write["splitk_reduce_kernel"] * 1024.0 * w_scale}
+    d = {"workload": w.name, "variant": variant, "kernel": main,
+         "kernel_sha": kernel_source_sha(),
+         "fetch_kib_raw": fetch[main], "write_kib_raw": write[main],
+         "copy_fetch_kib_raw": fetch["gather_kernel"], "copy_write_kib_raw": write["gather_kernel"],
+         "copy_bytes": copy_bytes, "fetch_scale": f_scale, "write_scale": w_scale,
+         "hbm_bytes_per_launch": fb + wb, "fetch_bytes_per_launch": fb,
+         "write_bytes_per_launch": wb, "algorithmic_bytes": w.algorithmic_bytes(),
+         "command": args.command, **extra}
+    path = os.path.join(ROOT, "profiles", f"traffic_{w.name}_{variant}.json")
+    with open(path, "w") as f:
+        json.dump(d, f, indent=1)
+    print(path, json.dumps(d))
+
+
 def main():
     args = parse()
+    if args.summarize_trace or args.summarize_traffic:
+        sys.path.insert(0, ROOT)
+        from all_gather_gemm_agmm_amd import inputs as I
+        w = I.WORKLOADS[args.workload]
+        variant = args.variant or w.variant
+        if variant == "auto":
+            variant = "skinny" if (w.m <= 256 and w.dtype != 2) else "fused"
+        if args.summarize_trace:
+            summarize_trace(args, w, variant)
+        if args.summarize_traffic:
+            summarize_traffic(args, w, variant)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one MI355X only: the all-gather matmul here runs each "
               "peer's shard as a local HBM buffer, so --gpus must be 1", file=sys.stderr)
@@ -147,8 +259,13 @@ def main():
     value = flops / (ms_per_step * 1e-3) / 1e12
 
     if args.only_run:
-        print(json.dumps({"workload": w.name, "variant": used, "ms_per_step": ms_per_step}),
-              flush=True)
+        if (w.k * w.elem_bytes) % 16 == 0:
+            G = torch.empty((w.m, w.k), dtype=tdt, device=dev)
+            for i in range(3):
+                plan.gather(sets[i % nsets][0], G, stream=stream)
+            torch.cuda.synchronize()
+        print(json.dumps({"workload": w.name, "variant": used, "ms_per_step": ms_per_step,
+                          "gather_bytes": w.gather_bytes()}), flush=True)
         plan.close()
         return
 
