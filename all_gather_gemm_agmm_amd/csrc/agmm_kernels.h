@@ -66,7 +66,10 @@ enum TileCfg : int {
   kTile256x256w8 = 6,    // 8 waves (two per SIMD), 128x64 per wave
   kTile256x128w8 = 7,    // 8 waves, 128x32 per wave
   kTile128x64 = 8,       // 4 waves, 64x32 per wave; B stored n x k only
-  kTileCount = 9,
+  kTile256x256pp = 9,    // 8 waves, 128x64 per wave, ping-pong compute/memory groups
+  kTile128x128s8 = 10,   // 8-stage LDS ring (whole short k ranges in flight)
+  kTile128x64s8 = 11,    // same for the 128x64 tile; B stored n x k only
+  kTileCount = 12,
 };
 int tile_bm(int cfg);
 int tile_bn(int cfg);

@@ -130,9 +130,12 @@ __device__ __forceinline__ u32x2_t read_tr(const char* p) {
 }
 
 // vmcnt(n) with the other counters left alone (gfx9 encoding).
+// The scheduling barrier keeps the wait where it is written: the compiler
+// would otherwise hoist it above independent MFMAs and stall them.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_sched_barrier(0);
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
@@ -197,10 +200,10 @@ struct GemmTile {
   static_assert(A_IPW >= 1 && B_IPW >= 1, "tile too small for the load split");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
   static_assert((NST - 1) * LOADS < 64, "vmcnt range");
-  static_assert(NST >= 2 && NST <= 4, "stages");
+  static_assert(NST >= 2 && NST <= 8, "stages");
 };
 
-template <int BM, int BN, int BK, int DT, bool BT, bool SPLIT, int NST, int WAVES, int OCC>
+template <int BM, int BN, int BK, int DT, bool BT, bool SPLIT, int NST, int WAVES, int OCC, bool PP>
 __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 void gemm_mfma_kernel(GemmProblem p) {
   using T = GemmTile<BM, BN, BK, DT, BT, NST, WAVES>;
@@ -374,6 +377,65 @@ void gemm_mfma_kernel(GemmProblem p) {
   constexpr int kMfmaPerSub = T::FM * T::FN;
   constexpr int kReadsPerSub = T::FM + (BT ? T::FN : 2 * T::FN);
 
+  // ---- main loop, ping-pong form (8 waves, two per SIMD) -------------------------
+  // Waves 0-3 (group 0) own output rows [0, BM/2) of the tile, waves 4-7
+  // (group 1) rows [BM/2, BM); the two waves on one SIMD belong to different
+  // groups.  Each k-tile has two phases separated by barriers; in every
+  // phase one group only issues MFMAs from fragments already in registers
+  // while the other group issues its share of the global->LDS loads and
+  // reads the fragments for its next compute phase:
+  //   phase A of tile it: group 0 multiplies tile it;
+  //                       group 1 loads tile it+3, reads tile it
+  //   phase B of tile it: group 1 multiplies tile it;
+  //                       group 0 loads tile it+3, reads tile it+1
+  // A wave that stalls on a load issue therefore never holds up the MFMA
+  // stream of its SIMD.  Tile t is complete in LDS before the barrier that
+  // opens phase B of tile t-1 (every wave waits for its own loads of t
+  // there); tile t+3 goes into the stage of tile t-1, whose last readers
+  // finished before the barrier that closes phase B of tile t-1.
+  if constexpr (PP) {
+    static_assert(WAVES == 8 && T::MID_SYNC && kStages == 4, "ping-pong layout");
+    const int grp = wave >> 2;
+    u32x4_t pa[T::SUB][T::FM], pb[T::SUB][T::FN];
+    auto read_tile = [&](int stage) {
+#pragma unroll
+      for (int s2 = 0; s2 < T::SUB; ++s2)
+        read_frags(smem + stage * T::STAGE_BYTES, s2, pa[s2], pb[s2]);
+    };
+    auto mul_tile = [&]() {
+#pragma unroll
+      for (int s2 = 0; s2 < T::SUB; ++s2) mfma_block(pa[s2], pb[s2]);
+    };
+#pragma unroll
+    for (int t = 0; t < 3; ++t) issue(t, k_begin + t * kBK);
+    wait_vmcnt<2 * T::LOADS>();
+    block_barrier();
+    if (grp == 0) read_tile(0);
+    int st_cur = 0;   // stage of tile it
+    int st_new = 3;   // stage of tile it+3
+    for (int it = 0; it < nk; ++it) {
+      const int st_next = (st_cur + 1) & 3;
+      const int k_new = k_begin + (it + 3) * kBK;
+      if (grp == 0) {
+        mul_tile();
+        wait_vmcnt<T::LOADS>();          // own loads of tile it+1 done
+      } else {
+        issue(st_new, k_new);
+        read_tile(st_cur);
+        wait_vmcnt<2 * T::LOADS>();      // own loads of tile it+1 done
+      }
+      block_barrier();
+      if (grp == 1) {
+        mul_tile();
+      } else {
+        issue(st_new, k_new);
+        read_tile(st_next);
+      }
+      block_barrier();
+      st_cur = st_next;
+      st_new = (st_new + 1) & 3;
+    }
+  } else {
   // ---- main loop ---------------------------------------------------------------
   // Fragment registers alternate between two sets: the LDS reads of substep
   // s+1 are in flight while the MFMAs of substep s run.  Once per k-tile the
@@ -439,6 +501,7 @@ void gemm_mfma_kernel(GemmProblem p) {
     st_cur = st_next;
     st_new = (st_new + 1 == kStages) ? 0 : st_new + 1;
     ++t_new;
+  }
   }
   // No LDS-bound load may still be in flight when the workgroup retires.
   wait_vmcnt<0>();
@@ -523,8 +586,18 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmProblem p) {
   const int64_t plane = (int64_t)M * N;
   const float* src = p.partials + (int64_t)row * N + col;
   if ((N % 4) == 0) {
+    // Up to 8 partial vectors are loaded before any is added, then added in
+    // split order.
     f32x4_t s = *reinterpret_cast<const f32x4_t*>(src);
-    for (int sp = 1; sp < p.splits; ++sp) s += *reinterpret_cast<const f32x4_t*>(src + sp * plane);
+    for (int sp0 = 1; sp0 < p.splits; sp0 += 8) {
+      f32x4_t v[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        if (sp0 + q < p.splits) v[q] = *reinterpret_cast<const f32x4_t*>(src + (sp0 + q) * plane);
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        if (sp0 + q < p.splits) s += v[q];
+    }
     u32x2_t v;
     v[0] = pack2<DT>(s[0], s[1]);
     v[1] = pack2<DT>(s[2], s[3]);
@@ -542,11 +615,11 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmProblem p) {
   }
 }
 
-template <int BM, int BN, int BK, int DT, bool BT, int NST, int WAVES, int OCC>
+template <int BM, int BN, int BK, int DT, bool BT, int NST, int WAVES, int OCC, bool PP = false>
 hipError_t launch_one(const GemmProblem& p, hipStream_t stream) {
   const int ntiles = p.order.num_rb * p.order.num_cb;
   if (p.splits > 1) {
-    hipLaunchKernelGGL((gemm_mfma_kernel<BM, BN, BK, DT, BT, true, NST, WAVES, OCC>),
+    hipLaunchKernelGGL((gemm_mfma_kernel<BM, BN, BK, DT, BT, true, NST, WAVES, OCC, PP>),
                        dim3(ntiles * p.splits), dim3(64 * WAVES), 0, stream, p);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
@@ -554,19 +627,19 @@ hipError_t launch_one(const GemmProblem& p, hipStream_t stream) {
     hipLaunchKernelGGL((splitk_reduce_kernel<DT>), dim3((unsigned)((work + 255) / 256)), dim3(256),
                        0, stream, p);
   } else {
-    hipLaunchKernelGGL((gemm_mfma_kernel<BM, BN, BK, DT, BT, false, NST, WAVES, OCC>),
+    hipLaunchKernelGGL((gemm_mfma_kernel<BM, BN, BK, DT, BT, false, NST, WAVES, OCC, PP>),
                        dim3(ntiles), dim3(64 * WAVES), 0, stream, p);
   }
   return hipGetLastError();
 }
 
-template <int BM, int BN, int BK, int NST, int WAVES, int OCC>
+template <int BM, int BN, int BK, int NST, int WAVES, int OCC, bool PP = false>
 hipError_t launch_tile(const GemmProblem& p, int dtype, bool bt, hipStream_t s) {
   if (dtype == kDtypeBf16)
-    return bt ? launch_one<BM, BN, BK, kDtypeBf16, true, NST, WAVES, OCC>(p, s)
-              : launch_one<BM, BN, BK, kDtypeBf16, false, NST, WAVES, OCC>(p, s);
-  return bt ? launch_one<BM, BN, BK, kDtypeFp16, true, NST, WAVES, OCC>(p, s)
-            : launch_one<BM, BN, BK, kDtypeFp16, false, NST, WAVES, OCC>(p, s);
+    return bt ? launch_one<BM, BN, BK, kDtypeBf16, true, NST, WAVES, OCC, PP>(p, s)
+              : launch_one<BM, BN, BK, kDtypeBf16, false, NST, WAVES, OCC, PP>(p, s);
+  return bt ? launch_one<BM, BN, BK, kDtypeFp16, true, NST, WAVES, OCC, PP>(p, s)
+            : launch_one<BM, BN, BK, kDtypeFp16, false, NST, WAVES, OCC, PP>(p, s);
 }
 
 }  // namespace
@@ -584,6 +657,9 @@ constexpr TileInfo kTiles[kTileCount] = {
     {256, 256, 32, 4, 8, 2},   // kTile256x256w8:    8 waves (2 per SIMD), 128x64 per wave
     {256, 128, 32, 4, 8, 2},   // kTile256x128w8:    8 waves, 128x32 per wave
     {128, 64, 32, 4, 4, 1},    // kTile128x64:       48 KiB; B stored n x k only (skinny m)
+    {256, 256, 32, 4, 8, 2},   // kTile256x256pp:    8 waves in ping-pong groups
+    {128, 128, 32, 8, 4, 1},   // kTile128x128s8:    128 KiB, 7 k-tiles in flight (short k ranges)
+    {128, 64, 32, 8, 4, 1},    // kTile128x64s8:     96 KiB, 7 k-tiles in flight; B n x k only
 };
 
 int tile_bm(int cfg) { return kTiles[cfg].bm; }
@@ -605,8 +681,15 @@ hipError_t launch_gemm_mfma(const GemmProblem& p, int tile_cfg, int dtype, bool 
     case kTile128x64:
       // an n-contiguous B tile of 64 columns is too narrow for its LDS swizzle
       if (!rhs_transpose) return hipErrorInvalidValue;
-      return dtype == kDtypeBf16 ? launch_one<128, 64, 32, kDtypeBf16, true, 4, 4, 1>(p, stream)
-                                 : launch_one<128, 64, 32, kDtypeFp16, true, 4, 4, 1>(p, stream);
+      return dtype == kDtypeBf16 ? launch_one<128, 64, 32, kDtypeBf16, true, 4, 4, 1, false>(p, stream)
+                                 : launch_one<128, 64, 32, kDtypeFp16, true, 4, 4, 1, false>(p, stream);
+    case kTile256x256pp:
+      return launch_tile<256, 256, 32, 4, 8, 2, true>(p, dtype, rhs_transpose, stream);
+    case kTile128x128s8: return launch_tile<128, 128, 32, 8, 4, 1>(p, dtype, rhs_transpose, stream);
+    case kTile128x64s8:
+      if (!rhs_transpose) return hipErrorInvalidValue;
+      return dtype == kDtypeBf16 ? launch_one<128, 64, 32, kDtypeBf16, true, 8, 4, 1, false>(p, stream)
+                                 : launch_one<128, 64, 32, kDtypeFp16, true, 8, 4, 1, false>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -81,10 +81,10 @@ def test_small_ragged(case, variant):
     check_against_oracle(w, shards, B, C)
 
 
-@pytest.mark.parametrize("tile", list(range(9)))
+@pytest.mark.parametrize("tile", list(range(12)))
 @pytest.mark.parametrize("dtype,rt", [(BF16, False), (BF16, True), (FP16, False), (FP16, True)])
 def test_tiles_ragged(tile, dtype, rt):
-    if tile == 8 and not rt:
+    if tile in (8, 11) and not rt:
         pytest.skip("the 128x64 tile takes B stored n x k only")
     w, shards, B = make_case(3, 200, 328, 392, dtype, rt, seed=900 + tile)
     shards_d = [to_device(s, dtype) for s in shards]
@@ -245,10 +245,10 @@ def test_fp16_subnormal_outputs():
     assert rel_err(got, ref) <= BOUND[FP16]
 
 
-@pytest.mark.parametrize("tile,splits", [(8, 4), (8, 7), (1, 3), (2, 2)])
+@pytest.mark.parametrize("tile,splits", [(8, 4), (8, 7), (1, 3), (2, 2), (10, 11), (11, 9)])
 def test_split_k_ragged(tile, splits):
     """Split-K partials + fixed-order reduction, with a ragged last k range."""
-    rt = tile == 8
+    rt = tile in (8, 11)
     w, shards, B = make_case(2, 50, 968, 200 if rt else 208, FP16, rt, seed=400 + tile + splits)
     C, used = run_variant(w, [to_device(s, FP16) for s in shards], to_device(B, FP16), "skinny",
                           tile=tile, splits=splits)
