@@ -153,9 +153,11 @@ bool is_f32(const agmm_plan* p) { return p->dtype == AGMM_FP32; }
 int choose_tile(const agmm_plan* p, int64_t m) {
   if (p->tile >= 0) return p->tile;
   struct Cand { int cfg; double eff; };
-  const Cand cands[] = {{agmm::kTile256x256, 1.0}, {agmm::kTile256x128, 0.9},
-                        {agmm::kTile128x128, 0.8}};
-  int best = agmm::kTile256x256;
+  // The 256x256 tile runs as the 64-deep part ring unless k is short
+  // (its k-tiles would then be mostly padding).
+  const int big = p->k >= 256 ? agmm::kTile256x256r5 : agmm::kTile256x256;
+  const Cand cands[] = {{big, 1.0}, {agmm::kTile256x128, 0.9}, {agmm::kTile128x128, 0.8}};
+  int best = big;
   double best_cost = 1e300;
   for (const Cand& c : cands) {
     const int64_t bm = agmm::tile_bm(c.cfg), bn = agmm::tile_bn(c.cfg);
@@ -235,7 +237,7 @@ int configure(agmm_plan* p) {
     p->bm = agmm::tile_bm(p->tile_used);
     p->bn = agmm::tile_bn(p->tile_used);
   } else if (v == AGMM_VARIANT_STAGED) {
-    p->tile_used = p->tile >= 0 ? p->tile : agmm::kTile256x256;
+    p->tile_used = p->tile >= 0 ? p->tile : (p->k >= 256 ? agmm::kTile256x256r5 : agmm::kTile256x256);
     p->bm = agmm::tile_bm(p->tile_used);
     p->bn = agmm::tile_bn(p->tile_used);
   } else {

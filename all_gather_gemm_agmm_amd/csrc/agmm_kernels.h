@@ -69,7 +69,9 @@ enum TileCfg : int {
   kTile256x256pp = 9,    // 8 waves, 128x64 per wave, ping-pong compute/memory groups
   kTile128x128s8 = 10,   // 8-stage LDS ring (whole short k ranges in flight)
   kTile128x64s8 = 11,    // same for the 128x64 tile; B stored n x k only
-  kTileCount = 12,
+  kTile256x256s5 = 12,   // 5-stage ring: 4 k-tiles in flight (latency of L2 misses)
+  kTile256x256r5 = 13,   // 64-deep k-tiles in a ring of 5 operand slots (whole L2 lines per load)
+  kTileCount = 14,
 };
 int tile_bm(int cfg);
 int tile_bn(int cfg);

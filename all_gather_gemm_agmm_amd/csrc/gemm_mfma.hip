@@ -124,6 +124,15 @@ __device__ __forceinline__ void load_lds16(const void* gsrc, char* lds_block) {
                : "m0");
 }
 
+// Same, with the LDS destination given as a 32-bit LDS address (no generic
+// pointer conversion per load).
+__device__ __forceinline__ void load_lds16_at(const void* gsrc, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(gsrc), "s"(__builtin_amdgcn_readfirstlane(lds_addr))
+               : "m0");
+}
+
 __device__ __forceinline__ u32x2_t read_tr(const char* p) {
   i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(lds_char_t*)p);
   return __builtin_bit_cast(u32x2_t, v);
@@ -171,7 +180,24 @@ __device__ __forceinline__ void tile_coords(const TileOrder& o, int wg, int nwg,
   rb = o.rb_order ? o.rb_order[rbi] : rbi;
 }
 
-template <int BM, int BN, int BK, int DT, bool BT, int NST, int WAVES>
+// Main-loop forms.
+//   kLoopStages:   ring of NST stages, each one k-tile of A and B.
+//   kLoopPingPong: 8 waves in two groups alternating compute and memory work.
+//   kLoopParts:    ring of NST slots, each holding one operand of one k-tile
+//                  ("part"); the parts alternate A, B, A, B, ...  With an odd
+//                  slot count this keeps 2.5 k-tiles of 64-deep operands in
+//                  LDS, i.e. 128-byte row pieces per load (a whole L2 line)
+//                  with a load depth that whole stages could not fit.
+template <bool B>
+struct BoolTag {
+  static constexpr bool value = B;
+};
+
+constexpr int kLoopStages = 0;
+constexpr int kLoopPingPong = 1;
+constexpr int kLoopParts = 2;
+
+template <int BM, int BN, int BK, int DT, bool BT, int NST, int WAVES, int LOOP = kLoopStages>
 struct GemmTile {
   static constexpr int kStages = NST;
   static constexpr int THREADS = 64 * WAVES;
@@ -185,7 +211,8 @@ struct GemmTile {
   static constexpr int A_BYTES = BM * KROW;
   static constexpr int B_BYTES = BN * KROW;            // same size in both B layouts
   static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
-  static constexpr int LDS_BYTES = kStages * STAGE_BYTES;
+  static constexpr int PART_BYTES = A_BYTES > B_BYTES ? A_BYTES : B_BYTES;
+  static constexpr int LDS_BYTES = LOOP == kLoopParts ? kStages * PART_BYTES : kStages * STAGE_BYTES;
   static constexpr int A_IPW = A_BYTES / 1024 / WAVES; // 1 KiB load instructions per wave
   static constexpr int B_IPW = B_BYTES / 1024 / WAVES;
   static constexpr int LOADS = A_IPW + B_IPW;          // per wave per k-tile
@@ -199,21 +226,26 @@ struct GemmTile {
   static_assert(FM >= 1 && FN >= 1, "tile too small");
   static_assert(A_IPW >= 1 && B_IPW >= 1, "tile too small for the load split");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
-  static_assert((NST - 1) * LOADS < 64, "vmcnt range");
+  static_assert(LOOP == kLoopParts || (NST - 1) * LOADS < 64, "vmcnt range");
   static_assert(NST >= 2 && NST <= 8, "stages");
+  // part ring: 5 slots (parts 2t, 2t+1 = A, B of k-tile t live in slots
+  // (2t) % 5 and (2t+1) % 5), equal part sizes so every part is the same
+  // number of load instructions
+  static_assert(LOOP != kLoopParts || (NST == 5 && A_IPW == B_IPW && SUB >= 2 && 3 * A_IPW < 64),
+                "part ring layout");
 };
 
-template <int BM, int BN, int BK, int DT, bool BT, bool SPLIT, int NST, int WAVES, int OCC, bool PP>
+template <int BM, int BN, int BK, int DT, bool BT, bool SPLIT, int NST, int WAVES, int OCC, int LOOP>
 __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 void gemm_mfma_kernel(GemmProblem p) {
-  using T = GemmTile<BM, BN, BK, DT, BT, NST, WAVES>;
+  using T = GemmTile<BM, BN, BK, DT, BT, NST, WAVES, LOOP>;
   constexpr int kBK = BK;
   constexpr int kStages = T::kStages;
   __shared__ __attribute__((aligned(1024))) char smem[T::LDS_BYTES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: LDS block addresses stay scalar
   const int wm = wave / T::WN, wn = wave % T::WN;
 
   const int M = p.m, N = p.n, K = p.k;
@@ -291,21 +323,26 @@ void gemm_mfma_kernel(GemmProblem p) {
   // Branch-free issue of one k-tile: lanes whose row/column is out of range,
   // or whose chunk lies past k_end (ragged k, or a k-tile past the end that
   // the uniform pipeline still issues), fetch the zero block instead.
-  auto issue = [&](int stage, int k0) {
-    char* sa = smem + stage * T::STAGE_BYTES;
-    char* sb = sa + T::A_BYTES;
+  auto issue_a = [&](char* sa, int k0) {
     const int64_t a_step = (int64_t)k0 * 2;
-    const int64_t b_step = BT ? (int64_t)k0 * 2 : (int64_t)k0 * p.ldb * 2;
 #pragma unroll
     for (int j = 0; j < T::A_IPW; ++j) {
       const bool ok = ((a_ok >> j) & 1) && (k0 + a_kc[j] < k_end);
       load_lds16(ok ? a_src[j] + a_step : zero, sa + (wave * T::A_IPW + j) * 1024);
     }
+  };
+  auto issue_b = [&](char* sb, int k0) {
+    const int64_t b_step = BT ? (int64_t)k0 * 2 : (int64_t)k0 * p.ldb * 2;
 #pragma unroll
     for (int j = 0; j < T::B_IPW; ++j) {
       const bool ok = ((b_ok >> j) & 1) && (k0 + b_kc[j] < k_end);
       load_lds16(ok ? b_src[j] + b_step : zero, sb + (wave * T::B_IPW + j) * 1024);
     }
+  };
+  auto issue = [&](int stage, int k0) {
+    char* sa = smem + stage * T::STAGE_BYTES;
+    issue_a(sa, k0);
+    issue_b(sa + T::A_BYTES, k0);
   };
 
   // ---- LDS fragment read offsets -------------------------------------------
@@ -327,7 +364,7 @@ void gemm_mfma_kernel(GemmProblem p) {
 #pragma unroll
     for (int f = 0; f < T::FN; ++f) {
       const int r = wn * T::TN + f * 32 + l32;
-      b_off[f] = T::A_BYTES + r * T::KROW;
+      b_off[f] = r * T::KROW;
       b_x[f] = hi ^ swz_k<BK>(r);
     }
   }
@@ -346,18 +383,13 @@ void gemm_mfma_kernel(GemmProblem p) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-  auto read_frags = [&](const char* stage, int s, u32x4_t* af, u32x4_t* bfr) {
-#pragma unroll
-    for (int f = 0; f < T::FM; ++f)
-      af[f] = *reinterpret_cast<const u32x4_t*>(stage + a_off[f] + (((2 * s) ^ a_x[f]) << 4));
-    if constexpr (BT) {
-#pragma unroll
-      for (int f = 0; f < T::FN; ++f)
-        bfr[f] = *reinterpret_cast<const u32x4_t*>(stage + b_off[f] + (((2 * s) ^ b_x[f]) << 4));
-    } else {
-      const char* sb = stage + T::A_BYTES;
-#pragma unroll
-      for (int f = 0; f < T::FN; ++f) {
+  // Fragments of k16 substep s from the A operand at `sa` and the B operand at `sb`.
+  auto read_frags2 = [&](const char* sa, const char* sb, int s, u32x4_t* af, u32x4_t* bfr) {
+    // in the order mfma_block consumes them: B0, A0 .. A(FM-1), B1 .. B(FN-1)
+    auto read_b = [&](int f) {
+      if constexpr (BT) {
+        bfr[f] = *reinterpret_cast<const u32x4_t*>(sb + b_off[f] + (((2 * s) ^ b_x[f]) << 4));
+      } else {
         const int n = tr_n[f];
         const int pos = (n >> 3) ^ tr_swz;
         const int within = (n & 7) * 2;
@@ -366,13 +398,24 @@ void gemm_mfma_kernel(GemmProblem p) {
         const u32x2_t hi2 = read_tr(p0 + 4 * T::B_ROW);
         bfr[f] = u32x4_t{lo[0], lo[1], hi2[0], hi2[1]};
       }
-    }
+    };
+    read_b(0);
+#pragma unroll
+    for (int f = 0; f < T::FM; ++f)
+      af[f] = *reinterpret_cast<const u32x4_t*>(sa + a_off[f] + (((2 * s) ^ a_x[f]) << 4));
+#pragma unroll
+    for (int f = 1; f < T::FN; ++f) read_b(f);
   };
+  auto read_frags = [&](const char* stage, int s, u32x4_t* af, u32x4_t* bfr) {
+    read_frags2(stage, stage + T::A_BYTES, s, af, bfr);
+  };
+  // B fragment outermost: the j-th group of MFMAs needs only B0..Bj and the
+  // A fragments, which arrive in that order.
   auto mfma_block = [&](const u32x4_t* af, const u32x4_t* bfr) {
 #pragma unroll
-    for (int i = 0; i < T::FM; ++i)
+    for (int j = 0; j < T::FN; ++j)
 #pragma unroll
-      for (int j = 0; j < T::FN; ++j) acc[i][j] = mfma32<DT>(bfr[j], af[i], acc[i][j]);
+      for (int i = 0; i < T::FM; ++i) acc[i][j] = mfma32<DT>(bfr[j], af[i], acc[i][j]);
   };
   constexpr int kMfmaPerSub = T::FM * T::FN;
   constexpr int kReadsPerSub = T::FM + (BT ? T::FN : 2 * T::FN);
@@ -393,7 +436,117 @@ void gemm_mfma_kernel(GemmProblem p) {
   // opens phase B of tile t-1 (every wave waits for its own loads of t
   // there); tile t+3 goes into the stage of tile t-1, whose last readers
   // finished before the barrier that closes phase B of tile t-1.
-  if constexpr (PP) {
+  // ---- main loop, part ring ----------------------------------------------------
+  // Slot q % 5 receives part q: A of k-tile q/2 for even q, B for odd q.
+  // Parts 0-3 are issued up front.  During k-tile t:
+  //   substeps 0 .. SUB-2: the loads of part 2t+4 (A of t+2) are spread over
+  //     the MFMAs, into the slot of B of t-1 (free since the previous sync);
+  //   substep SUB-1: each wave waits for its own loads of parts 2t+2, 2t+3
+  //     (k-tile t+1; part 2t+4 may still be in flight) and for its LDS reads
+  //     of k-tile t; one barrier; then part 2t+5 (B of t+2) goes into the
+  //     slot of A of t, and the fragments of k-tile t+1 are read while the
+  //     last MFMAs of k-tile t run.
+  // Spreading the loads keeps the L1/L2 request stream even instead of one
+  // burst per k-tile from every CU at once.  Past the end the parts fetch
+  // zeros into slots nobody reads again, so the vmcnt arithmetic is the same
+  // in every iteration.
+  if constexpr (LOOP == kLoopParts) {
+    constexpr int L = T::A_IPW;                       // load instructions per part per wave
+    constexpr int PB = T::PART_BYTES;
+    constexpr int SPREAD = T::SUB - 1;                // substeps that carry A loads
+    // Interior tiles (every row and column in range, whole k-tiles) load
+    // without per-lane masks: the source is the lane's row pointer plus a
+    // uniform k offset, and k-tiles past the end re-read the last k-tile
+    // (valid memory; those slots are never read).  Edge tiles redirect
+    // out-of-range chunks to the zero block.
+    const bool interior = (m0 + BM <= M) && (n0 + BN <= N) && ((k_end - k_begin) % kBK == 0) && nk > 0;
+    auto ring = [&](auto tag) {
+      constexpr bool FAST = decltype(tag)::value;
+      auto a_addr = [&](int j, int t) -> const char* {
+        if constexpr (FAST) {
+          const int kk = k_begin + (t < nk ? t : nk - 1) * kBK;
+          return a_src[j] + (int64_t)kk * 2;
+        } else {
+          const int kk = k_begin + t * kBK;
+          const bool ok = ((a_ok >> j) & 1) && (kk + a_kc[j] < k_end);
+          return ok ? a_src[j] + (int64_t)kk * 2 : zero;
+        }
+      };
+      auto b_addr = [&](int j, int t) -> const char* {
+        if constexpr (FAST) {
+          const int kk = k_begin + (t < nk ? t : nk - 1) * kBK;
+          return b_src[j] + (BT ? (int64_t)kk * 2 : (int64_t)kk * p.ldb * 2);
+        } else {
+          const int kk = k_begin + t * kBK;
+          const bool ok = ((b_ok >> j) & 1) && (kk + b_kc[j] < k_end);
+          return ok ? b_src[j] + (BT ? (int64_t)kk * 2 : (int64_t)kk * p.ldb * 2) : zero;
+        }
+      };
+      const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_char_t*)smem + wave * (T::A_IPW * 1024);
+      auto put_a = [&](int slot, int t, int j0, int j1) {
+#pragma unroll
+        for (int j = j0; j < j1; ++j) load_lds16_at(a_addr(j, t), lds0 + slot * PB + j * 1024);
+      };
+      auto put_b = [&](int slot, int t) {
+#pragma unroll
+        for (int j = 0; j < T::B_IPW; ++j) load_lds16_at(b_addr(j, t), lds0 + slot * PB + j * 1024);
+      };
+      u32x4_t fa[2][T::FM], fb[2][T::FN];
+      put_a(0, 0, 0, L);
+      put_b(1, 0);
+      put_a(2, 1, 0, L);
+      put_b(3, 1);
+      wait_vmcnt<2 * L>();
+      block_barrier();
+      read_frags2(smem, smem + PB, 0, fa[0], fb[0]);
+      int sa_slot = 0, sb_slot = 1;   // slots of A and B of k-tile it
+      for (int it = 0; it < nk; ++it) {
+        const char* sa = smem + sa_slot * PB;
+        const char* sb = smem + sb_slot * PB;
+        const int a_new = sb_slot + 3 >= 5 ? sb_slot - 2 : sb_slot + 3;   // slot of B of it-1
+        const int na = sa_slot + 2 >= 5 ? sa_slot - 3 : sa_slot + 2;
+        const int nb = sb_slot + 2 >= 5 ? sb_slot - 3 : sb_slot + 2;
+#pragma unroll
+        for (int s = 0; s < T::SUB; ++s) {
+          int nv;
+          if (s == T::SUB - 1) {
+            wait_vmcnt<L>();
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            block_barrier();
+            read_frags2(smem + na * PB, smem + nb * PB, 0, fa[0], fb[0]);
+            put_b(sa_slot, it + 2);
+            nv = L;
+          } else {
+            const int j0 = s * L / SPREAD, j1 = (s + 1) * L / SPREAD;
+            read_frags2(sa, sb, s + 1, fa[(s + 1) & 1], fb[(s + 1) & 1]);
+            put_a(a_new, it + 2, j0, j1);
+            nv = j1 - j0;
+          }
+          mfma_block(fa[s & 1], fb[s & 1]);
+          // interleave: MFMA, LDS read, ... (all reads first: the next
+          // substep waits on them), then MFMA, global->LDS load(s), ...
+          constexpr int nr = kReadsPerSub < kMfmaPerSub ? kReadsPerSub : kMfmaPerSub;
+          const int left = kMfmaPerSub - nr;
+#pragma unroll
+          for (int q = 0; q < nr; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          }
+#pragma unroll
+          for (int q = 0; q < left; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+#pragma unroll
+            for (int r = q * nv / left; r < (q + 1) * nv / left; ++r)
+              __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+          }
+        }
+        sa_slot = na;
+        sb_slot = nb;
+      }
+    };
+    if (interior) ring(BoolTag<true>{});
+    else ring(BoolTag<false>{});
+  } else if constexpr (LOOP == kLoopPingPong) {
     static_assert(WAVES == 8 && T::MID_SYNC && kStages == 4, "ping-pong layout");
     const int grp = wave >> 2;
     u32x4_t pa[T::SUB][T::FM], pb[T::SUB][T::FN];
@@ -615,11 +768,11 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmProblem p) {
   }
 }
 
-template <int BM, int BN, int BK, int DT, bool BT, int NST, int WAVES, int OCC, bool PP = false>
+template <int BM, int BN, int BK, int DT, bool BT, int NST, int WAVES, int OCC, int LOOP = kLoopStages>
 hipError_t launch_one(const GemmProblem& p, hipStream_t stream) {
   const int ntiles = p.order.num_rb * p.order.num_cb;
   if (p.splits > 1) {
-    hipLaunchKernelGGL((gemm_mfma_kernel<BM, BN, BK, DT, BT, true, NST, WAVES, OCC, PP>),
+    hipLaunchKernelGGL((gemm_mfma_kernel<BM, BN, BK, DT, BT, true, NST, WAVES, OCC, LOOP>),
                        dim3(ntiles * p.splits), dim3(64 * WAVES), 0, stream, p);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
@@ -627,19 +780,19 @@ hipError_t launch_one(const GemmProblem& p, hipStream_t stream) {
     hipLaunchKernelGGL((splitk_reduce_kernel<DT>), dim3((unsigned)((work + 255) / 256)), dim3(256),
                        0, stream, p);
   } else {
-    hipLaunchKernelGGL((gemm_mfma_kernel<BM, BN, BK, DT, BT, false, NST, WAVES, OCC, PP>),
+    hipLaunchKernelGGL((gemm_mfma_kernel<BM, BN, BK, DT, BT, false, NST, WAVES, OCC, LOOP>),
                        dim3(ntiles), dim3(64 * WAVES), 0, stream, p);
   }
   return hipGetLastError();
 }
 
-template <int BM, int BN, int BK, int NST, int WAVES, int OCC, bool PP = false>
+template <int BM, int BN, int BK, int NST, int WAVES, int OCC, int LOOP = kLoopStages>
 hipError_t launch_tile(const GemmProblem& p, int dtype, bool bt, hipStream_t s) {
   if (dtype == kDtypeBf16)
-    return bt ? launch_one<BM, BN, BK, kDtypeBf16, true, NST, WAVES, OCC, PP>(p, s)
-              : launch_one<BM, BN, BK, kDtypeBf16, false, NST, WAVES, OCC, PP>(p, s);
-  return bt ? launch_one<BM, BN, BK, kDtypeFp16, true, NST, WAVES, OCC, PP>(p, s)
-            : launch_one<BM, BN, BK, kDtypeFp16, false, NST, WAVES, OCC, PP>(p, s);
+    return bt ? launch_one<BM, BN, BK, kDtypeBf16, true, NST, WAVES, OCC, LOOP>(p, s)
+              : launch_one<BM, BN, BK, kDtypeBf16, false, NST, WAVES, OCC, LOOP>(p, s);
+  return bt ? launch_one<BM, BN, BK, kDtypeFp16, true, NST, WAVES, OCC, LOOP>(p, s)
+            : launch_one<BM, BN, BK, kDtypeFp16, false, NST, WAVES, OCC, LOOP>(p, s);
 }
 
 }  // namespace
@@ -660,6 +813,8 @@ constexpr TileInfo kTiles[kTileCount] = {
     {256, 256, 32, 4, 8, 2},   // kTile256x256pp:    8 waves in ping-pong groups
     {128, 128, 32, 8, 4, 1},   // kTile128x128s8:    128 KiB, 7 k-tiles in flight (short k ranges)
     {128, 64, 32, 8, 4, 1},    // kTile128x64s8:     96 KiB, 7 k-tiles in flight; B n x k only
+    {256, 256, 32, 5, 4, 1},   // kTile256x256s5:    160 KiB (all of LDS), 4 k-tiles in flight
+    {256, 256, 64, 5, 4, 1},   // kTile256x256r5:    160 KiB part ring, 64-deep k-tiles
 };
 
 int tile_bm(int cfg) { return kTiles[cfg].bm; }
@@ -681,15 +836,18 @@ hipError_t launch_gemm_mfma(const GemmProblem& p, int tile_cfg, int dtype, bool 
     case kTile128x64:
       // an n-contiguous B tile of 64 columns is too narrow for its LDS swizzle
       if (!rhs_transpose) return hipErrorInvalidValue;
-      return dtype == kDtypeBf16 ? launch_one<128, 64, 32, kDtypeBf16, true, 4, 4, 1, false>(p, stream)
-                                 : launch_one<128, 64, 32, kDtypeFp16, true, 4, 4, 1, false>(p, stream);
+      return dtype == kDtypeBf16 ? launch_one<128, 64, 32, kDtypeBf16, true, 4, 4, 1>(p, stream)
+                                 : launch_one<128, 64, 32, kDtypeFp16, true, 4, 4, 1>(p, stream);
     case kTile256x256pp:
-      return launch_tile<256, 256, 32, 4, 8, 2, true>(p, dtype, rhs_transpose, stream);
+      return launch_tile<256, 256, 32, 4, 8, 2, kLoopPingPong>(p, dtype, rhs_transpose, stream);
     case kTile128x128s8: return launch_tile<128, 128, 32, 8, 4, 1>(p, dtype, rhs_transpose, stream);
     case kTile128x64s8:
       if (!rhs_transpose) return hipErrorInvalidValue;
-      return dtype == kDtypeBf16 ? launch_one<128, 64, 32, kDtypeBf16, true, 8, 4, 1, false>(p, stream)
-                                 : launch_one<128, 64, 32, kDtypeFp16, true, 8, 4, 1, false>(p, stream);
+      return dtype == kDtypeBf16 ? launch_one<128, 64, 32, kDtypeBf16, true, 8, 4, 1>(p, stream)
+                                 : launch_one<128, 64, 32, kDtypeFp16, true, 8, 4, 1>(p, stream);
+    case kTile256x256s5: return launch_tile<256, 256, 32, 5, 4, 1>(p, dtype, rhs_transpose, stream);
+    case kTile256x256r5:
+      return launch_tile<256, 256, 64, 5, 4, 1, kLoopParts>(p, dtype, rhs_transpose, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -152,7 +152,15 @@ int agmm_run_gathered(agmm_plan_t plan, const void *gathered, const void *B, voi
  *   "variant"       agmm_variant
  *   "pvalue"        >= 1: tile-rows of each shard per staged chunk
  *   "nbuf"          >= 1: ring slots for the staged variant
- *   "tile"          0: 256x256, 1: 128x128, 2: 256x128 output tile (bf16/fp16)
+ *   "tile"          -1: automatic, else a compiled bf16/fp16 tile shape:
+ *                   0 256x256 (32-deep k-tiles, 4 stages), 1 128x128,
+ *                   2 256x128, 3 256x256 (64-deep, 2 stages), 4 256x128
+ *                   (64-deep), 5 128x128 (64-deep), 6 256x256 (8 waves),
+ *                   7 256x128 (8 waves), 8 128x64 (rhs_transpose only),
+ *                   9 256x256 (8 waves, ping-pong), 10 128x128 (8 stages),
+ *                   11 128x64 (8 stages, rhs_transpose only), 12 256x256
+ *                   (5 stages), 13 256x256 (64-deep k-tiles in a 5-slot
+ *                   operand ring; the automatic choice for k >= 256)
  *   "splits"        >= 1: k-splits for the skinny variant
  *   "local_shard"   0 .. num_shards-1: where the ring order starts
  *   "order"         0: ring order from local_shard, 1: natural order

@@ -81,7 +81,7 @@ def test_small_ragged(case, variant):
     check_against_oracle(w, shards, B, C)
 
 
-@pytest.mark.parametrize("tile", list(range(12)))
+@pytest.mark.parametrize("tile", list(range(14)))
 @pytest.mark.parametrize("dtype,rt", [(BF16, False), (BF16, True), (FP16, False), (FP16, True)])
 def test_tiles_ragged(tile, dtype, rt):
     if tile in (8, 11) and not rt:
