@@ -661,7 +661,62 @@ void gemm_mfma_kernel(GemmProblem p) {
 
   // ---- epilogue --------------------------------------------------------------
   // acc[i][j][4q + e] holds C[m0 + wm*TM + i*32 + l32][n0 + wn*TN + j*32 + 8q + 4hi + e].
+  //
+  // Interior tiles with 16-byte aligned C rows go through LDS: every wave
+  // writes its converted sub-tile into a [BM][BN] staging tile (16-byte
+  // chunk c of row r at position c ^ (r % chunks-per-row), which spreads
+  // the 32 rows one ds_write touches over the banks), then the workgroup
+  // writes C row by row, 16 bytes per lane and whole rows per group of
+  // lanes, instead of 16-byte pieces of 32 different rows per store.
+  constexpr int kRowB = BN * 2;            // bytes of a staged C row
+  constexpr int kChunks = kRowB / 16;      // 16-byte chunks per row
+  static_assert(T::LDS_BYTES >= BM * kRowB, "LDS too small to stage the C tile");
+  static_assert((kChunks & (kChunks - 1)) == 0 && T::THREADS % kChunks == 0, "staging layout");
+  bool staged = false;
   if constexpr (!SPLIT) {
+    staged = (m0 + BM <= M) && (n0 + BN <= N) && (p.ldc % 8) == 0 &&
+             ((reinterpret_cast<uintptr_t>(p.c) & 15) == 0);
+  }
+  if (staged) {
+    block_barrier();   // every wave's fragment reads and LDS-bound loads are done
+#pragma unroll
+    for (int i = 0; i < T::FM; ++i) {
+      const int r = wm * T::TM + i * 32 + l32;
+      char* row = smem + r * kRowB;
+#pragma unroll
+      for (int j = 0; j < T::FN; ++j) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int c = wn * T::TN + j * 32 + 8 * q;          // first column of the chunk
+          const int pos = (c >> 3) ^ (r & (kChunks - 1));
+          const f32x16_t& a = acc[i][j];
+          u32x2_t v;
+          v[0] = pack2<DT>(a[4 * q + 0], a[4 * q + 1]);
+          v[1] = pack2<DT>(a[4 * q + 2], a[4 * q + 3]);
+          *reinterpret_cast<u32x2_t*>(row + pos * 16 + hi * 8) = v;
+        }
+      }
+    }
+    block_barrier();
+    constexpr int kRowsPerPass = T::THREADS / kChunks;
+    const int ch = tid % kChunks;
+    int r = tid / kChunks;
+    int gi = m0 + r;
+    int g = gi / p.rows.rows_per_group;
+    int t = gi - g * p.rows.rows_per_group;
+    uint16_t* cbase = static_cast<uint16_t*>(p.c) + n0 + ch * 8;
+#pragma unroll 4
+    for (; r < BM; r += kRowsPerPass) {
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(smem + r * kRowB + ((ch ^ (r & (kChunks - 1))) << 4));
+      const int64_t crow = (int64_t)g * p.rows.c_group_rows + p.rows.c_row_off + t;
+      *reinterpret_cast<u32x4_t*>(cbase + crow * p.ldc) = v;
+      t += kRowsPerPass;
+      while (t >= p.rows.rows_per_group) {
+        t -= p.rows.rows_per_group;
+        ++g;
+      }
+    }
+  } else if constexpr (!SPLIT) {
     const bool vec_ok = (N % 4) == 0 && (p.ldc % 4) == 0;
 #pragma unroll
     for (int i = 0; i < T::FM; ++i) {
