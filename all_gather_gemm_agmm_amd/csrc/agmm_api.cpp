@@ -153,10 +153,12 @@ bool is_f32(const agmm_plan* p) { return p->dtype == AGMM_FP32; }
 int choose_tile(const agmm_plan* p, int64_t m) {
   if (p->tile >= 0) return p->tile;
   struct Cand { int cfg; double eff; };
-  // The 256x256 tile runs as the 64-deep part ring unless k is short
-  // (its k-tiles would then be mostly padding).
-  const int big = p->k >= 256 ? agmm::kTile256x256r5 : agmm::kTile256x256;
-  const Cand cands[] = {{big, 1.0}, {agmm::kTile256x128, 0.9}, {agmm::kTile128x128, 0.8}};
+  // The 256x256 and 128x128 tiles run as the 64-deep part ring unless k is
+  // short (its k-tiles would then be mostly padding).
+  const bool deep = p->k >= 256;
+  const int big = deep ? agmm::kTile256x256r5 : agmm::kTile256x256;
+  const int small = deep ? agmm::kTile128x128r5 : agmm::kTile128x128;
+  const Cand cands[] = {{big, 1.0}, {agmm::kTile256x128, 0.9}, {small, 0.8}};
   int best = big;
   double best_cost = 1e300;
   for (const Cand& c : cands) {
@@ -263,14 +265,22 @@ int configure(agmm_plan* p) {
     p->nslots = 1;
     p->slot_bytes = (size_t)p->m * p->k * e;
     ring_bytes = p->slot_bytes;
-  } else if (v == AGMM_VARIANT_SKINNY) {
+  }
+  // split-K: skinny problems always, fused / unfused ones when they have too
+  // few output tiles to give every CU a workgroup.  A power of two of k
+  // ranges (multiples of the k granularity), chosen so that splits * tiles
+  // still fits on the CUs; fp32 partial sums then a fixed-order reduction.
+  if (!is_f32(p) && (v == AGMM_VARIANT_SKINNY || v == AGMM_VARIANT_FUSED || v == AGMM_VARIANT_UNFUSED)) {
     const int64_t tiles = cdiv(p->m, p->bm) * cdiv(p->n, p->bn);
-    // enough k-splits to give every CU a workgroup, rounded down to a power
-    // of two so the k ranges stay even
     int64_t want = p->splits;
     if (want <= 0) {
       want = 1;
-      while (want * 2 * tiles <= p->cu_count) want *= 2;
+      if (v == AGMM_VARIANT_SKINNY || 2 * tiles <= p->cu_count) {
+        // long enough k ranges that the partial sums stay small next to the
+        // operand traffic (skinny problems have no other way to fill the GPU)
+        const int64_t min_k = v == AGMM_VARIANT_SKINNY ? agmm::kTileBK : 1024;
+        while (want * 2 * tiles <= p->cu_count && p->k / (want * 2) >= min_k) want *= 2;
+      }
     }
     want = std::max<int64_t>(1, std::min<int64_t>(want, cdiv(p->k, agmm::kTileBK)));
     p->k_per_split = cdiv(cdiv(p->k, want), agmm::kTileBK) * agmm::kTileBK;
@@ -365,6 +375,15 @@ agmm::GemmProblem base_problem(const agmm_plan* p, const agmm::RowMap& rows, int
   g.splits = 1;
   g.k_per_split = (int32_t)p->k;
   return g;
+}
+
+// Whole-problem launches (not the staged chunks) use the plan's split-K.
+void with_splits(const agmm_plan* p, agmm::GemmProblem& g) {
+  if (p->splits_used > 1) {
+    g.splits = p->splits_used;
+    g.k_per_split = (int32_t)p->k_per_split;
+    g.partials = p->partials;
+  }
 }
 
 int launch_gemm(agmm_plan* p, agmm::GemmProblem& g, hipStream_t s) {
@@ -615,16 +634,10 @@ int agmm_run(agmm_plan_t p, const void* const* shard_ptrs, const void* B, void* 
   std::lock_guard<std::mutex> lk(p->mu);
   hipStream_t s = static_cast<hipStream_t>(stream);
   switch (p->variant_used) {
-    case AGMM_VARIANT_FUSED: {
-      agmm::GemmProblem g = base_problem(p, shard_rows(p, shard_ptrs), p->m, B, C, 0);
-      rc = launch_gemm(p, g, s);
-      return rc == AGMM_OK ? ok() : rc;
-    }
+    case AGMM_VARIANT_FUSED:
     case AGMM_VARIANT_SKINNY: {
       agmm::GemmProblem g = base_problem(p, shard_rows(p, shard_ptrs), p->m, B, C, 0);
-      g.splits = p->splits_used;
-      g.k_per_split = (int32_t)p->k_per_split;
-      g.partials = p->partials;
+      with_splits(p, g);
       rc = launch_gemm(p, g, s);
       return rc == AGMM_OK ? ok() : rc;
     }
@@ -639,6 +652,7 @@ int agmm_run(agmm_plan_t p, const void* const* shard_ptrs, const void* B, void* 
       rm.c_group_rows = 0;
       rm.c_row_off = 0;
       agmm::GemmProblem g = base_problem(p, rm, p->m, B, C, -1);
+      with_splits(p, g);
       rc = launch_gemm(p, g, s);
       return rc == AGMM_OK ? ok() : rc;
     }
@@ -681,11 +695,7 @@ int agmm_run_gathered(agmm_plan_t p, const void* gathered, const void* B, void* 
   rm.c_group_rows = 0;
   rm.c_row_off = 0;
   agmm::GemmProblem g = base_problem(p, rm, p->m, B, C, -1);
-  if (p->variant_used == AGMM_VARIANT_SKINNY && p->splits_used > 1) {
-    g.splits = p->splits_used;
-    g.k_per_split = (int32_t)p->k_per_split;
-    g.partials = p->partials;
-  }
+  with_splits(p, g);
   const int rc = launch_gemm(p, g, static_cast<hipStream_t>(stream));
   return rc == AGMM_OK ? ok() : rc;
 }

@@ -71,7 +71,9 @@ enum TileCfg : int {
   kTile128x64s8 = 11,    // same for the 128x64 tile; B stored n x k only
   kTile256x256s5 = 12,   // 5-stage ring: 4 k-tiles in flight (latency of L2 misses)
   kTile256x256r5 = 13,   // 64-deep k-tiles in a ring of 5 operand slots (whole L2 lines per load)
-  kTileCount = 14,
+  kTile128x128r5 = 14,   // same ring, 128x128, two workgroups per CU
+  kTile128x64r5 = 15,    // same ring, 128x64; B stored n x k only
+  kTileCount = 16,
 };
 int tile_bm(int cfg);
 int tile_bn(int cfg);

@@ -229,9 +229,8 @@ struct GemmTile {
   static_assert(LOOP == kLoopParts || (NST - 1) * LOADS < 64, "vmcnt range");
   static_assert(NST >= 2 && NST <= 8, "stages");
   // part ring: 5 slots (parts 2t, 2t+1 = A, B of k-tile t live in slots
-  // (2t) % 5 and (2t+1) % 5), equal part sizes so every part is the same
-  // number of load instructions
-  static_assert(LOOP != kLoopParts || (NST == 5 && A_IPW == B_IPW && SUB >= 2 && 3 * A_IPW < 64),
+  // (2t) % 5 and (2t+1) % 5), at most 2 A parts and one B part in flight
+  static_assert(LOOP != kLoopParts || (NST == 5 && A_IPW >= B_IPW && SUB >= 2 && 2 * A_IPW + B_IPW < 64),
                 "part ring layout");
 };
 
@@ -451,7 +450,8 @@ void gemm_mfma_kernel(GemmProblem p) {
   // zeros into slots nobody reads again, so the vmcnt arithmetic is the same
   // in every iteration.
   if constexpr (LOOP == kLoopParts) {
-    constexpr int L = T::A_IPW;                       // load instructions per part per wave
+    constexpr int L = T::A_IPW;                       // load instructions per A part per wave
+    constexpr int LB = T::B_IPW;                      // ... per B part
     constexpr int PB = T::PART_BYTES;
     constexpr int SPREAD = T::SUB - 1;                // substeps that carry A loads
     // Interior tiles (every row and column in range, whole k-tiles) load
@@ -482,21 +482,23 @@ void gemm_mfma_kernel(GemmProblem p) {
           return ok ? b_src[j] + (BT ? (int64_t)kk * 2 : (int64_t)kk * p.ldb * 2) : zero;
         }
       };
-      const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_char_t*)smem + wave * (T::A_IPW * 1024);
+      const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_char_t*)smem;
+      const uint32_t lds_a = lds0 + wave * (T::A_IPW * 1024);
+      const uint32_t lds_b = lds0 + wave * (T::B_IPW * 1024);
       auto put_a = [&](int slot, int t, int j0, int j1) {
 #pragma unroll
-        for (int j = j0; j < j1; ++j) load_lds16_at(a_addr(j, t), lds0 + slot * PB + j * 1024);
+        for (int j = j0; j < j1; ++j) load_lds16_at(a_addr(j, t), lds_a + slot * PB + j * 1024);
       };
       auto put_b = [&](int slot, int t) {
 #pragma unroll
-        for (int j = 0; j < T::B_IPW; ++j) load_lds16_at(b_addr(j, t), lds0 + slot * PB + j * 1024);
+        for (int j = 0; j < T::B_IPW; ++j) load_lds16_at(b_addr(j, t), lds_b + slot * PB + j * 1024);
       };
       u32x4_t fa[2][T::FM], fb[2][T::FN];
       put_a(0, 0, 0, L);
       put_b(1, 0);
       put_a(2, 1, 0, L);
       put_b(3, 1);
-      wait_vmcnt<2 * L>();
+      wait_vmcnt<L + LB>();
       block_barrier();
       read_frags2(smem, smem + PB, 0, fa[0], fb[0]);
       int sa_slot = 0, sb_slot = 1;   // slots of A and B of k-tile it
@@ -515,7 +517,7 @@ void gemm_mfma_kernel(GemmProblem p) {
             block_barrier();
             read_frags2(smem + na * PB, smem + nb * PB, 0, fa[0], fb[0]);
             put_b(sa_slot, it + 2);
-            nv = L;
+            nv = LB;
           } else {
             const int j0 = s * L / SPREAD, j1 = (s + 1) * L / SPREAD;
             read_frags2(sa, sb, s + 1, fa[(s + 1) & 1], fb[(s + 1) & 1]);
@@ -870,6 +872,8 @@ constexpr TileInfo kTiles[kTileCount] = {
     {128, 64, 32, 8, 4, 1},    // kTile128x64s8:     96 KiB, 7 k-tiles in flight; B n x k only
     {256, 256, 32, 5, 4, 1},   // kTile256x256s5:    160 KiB (all of LDS), 4 k-tiles in flight
     {256, 256, 64, 5, 4, 1},   // kTile256x256r5:    160 KiB part ring, 64-deep k-tiles
+    {128, 128, 64, 5, 4, 2},   // kTile128x128r5:    80 KiB part ring, two workgroups per CU
+    {128, 64, 64, 5, 4, 2},    // kTile128x64r5:     80 KiB part ring; B stored n x k only
 };
 
 int tile_bm(int cfg) { return kTiles[cfg].bm; }
@@ -903,6 +907,12 @@ hipError_t launch_gemm_mfma(const GemmProblem& p, int tile_cfg, int dtype, bool 
     case kTile256x256s5: return launch_tile<256, 256, 32, 5, 4, 1>(p, dtype, rhs_transpose, stream);
     case kTile256x256r5:
       return launch_tile<256, 256, 64, 5, 4, 1, kLoopParts>(p, dtype, rhs_transpose, stream);
+    case kTile128x128r5:
+      return launch_tile<128, 128, 64, 5, 4, 2, kLoopParts>(p, dtype, rhs_transpose, stream);
+    case kTile128x64r5:
+      if (!rhs_transpose) return hipErrorInvalidValue;
+      return dtype == kDtypeBf16 ? launch_one<128, 64, 64, kDtypeBf16, true, 5, 4, 2, kLoopParts>(p, stream)
+                                 : launch_one<128, 64, 64, kDtypeFp16, true, 5, 4, 2, kLoopParts>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }

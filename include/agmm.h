@@ -160,8 +160,13 @@ int agmm_run_gathered(agmm_plan_t plan, const void *gathered, const void *B, voi
  *                   9 256x256 (8 waves, ping-pong), 10 128x128 (8 stages),
  *                   11 128x64 (8 stages, rhs_transpose only), 12 256x256
  *                   (5 stages), 13 256x256 (64-deep k-tiles in a 5-slot
- *                   operand ring; the automatic choice for k >= 256)
- *   "splits"        >= 1: k-splits for the skinny variant
+ *                   operand ring; the automatic choice for k >= 256), 14 128x128 and
+ *                   15 128x64 (rhs_transpose only) in the same ring
+ *   "splits"        0: automatic, else k-splits (fp32 partial sums, then a
+ *                   fixed-order reduction) for the skinny, fused and unfused
+ *                   variants; automatic splits are used by the skinny
+ *                   variant and by fused/unfused problems whose output tiles
+ *                   fill at most half of the CUs
  *   "local_shard"   0 .. num_shards-1: where the ring order starts
  *   "order"         0: ring order from local_shard, 1: natural order
  *   "group_m"       >= 1: row blocks walked together (L2 reuse)

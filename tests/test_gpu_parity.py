@@ -81,12 +81,16 @@ def test_small_ragged(case, variant):
     check_against_oracle(w, shards, B, C)
 
 
-@pytest.mark.parametrize("tile", list(range(14)))
+@pytest.mark.parametrize("tile", list(range(16)))
 @pytest.mark.parametrize("dtype,rt", [(BF16, False), (BF16, True), (FP16, False), (FP16, True)])
-def test_tiles_ragged(tile, dtype, rt):
-    if tile in (8, 11) and not rt:
+@pytest.mark.parametrize("k", [328, 384])
+def test_tiles_ragged(tile, dtype, rt, k):
+    """Every tile shape against the oracle on ragged m and n; k = 328 leaves a
+    ragged last k-tile, k = 384 is whole 64-deep k-tiles, so interior tiles
+    take the unmasked load path."""
+    if tile in (8, 11, 15) and not rt:
         pytest.skip("the 128x64 tile takes B stored n x k only")
-    w, shards, B = make_case(3, 200, 328, 392, dtype, rt, seed=900 + tile)
+    w, shards, B = make_case(3, 200, k, 392, dtype, rt, seed=900 + tile + k)
     shards_d = [to_device(s, dtype) for s in shards]
     B_d = to_device(B, dtype)
     C, _ = run_variant(w, shards_d, B_d, "fused", tile=tile)
@@ -245,15 +249,33 @@ def test_fp16_subnormal_outputs():
     assert rel_err(got, ref) <= BOUND[FP16]
 
 
-@pytest.mark.parametrize("tile,splits", [(8, 4), (8, 7), (1, 3), (2, 2), (10, 11), (11, 9)])
+@pytest.mark.parametrize("tile,splits", [(8, 4), (8, 7), (1, 3), (2, 2), (10, 11), (11, 9), (14, 3), (15, 5)])
 def test_split_k_ragged(tile, splits):
     """Split-K partials + fixed-order reduction, with a ragged last k range."""
-    rt = tile in (8, 11)
+    rt = tile in (8, 11, 15)
     w, shards, B = make_case(2, 50, 968, 200 if rt else 208, FP16, rt, seed=400 + tile + splits)
     C, used = run_variant(w, [to_device(s, FP16) for s in shards], to_device(B, FP16), "skinny",
                           tile=tile, splits=splits)
     assert used == agmm.AGMM_VARIANT_SKINNY
     check_against_oracle(w, shards, B, C)
+
+
+@pytest.mark.parametrize("variant,tile,splits,rt", [("fused", 13, 3, False), ("fused", 1, 0, False),
+                                                   ("unfused", 5, 2, True), ("fused", 0, 2, True),
+                                                   ("fused", 13, 0, True)])
+def test_split_k_fused_unfused(variant, tile, splits, rt):
+    """Split-K on the fused and unfused variants (explicit and automatic k
+    ranges), ragged m, n and a ragged last k range."""
+    w, shards, B = make_case(2, 200, 2248, 264, BF16, rt, seed=450 + tile + splits)
+    plan = agmm.Plan(w.num_shards, w.m_per_shard, w.k, w.n_local, BF16, rt, variant=variant,
+                     tile=tile, splits=splits)
+    try:
+        assert plan.get("splits") > 1
+        C = plan.run([to_device(s, BF16) for s in shards], to_device(B, BF16))
+        torch.cuda.synchronize()
+        check_against_oracle(w, shards, B, C)
+    finally:
+        plan.close()
 
 
 def test_repeated_runs_fresh_inputs():
