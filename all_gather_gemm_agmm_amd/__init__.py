@@ -33,6 +33,7 @@ EXPORTS = [
     ("agmm_run", _ci, [_vp, ctypes.POINTER(_vp), _vp, _vp, _vp]),
     ("agmm_gather", _ci, [_vp, ctypes.POINTER(_vp), _vp, _vp]),
     ("agmm_run_gathered", _ci, [_vp, _vp, _vp, _vp, _vp]),
+    ("agmm_run_gather_out", _ci, [_vp, ctypes.POINTER(_vp), _vp, _vp, _vp, _vp]),
     ("agmm_plan_set_int", _ci, [_vp, _cc, _i64]),
     ("agmm_plan_get_int", _ci, [_vp, _cc, ctypes.POINTER(_i64)]),
     ("agmm_plan_workspace_bytes", ctypes.c_size_t, [_vp]),
@@ -110,6 +111,12 @@ def agmm_gather(plan, shard_ptrs: Sequence[int], gathered: int, stream: int) -> 
 
 def agmm_run_gathered(plan, gathered: int, B: int, C: int, stream: int) -> int:
     return _check(load_library().agmm_run_gathered(plan, gathered, B, C, stream))
+
+
+def agmm_run_gather_out(plan, shard_ptrs: Sequence[int], B: int, C: int, gathered: int,
+                        stream: int) -> int:
+    return _check(load_library().agmm_run_gather_out(plan, _ptr_table(shard_ptrs), B, C, gathered,
+                                                     stream))
 
 
 def agmm_plan_set_int(plan, key: str, value: int) -> int:
@@ -236,6 +243,24 @@ class Plan:
         agmm_run(self.handle, [s.data_ptr() for s in shards], B.data_ptr(), C.data_ptr(),
                  _stream_handle(stream))
         return C
+
+    def run_gather_out(self, shards, B, C=None, gathered=None, stream=None):
+        """C = concat(shards) @ B and the gathered operand; returns (C, gathered)."""
+        import torch
+        if len(shards) != self.num_shards:
+            raise ValueError(f"expected {self.num_shards} shards, got {len(shards)}")
+        for r, s in enumerate(shards):
+            self._check_tensor(s, (self.m_per_shard, self.k), f"shards[{r}]")
+        self._check_tensor(B, self.b_shape(), "B")
+        if C is None:
+            C = torch.empty((self.m, self.n_local), dtype=_torch_dtype(self.dtype), device=B.device)
+        if gathered is None:
+            gathered = torch.empty((self.m, self.k), dtype=_torch_dtype(self.dtype), device=B.device)
+        self._check_tensor(C, (self.m, self.n_local), "C")
+        self._check_tensor(gathered, (self.m, self.k), "gathered")
+        agmm_run_gather_out(self.handle, [s.data_ptr() for s in shards], B.data_ptr(), C.data_ptr(),
+                            gathered.data_ptr(), _stream_handle(stream))
+        return C, gathered
 
     def gather(self, shards, out=None, stream=None):
         import torch

@@ -136,6 +136,7 @@ struct agmm_plan {
   std::vector<int32_t> order_len;
   hipStream_t copy_stream = nullptr;
   hipEvent_t ev_entry = nullptr;
+  hipEvent_t ev_side = nullptr;   // end of a side gather on the copy stream
   std::vector<hipEvent_t> ev_ready, ev_free;
   // timing
   bool timing = false;
@@ -239,7 +240,9 @@ int configure(agmm_plan* p) {
     p->bm = agmm::tile_bm(p->tile_used);
     p->bn = agmm::tile_bn(p->tile_used);
   } else if (v == AGMM_VARIANT_STAGED) {
-    p->tile_used = p->tile >= 0 ? p->tile : (p->k >= 256 ? agmm::kTile256x256r5 : agmm::kTile256x256);
+    // tile chosen for one chunk's launch (pvalue tile-rows of every shard)
+    const int64_t chunk_m = (int64_t)p->N * std::min<int64_t>(p->m_s, (int64_t)p->pvalue * 256);
+    p->tile_used = choose_tile(p, chunk_m);
     p->bm = agmm::tile_bm(p->tile_used);
     p->bn = agmm::tile_bn(p->tile_used);
   } else {
@@ -266,12 +269,15 @@ int configure(agmm_plan* p) {
     p->slot_bytes = (size_t)p->m * p->k * e;
     ring_bytes = p->slot_bytes;
   }
-  // split-K: skinny problems always, fused / unfused ones when they have too
-  // few output tiles to give every CU a workgroup.  A power of two of k
+  // split-K: skinny problems always, the other variants when one launch has
+  // too few output tiles to give every CU a workgroup.  A power of two of k
   // ranges (multiples of the k granularity), chosen so that splits * tiles
   // still fits on the CUs; fp32 partial sums then a fixed-order reduction.
-  if (!is_f32(p) && (v == AGMM_VARIANT_SKINNY || v == AGMM_VARIANT_FUSED || v == AGMM_VARIANT_UNFUSED)) {
-    const int64_t tiles = cdiv(p->m, p->bm) * cdiv(p->n, p->bn);
+  // A staged plan's launches are its chunks, which run one after another on
+  // the caller's stream and share one partials buffer.
+  if (!is_f32(p)) {
+    const int64_t launch_m = v == AGMM_VARIANT_STAGED ? (int64_t)p->N * p->rows_per_chunk : p->m;
+    const int64_t tiles = cdiv(launch_m, p->bm) * cdiv(p->n, p->bn);
     int64_t want = p->splits;
     if (want <= 0) {
       want = 1;
@@ -285,7 +291,7 @@ int configure(agmm_plan* p) {
     want = std::max<int64_t>(1, std::min<int64_t>(want, cdiv(p->k, agmm::kTileBK)));
     p->k_per_split = cdiv(cdiv(p->k, want), agmm::kTileBK) * agmm::kTileBK;
     p->splits_used = (int)cdiv(p->k, p->k_per_split);
-    if (p->splits_used > 1) part_bytes = (size_t)p->splits_used * p->m * p->n * sizeof(float);
+    if (p->splits_used > 1) part_bytes = (size_t)p->splits_used * launch_m * p->n * sizeof(float);
   }
 
   // tile orders (one table per chunk)
@@ -430,7 +436,11 @@ int gather_chunk(agmm_plan* p, const void* const* shards, int64_t row0, int64_t 
   return AGMM_OK;
 }
 
-int run_staged(agmm_plan* p, const void* const* shards, const void* B, void* C, hipStream_t s) {
+// Staged pipeline.  With `gathered` == nullptr the chunks go through the
+// plan's ring of slots; otherwise each chunk is copied to its final place in
+// the caller's [m, k] buffer (no slot is reused, so no copy waits for a GEMM).
+int run_staged(agmm_plan* p, const void* const* shards, const void* B, void* C, hipStream_t s,
+               void* gathered = nullptr) {
   hipError_t err = hipEventRecord(p->ev_entry, s);
   if (err != hipSuccess) return hip_err(err, "hipEventRecord");
   err = hipStreamWaitEvent(p->copy_stream, p->ev_entry, 0);
@@ -441,28 +451,32 @@ int run_staged(agmm_plan* p, const void* const* shards, const void* B, void* C, 
     const int slot = c % p->nslots;
     const int64_t row0 = (int64_t)c * p->rows_per_chunk;
     const int64_t rows_c = std::min<int64_t>(p->rows_per_chunk, p->m_s - row0);
-    char* slot_ptr = p->ring + (size_t)slot * p->slot_bytes;
-    if (c >= p->nslots) {
+    // destination of shard g's rows of this chunk: dst + g * dst_group_rows rows
+    char* dst = gathered ? static_cast<char*>(gathered) + (size_t)row0 * p->k * e
+                         : p->ring + (size_t)slot * p->slot_bytes;
+    const int64_t dst_group_rows = gathered ? p->m_s : rows_c;
+    if (!gathered && c >= p->nslots) {
       err = hipStreamWaitEvent(p->copy_stream, p->ev_free[slot], 0);
       if (err != hipSuccess) return hip_err(err, "hipStreamWaitEvent(free)");
     }
-    int rc = gather_chunk(p, shards, row0, rows_c, slot_ptr, rows_c, copy_wgs, p->copy_stream);
+    int rc = gather_chunk(p, shards, row0, rows_c, dst, dst_group_rows, copy_wgs, p->copy_stream);
     if (rc != AGMM_OK) return rc;
     if ((err = hipEventRecord(p->ev_ready[slot], p->copy_stream)) != hipSuccess)
       return hip_err(err, "hipEventRecord(ready)");
     if ((err = hipStreamWaitEvent(s, p->ev_ready[slot], 0)) != hipSuccess)
       return hip_err(err, "hipStreamWaitEvent(ready)");
     agmm::RowMap rm{};
-    for (int g = 0; g < p->N; ++g) rm.a_group[g] = slot_ptr + (size_t)g * rows_c * p->k * e;
+    for (int g = 0; g < p->N; ++g) rm.a_group[g] = dst + (size_t)g * dst_group_rows * p->k * e;
     rm.a_ld = p->k;
     rm.rows_per_group = (int32_t)rows_c;
     rm.num_groups = p->N;
     rm.c_group_rows = p->m_s;
     rm.c_row_off = row0;
     agmm::GemmProblem g = base_problem(p, rm, rows_c * p->N, B, C, c);
+    with_splits(p, g);
     rc = launch_gemm(p, g, s);
     if (rc != AGMM_OK) return rc;
-    if ((err = hipEventRecord(p->ev_free[slot], s)) != hipSuccess)
+    if (!gathered && (err = hipEventRecord(p->ev_free[slot], s)) != hipSuccess)
       return hip_err(err, "hipEventRecord(free)");
   }
   return ok();
@@ -510,7 +524,9 @@ agmm_plan_t agmm_plan_create(int num_shards, int64_t m_per_shard, int64_t k, int
     return nullptr;
   }
   err = hipEventCreateWithFlags(&p->ev_entry, hipEventDisableTiming);
+  if (err == hipSuccess) err = hipEventCreateWithFlags(&p->ev_side, hipEventDisableTiming);
   if (err != hipSuccess) {
+    if (p->ev_entry) hipEventDestroy(p->ev_entry);
     hip_err(err, "hipEventCreate");
     hipStreamDestroy(p->copy_stream);
     delete p;
@@ -700,6 +716,58 @@ int agmm_run_gathered(agmm_plan_t p, const void* gathered, const void* B, void* 
   return rc == AGMM_OK ? ok() : rc;
 }
 
+int agmm_run_gather_out(agmm_plan_t p, const void* const* shard_ptrs, const void* B, void* C,
+                        void* gathered, void* stream) {
+  int rc = check_ptrs(p, shard_ptrs, B, C);
+  if (rc != AGMM_OK) return rc;
+  if (!gathered) return set_err(AGMM_ERR_INVALID_ARG, "gathered is NULL");
+  if (!aligned16(gathered)) return set_err(AGMM_ERR_UNSUPPORTED, "gathered is not 16-byte aligned");
+  if ((p->k * (int64_t)elem_bytes(p->dtype)) % 16 != 0)
+    return set_err(AGMM_ERR_UNSUPPORTED, "the gather copy needs 16-byte rows (k * elem_bytes %% 16 == 0)");
+  std::lock_guard<std::mutex> lk(p->mu);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int copy_wgs = p->copy_wgs > 0 ? p->copy_wgs : p->cu_count;
+  switch (p->variant_used) {
+    case AGMM_VARIANT_STAGED:
+      return run_staged(p, shard_ptrs, B, C, s, gathered);
+    case AGMM_VARIANT_UNFUSED: {
+      // the gather is the first half of this variant anyway
+      rc = gather_chunk(p, shard_ptrs, 0, p->m_s, gathered, p->m_s, 0, s);
+      if (rc != AGMM_OK) return rc;
+      agmm::RowMap rm{};
+      rm.a_group[0] = gathered;
+      rm.a_ld = p->k;
+      rm.rows_per_group = (int32_t)p->m;
+      rm.num_groups = 1;
+      rm.c_group_rows = 0;
+      rm.c_row_off = 0;
+      agmm::GemmProblem g = base_problem(p, rm, p->m, B, C, -1);
+      with_splits(p, g);
+      rc = launch_gemm(p, g, s);
+      return rc == AGMM_OK ? ok() : rc;
+    }
+    default: {
+      // fused / skinny / fp32: the GEMM reads the shards on the caller's
+      // stream while the copy stream writes the gathered operand; the
+      // caller's stream then waits for the copy
+      hipError_t err = hipEventRecord(p->ev_entry, s);
+      if (err == hipSuccess) err = hipStreamWaitEvent(p->copy_stream, p->ev_entry, 0);
+      if (err != hipSuccess) return hip_err(err, "stream fork");
+      rc = gather_chunk(p, shard_ptrs, 0, p->m_s, gathered, p->m_s, copy_wgs, p->copy_stream);
+      if (rc != AGMM_OK) return rc;
+      if ((err = hipEventRecord(p->ev_side, p->copy_stream)) != hipSuccess)
+        return hip_err(err, "hipEventRecord(side)");
+      agmm::GemmProblem g = base_problem(p, shard_rows(p, shard_ptrs), p->m, B, C, 0);
+      with_splits(p, g);
+      rc = launch_gemm(p, g, s);
+      if (rc != AGMM_OK) return rc;
+      if ((err = hipStreamWaitEvent(s, p->ev_side, 0)) != hipSuccess)
+        return hip_err(err, "stream join");
+      return ok();
+    }
+  }
+}
+
 int agmm_plan_timing_begin(agmm_plan_t p) {
   if (!p) return set_err(AGMM_ERR_INVALID_ARG, "plan is NULL");
   std::lock_guard<std::mutex> lk(p->mu);
@@ -747,6 +815,7 @@ void agmm_plan_destroy(agmm_plan_t p) {
   for (hipEvent_t e : p->ev_free) hipEventDestroy(e);
   for (hipEvent_t e : p->tev) hipEventDestroy(e);
   if (p->ev_entry) hipEventDestroy(p->ev_entry);
+  if (p->ev_side) hipEventDestroy(p->ev_side);
   if (p->copy_stream) hipStreamDestroy(p->copy_stream);
   delete p;
 }

@@ -148,6 +148,26 @@ int agmm_run_gathered(agmm_plan_t plan, const void *gathered, const void *B, voi
                       void *stream);
 
 /*
+ * Enqueue C = concat_r(A_r) @ B exactly as agmm_run, and also write the
+ * gathered operand G[r*m_per_shard + i, :] = shard r row i (a bit-exact copy)
+ * to `gathered` [m, k]: the gathered input handed back as a second output,
+ * as the tpu-inference kernel does with its HBM scratch, so that a later
+ * agmm_run_gathered can multiply it against another column block of B
+ * without gathering again (that page's "split n" note).
+ *   staged plans:  each chunk is copied straight to its place in `gathered`
+ *                  and that chunk's GEMM reads it from there (no ring slot);
+ *   unfused plans: gather into `gathered`, then the GEMM reads it;
+ *   fused, skinny and fp32 plans: the GEMM reads the shards on `stream`
+ *                  while the plan's second stream writes `gathered`.
+ * `gathered` is a caller-owned device buffer of the plan's dtype, 16-byte
+ * aligned, not aliasing the shards, B or C; requires k * elem_bytes % 16 == 0
+ * (else AGMM_ERR_UNSUPPORTED).  Same stream rules and return codes as
+ * agmm_run; work enqueued later on `stream` sees both outputs complete.
+ */
+int agmm_run_gather_out(agmm_plan_t plan, const void *const *shard_ptrs, const void *B, void *C,
+                        void *gathered, void *stream);
+
+/*
  * Tune a plan.  Keys (value ranges):
  *   "variant"       agmm_variant
  *   "pvalue"        >= 1: tile-rows of each shard per staged chunk
@@ -163,10 +183,10 @@ int agmm_run_gathered(agmm_plan_t plan, const void *gathered, const void *B, voi
  *                   operand ring; the automatic choice for k >= 256), 14 128x128 and
  *                   15 128x64 (rhs_transpose only) in the same ring
  *   "splits"        0: automatic, else k-splits (fp32 partial sums, then a
- *                   fixed-order reduction) for the skinny, fused and unfused
- *                   variants; automatic splits are used by the skinny
- *                   variant and by fused/unfused problems whose output tiles
- *                   fill at most half of the CUs
+ *                   fixed-order reduction) of every bf16/fp16 launch (for the
+ *                   staged variant: of each chunk's launch); automatic splits
+ *                   are used by the skinny variant and by launches whose
+ *                   output tiles fill at most half of the CUs
  *   "local_shard"   0 .. num_shards-1: where the ring order starts
  *   "order"         0: ring order from local_shard, 1: natural order
  *   "group_m"       >= 1: row blocks walked together (L2 reuse)

@@ -260,15 +260,17 @@ def test_split_k_ragged(tile, splits):
     check_against_oracle(w, shards, B, C)
 
 
-@pytest.mark.parametrize("variant,tile,splits,rt", [("fused", 13, 3, False), ("fused", 1, 0, False),
-                                                   ("unfused", 5, 2, True), ("fused", 0, 2, True),
-                                                   ("fused", 13, 0, True)])
-def test_split_k_fused_unfused(variant, tile, splits, rt):
-    """Split-K on the fused and unfused variants (explicit and automatic k
-    ranges), ragged m, n and a ragged last k range."""
+@pytest.mark.parametrize("variant,tile,splits,rt,pvalue", [
+    ("fused", 13, 3, False, None), ("fused", 1, 0, False, None), ("unfused", 5, 2, True, None),
+    ("fused", 0, 2, True, None), ("fused", 13, 0, True, None),
+    ("staged", 14, 2, False, 1), ("staged", 15, 0, True, 1)])
+def test_split_k_variants(variant, tile, splits, rt, pvalue):
+    """Split-K on the fused, unfused and staged variants (explicit and
+    automatic k ranges; staged: per chunk, two chunks with a ragged second
+    one), ragged m, n and a ragged last k range."""
     w, shards, B = make_case(2, 200, 2248, 264, BF16, rt, seed=450 + tile + splits)
     plan = agmm.Plan(w.num_shards, w.m_per_shard, w.k, w.n_local, BF16, rt, variant=variant,
-                     tile=tile, splits=splits)
+                     tile=tile, splits=splits, pvalue=pvalue)
     try:
         assert plan.get("splits") > 1
         C = plan.run([to_device(s, BF16) for s in shards], to_device(B, BF16))
@@ -312,6 +314,33 @@ def test_run_gathered_matches_fused():
         plan.close()
     assert np.array_equal(to_bits(C1), to_bits(C2))
     check_against_oracle(w, shards, B, C1)
+
+
+@pytest.mark.parametrize("variant,dtype,rt,settings", [
+    ("fused", BF16, False, {"tile": 14}), ("staged", FP16, True, {"pvalue": 1, "tile": 14}),
+    ("unfused", BF16, True, {}), ("skinny", BF16, True, {}), ("fused", FP32, False, {})])
+def test_run_gather_out(variant, dtype, rt, settings):
+    """C and the gathered operand from one call: the gathered buffer is the
+    bit-exact concatenation, C is bit-identical to agmm_run's, and the
+    gathered buffer feeds a second product against another B ("split n")."""
+    m_s = 24 if variant == "skinny" else 200
+    w, shards, B = make_case(3, m_s, 320, 136, dtype, rt, seed=470 + len(variant))
+    _, _, B2 = make_case(3, m_s, 320, 136, dtype, rt, seed=471 + len(variant))
+    sd = [to_device(x, dtype) for x in shards]
+    plan = agmm.Plan(w.num_shards, w.m_per_shard, w.k, w.n_local, dtype, rt, variant=variant,
+                     **settings)
+    try:
+        assert plan.get("variant_used") == agmm.VARIANTS[variant]
+        C, G = plan.run_gather_out(sd, to_device(B, dtype))
+        C_ref = plan.run(sd, to_device(B, dtype))
+        C2 = plan.run_gathered(G, to_device(B2, dtype))
+        torch.cuda.synchronize()
+    finally:
+        plan.close()
+    assert np.array_equal(to_bits(G), np.concatenate(shards, axis=0))
+    assert np.array_equal(to_bits(C), to_bits(C_ref))
+    check_against_oracle(w, shards, B, C)
+    check_against_oracle(w, shards, B2, C2)
 
 
 def test_run_rejects_misaligned_pointer():
