@@ -114,6 +114,7 @@ struct agmm_plan {
   int group_m = 4;
   int xcd_remap = 1;
   int copy_wgs = 0;
+  int gemm_streams = 2;   // staged: chunk GEMMs alternate over this many streams (1 or 2)
   int debug_keep_slots = 0;
   // derived
   int variant_used = AGMM_VARIANT_FUSED;
@@ -135,8 +136,10 @@ struct agmm_plan {
   std::vector<int64_t> order_off;   // offset of chunk c's table
   std::vector<int32_t> order_len;
   hipStream_t copy_stream = nullptr;
+  hipStream_t compute2 = nullptr;   // second GEMM stream: staged chunks alternate
   hipEvent_t ev_entry = nullptr;
   hipEvent_t ev_side = nullptr;   // end of a side gather on the copy stream
+  hipEvent_t ev_c2 = nullptr;     // end of the second GEMM stream's chunks
   std::vector<hipEvent_t> ev_ready, ev_free;
   // timing
   bool timing = false;
@@ -445,6 +448,13 @@ int run_staged(agmm_plan* p, const void* const* shards, const void* B, void* C, 
   if (err != hipSuccess) return hip_err(err, "hipEventRecord");
   err = hipStreamWaitEvent(p->copy_stream, p->ev_entry, 0);
   if (err != hipSuccess) return hip_err(err, "hipStreamWaitEvent");
+  // Odd chunks' GEMMs run on a second stream, so the workgroups of chunk c+1
+  // take the CUs chunk c's workgroups leave (each chunk's launch is usually
+  // a partial round); only the ring-slot events order them.  With split-K the
+  // chunks share one partials buffer and stay on the caller's stream.
+  const bool alt = p->gemm_streams == 2 && p->splits_used == 1 && p->num_chunks > 1;
+  if (alt && (err = hipStreamWaitEvent(p->compute2, p->ev_entry, 0)) != hipSuccess)
+    return hip_err(err, "hipStreamWaitEvent");
   const int64_t e = elem_bytes(p->dtype);
   const int copy_wgs = p->copy_wgs > 0 ? p->copy_wgs : p->cu_count;
   for (int c = 0; c < p->num_chunks; ++c) {
@@ -459,11 +469,16 @@ int run_staged(agmm_plan* p, const void* const* shards, const void* B, void* C, 
       err = hipStreamWaitEvent(p->copy_stream, p->ev_free[slot], 0);
       if (err != hipSuccess) return hip_err(err, "hipStreamWaitEvent(free)");
     }
-    int rc = gather_chunk(p, shards, row0, rows_c, dst, dst_group_rows, copy_wgs, p->copy_stream);
+    // chunk 0's copy has no GEMM to overlap and gets the whole GPU; later
+    // copies run next to a GEMM and are held to one workgroup per CU (unless
+    // the plan sets copy_wgs)
+    const int wgs = (c == 0 && p->copy_wgs == 0) ? 0 : copy_wgs;
+    int rc = gather_chunk(p, shards, row0, rows_c, dst, dst_group_rows, wgs, p->copy_stream);
     if (rc != AGMM_OK) return rc;
     if ((err = hipEventRecord(p->ev_ready[slot], p->copy_stream)) != hipSuccess)
       return hip_err(err, "hipEventRecord(ready)");
-    if ((err = hipStreamWaitEvent(s, p->ev_ready[slot], 0)) != hipSuccess)
+    hipStream_t cs = (alt && (c & 1)) ? p->compute2 : s;
+    if ((err = hipStreamWaitEvent(cs, p->ev_ready[slot], 0)) != hipSuccess)
       return hip_err(err, "hipStreamWaitEvent(ready)");
     agmm::RowMap rm{};
     for (int g = 0; g < p->N; ++g) rm.a_group[g] = dst + (size_t)g * dst_group_rows * p->k * e;
@@ -474,10 +489,14 @@ int run_staged(agmm_plan* p, const void* const* shards, const void* B, void* C, 
     rm.c_row_off = row0;
     agmm::GemmProblem g = base_problem(p, rm, rows_c * p->N, B, C, c);
     with_splits(p, g);
-    rc = launch_gemm(p, g, s);
+    rc = launch_gemm(p, g, cs);
     if (rc != AGMM_OK) return rc;
-    if (!gathered && (err = hipEventRecord(p->ev_free[slot], s)) != hipSuccess)
+    if (!gathered && (err = hipEventRecord(p->ev_free[slot], cs)) != hipSuccess)
       return hip_err(err, "hipEventRecord(free)");
+  }
+  if (alt) {
+    if ((err = hipEventRecord(p->ev_c2, p->compute2)) != hipSuccess) return hip_err(err, "hipEventRecord");
+    if ((err = hipStreamWaitEvent(s, p->ev_c2, 0)) != hipSuccess) return hip_err(err, "stream join");
   }
   return ok();
 }
@@ -525,8 +544,13 @@ agmm_plan_t agmm_plan_create(int num_shards, int64_t m_per_shard, int64_t k, int
   }
   err = hipEventCreateWithFlags(&p->ev_entry, hipEventDisableTiming);
   if (err == hipSuccess) err = hipEventCreateWithFlags(&p->ev_side, hipEventDisableTiming);
+  if (err == hipSuccess) err = hipEventCreateWithFlags(&p->ev_c2, hipEventDisableTiming);
+  if (err == hipSuccess) err = hipStreamCreateWithFlags(&p->compute2, hipStreamNonBlocking);
   if (err != hipSuccess) {
     if (p->ev_entry) hipEventDestroy(p->ev_entry);
+    if (p->ev_side) hipEventDestroy(p->ev_side);
+    if (p->ev_c2) hipEventDestroy(p->ev_c2);
+    if (p->compute2) hipStreamDestroy(p->compute2);
     hip_err(err, "hipEventCreate");
     hipStreamDestroy(p->copy_stream);
     delete p;
@@ -578,6 +602,9 @@ int agmm_plan_set_int(agmm_plan_t p, const char* key, int64_t v) {
   } else if (k == "xcd_remap") {
     if (v != 0 && v != 1) return bad();
     p->xcd_remap = (int)v;
+  } else if (k == "gemm_streams") {
+    if (v < 1 || v > 2) return bad();
+    p->gemm_streams = (int)v;
   } else if (k == "copy_wgs") {
     if (v < 0 || v > 1 << 20) return bad();
     p->copy_wgs = (int)v;
@@ -608,6 +635,7 @@ int agmm_plan_get_int(agmm_plan_t p, const char* key, int64_t* value) {
   else if (k == "group_m") v = p->group_m;
   else if (k == "xcd_remap") v = p->xcd_remap;
   else if (k == "copy_wgs") v = p->copy_wgs;
+  else if (k == "gemm_streams") v = p->gemm_streams;
   else if (k == "debug_keep_slots") v = p->debug_keep_slots;
   else if (k == "num_chunks") v = p->num_chunks;
   else if (k == "rows_per_chunk") v = p->rows_per_chunk;
@@ -809,6 +837,7 @@ int agmm_plan_timing_end(agmm_plan_t p) {
 void agmm_plan_destroy(agmm_plan_t p) {
   if (!p) return;
   if (p->copy_stream) hipStreamSynchronize(p->copy_stream);
+  if (p->compute2) hipStreamSynchronize(p->compute2);
   hipDeviceSynchronize();
   free_resources(p);
   for (hipEvent_t e : p->ev_ready) hipEventDestroy(e);
@@ -816,6 +845,8 @@ void agmm_plan_destroy(agmm_plan_t p) {
   for (hipEvent_t e : p->tev) hipEventDestroy(e);
   if (p->ev_entry) hipEventDestroy(p->ev_entry);
   if (p->ev_side) hipEventDestroy(p->ev_side);
+  if (p->ev_c2) hipEventDestroy(p->ev_c2);
+  if (p->compute2) hipStreamDestroy(p->compute2);
   if (p->copy_stream) hipStreamDestroy(p->copy_stream);
   delete p;
 }

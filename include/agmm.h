@@ -191,7 +191,12 @@ int agmm_run_gather_out(agmm_plan_t plan, const void *const *shard_ptrs, const v
  *   "order"         0: ring order from local_shard, 1: natural order
  *   "group_m"       >= 1: row blocks walked together (L2 reuse)
  *   "xcd_remap"     0/1: keep consecutive tiles on one XCD
- *   "copy_wgs"      >= 0: workgroups of the staged gather copy (0 = auto)
+ *   "copy_wgs"      >= 0: workgroups of the staged gather copy (0 = auto:
+ *                   the first chunk's copy, which has no GEMM to overlap,
+ *                   uses the whole GPU; later ones one workgroup per CU)
+ *   "gemm_streams"  1 or 2 (default 2): staged chunk GEMMs alternate over
+ *                   this many streams, so one chunk's workgroups fill the
+ *                   CUs the previous chunk's leave (1 with split-K)
  *   "debug_keep_slots" 0/1: staged variant uses one slot per chunk (nothing
  *                   is overwritten; for inspection by agmm_plan_slot_ptr)
  * Changing a key that affects the workspace reallocates it (synchronously).

@@ -280,6 +280,29 @@ def test_split_k_variants(variant, tile, splits, rt, pvalue):
         plan.close()
 
 
+@pytest.mark.parametrize("dtype,rt", [(BF16, False), (FP16, True)])
+def test_staged_slot_reuse_alternating_streams(dtype, rt):
+    """Four chunks through two ring slots (each slot reused), chunk GEMMs
+    alternating between the plan's two GEMM streams: same bits as the fused
+    path with the same tile, and the oracle's values."""
+    w, shards, B = make_case(3, 400, 256, 264, dtype, rt, seed=500 + dtype)
+    sd = [to_device(x, dtype) for x in shards]
+    bd = to_device(B, dtype)
+    out = {}
+    for variant, extra in (("staged", {"pvalue": 1, "nbuf": 2}), ("fused", {})):
+        plan = agmm.Plan(3, 400, 256, 264, dtype, rt, variant=variant, tile=14, splits=1, **extra)
+        try:
+            if variant == "staged":
+                assert plan.get("num_chunks") == 4
+            for _ in range(2):      # twice: the second run reuses the ring and events
+                out[variant] = plan.run(sd, bd)
+            torch.cuda.synchronize()
+        finally:
+            plan.close()
+    assert np.array_equal(to_bits(out["staged"]), to_bits(out["fused"]))
+    check_against_oracle(w, shards, B, out["staged"])
+
+
 def test_repeated_runs_fresh_inputs():
     """Back-to-back runs with new inputs (staged ring reuse, split-K counters
     reset): every run matches its own oracle."""
