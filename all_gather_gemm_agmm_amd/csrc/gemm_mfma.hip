@@ -711,7 +711,7 @@ void gemm_mfma_kernel(GemmProblem p) {
     for (; r < BM; r += kRowsPerPass) {
       const u32x4_t v = *reinterpret_cast<const u32x4_t*>(smem + r * kRowB + ((ch ^ (r & (kChunks - 1))) << 4));
       const int64_t crow = (int64_t)g * p.rows.c_group_rows + p.rows.c_row_off + t;
-      *reinterpret_cast<u32x4_t*>(cbase + crow * p.ldc) = v;
+      __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(cbase + crow * p.ldc));   // C is not re-read: keep L2 for A and B
       t += kRowsPerPass;
       while (t >= p.rows.rows_per_group) {
         t -= p.rows.rows_per_group;
