@@ -214,7 +214,10 @@ class Plan:
     def get(self, key: str) -> int:
         return agmm_plan_get_int(self.handle, key)
 
-    def _check_tensor(self, t, shape, name):
+    def _check_tensor(self, t, shape, name, ld_key=None):
+        """Shape / dtype / device checks.  With `ld_key` ("lda", "ldb", "ldc")
+        the tensor may be a row-strided view whose row stride is the plan's
+        setting for that key; otherwise it must be dense row-major."""
         import torch
         if not isinstance(t, torch.Tensor):
             raise TypeError(f"{name} must be a torch.Tensor")
@@ -224,8 +227,16 @@ class Plan:
             raise TypeError(f"{name} has dtype {t.dtype}, plan expects {_torch_dtype(self.dtype)}")
         if tuple(t.shape) != tuple(shape):
             raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
-        if not t.is_contiguous():
-            raise ValueError(f"{name} must be contiguous (row-major)")
+        ld = self.get(ld_key) if ld_key else shape[1]
+        if t.stride(1) != 1 or (shape[0] > 1 and t.stride(0) != ld):
+            raise ValueError(f"{name} must be row-major with rows {ld} elements apart "
+                             f"(stride {tuple(t.stride())})")
+
+    def _new_c(self, device):
+        """A C buffer with the plan's row stride (a view when ldc > n_local)."""
+        import torch
+        ldc = self.get("ldc")
+        return torch.empty((self.m, ldc), dtype=_torch_dtype(self.dtype), device=device)[:, :self.n_local]
 
     def b_shape(self):
         return (self.n_local, self.k) if self.rhs_transpose else (self.k, self.n_local)
@@ -235,11 +246,11 @@ class Plan:
         if len(shards) != self.num_shards:
             raise ValueError(f"expected {self.num_shards} shards, got {len(shards)}")
         for r, s in enumerate(shards):
-            self._check_tensor(s, (self.m_per_shard, self.k), f"shards[{r}]")
-        self._check_tensor(B, self.b_shape(), "B")
+            self._check_tensor(s, (self.m_per_shard, self.k), f"shards[{r}]", "lda")
+        self._check_tensor(B, self.b_shape(), "B", "ldb")
         if C is None:
-            C = torch.empty((self.m, self.n_local), dtype=_torch_dtype(self.dtype), device=B.device)
-        self._check_tensor(C, (self.m, self.n_local), "C")
+            C = self._new_c(B.device)
+        self._check_tensor(C, (self.m, self.n_local), "C", "ldc")
         agmm_run(self.handle, [s.data_ptr() for s in shards], B.data_ptr(), C.data_ptr(),
                  _stream_handle(stream))
         return C
@@ -250,13 +261,13 @@ class Plan:
         if len(shards) != self.num_shards:
             raise ValueError(f"expected {self.num_shards} shards, got {len(shards)}")
         for r, s in enumerate(shards):
-            self._check_tensor(s, (self.m_per_shard, self.k), f"shards[{r}]")
-        self._check_tensor(B, self.b_shape(), "B")
+            self._check_tensor(s, (self.m_per_shard, self.k), f"shards[{r}]", "lda")
+        self._check_tensor(B, self.b_shape(), "B", "ldb")
         if C is None:
-            C = torch.empty((self.m, self.n_local), dtype=_torch_dtype(self.dtype), device=B.device)
+            C = self._new_c(B.device)
         if gathered is None:
             gathered = torch.empty((self.m, self.k), dtype=_torch_dtype(self.dtype), device=B.device)
-        self._check_tensor(C, (self.m, self.n_local), "C")
+        self._check_tensor(C, (self.m, self.n_local), "C", "ldc")
         self._check_tensor(gathered, (self.m, self.k), "gathered")
         agmm_run_gather_out(self.handle, [s.data_ptr() for s in shards], B.data_ptr(), C.data_ptr(),
                             gathered.data_ptr(), _stream_handle(stream))
@@ -265,7 +276,7 @@ class Plan:
     def gather(self, shards, out=None, stream=None):
         import torch
         for r, s in enumerate(shards):
-            self._check_tensor(s, (self.m_per_shard, self.k), f"shards[{r}]")
+            self._check_tensor(s, (self.m_per_shard, self.k), f"shards[{r}]", "lda")
         if out is None:
             out = torch.empty((self.m, self.k), dtype=_torch_dtype(self.dtype), device=shards[0].device)
         self._check_tensor(out, (self.m, self.k), "gathered")
@@ -275,10 +286,10 @@ class Plan:
     def run_gathered(self, gathered, B, C=None, stream=None):
         import torch
         self._check_tensor(gathered, (self.m, self.k), "gathered")
-        self._check_tensor(B, self.b_shape(), "B")
+        self._check_tensor(B, self.b_shape(), "B", "ldb")
         if C is None:
-            C = torch.empty((self.m, self.n_local), dtype=_torch_dtype(self.dtype), device=B.device)
-        self._check_tensor(C, (self.m, self.n_local), "C")
+            C = self._new_c(B.device)
+        self._check_tensor(C, (self.m, self.n_local), "C", "ldc")
         agmm_run_gathered(self.handle, gathered.data_ptr(), B.data_ptr(), C.data_ptr(),
                           _stream_handle(stream))
         return C

@@ -93,6 +93,10 @@ int validate(int N, int64_t m_s, int64_t k, int64_t n, int dtype, int rt) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+int64_t lda_of(const agmm_plan* p);
+int64_t ldb_of(const agmm_plan* p);
+int64_t ldc_of(const agmm_plan* p);
+
 }  // namespace
 
 struct agmm_plan {
@@ -114,6 +118,8 @@ struct agmm_plan {
   int group_m = 4;
   int xcd_remap = 1;
   int copy_wgs = 0;
+  // element strides between rows of the caller's buffers (0: dense)
+  int64_t lda = 0, ldb = 0, ldc = 0;
   int gemm_streams = 2;   // staged: chunk GEMMs alternate over this many streams (1 or 2)
   int debug_keep_slots = 0;
   // derived
@@ -154,6 +160,10 @@ bool is_f32(const agmm_plan* p) { return p->dtype == AGMM_FP32; }
 
 // Tile choice for the MFMA path: fewest "tile waves" weighted by the
 // per-tile efficiency of the larger shapes.
+int64_t lda_of(const agmm_plan* p) { return p->lda ? p->lda : p->k; }
+int64_t ldb_of(const agmm_plan* p) { return p->ldb ? p->ldb : (p->rt ? p->k : p->n); }
+int64_t ldc_of(const agmm_plan* p) { return p->ldc ? p->ldc : p->n; }
+
 int choose_tile(const agmm_plan* p, int64_t m) {
   if (p->tile >= 0) return p->tile;
   struct Cand { int cfg; double eff; };
@@ -354,7 +364,7 @@ int configure(agmm_plan* p) {
 agmm::RowMap shard_rows(const agmm_plan* p, const void* const* shards) {
   agmm::RowMap r{};
   for (int g = 0; g < p->N; ++g) r.a_group[g] = shards[g];
-  r.a_ld = p->k;
+  r.a_ld = lda_of(p);
   r.rows_per_group = (int32_t)p->m_s;
   r.num_groups = p->N;
   r.c_group_rows = p->m_s;
@@ -370,9 +380,9 @@ agmm::GemmProblem base_problem(const agmm_plan* p, const agmm::RowMap& rows, int
   g.n = (int32_t)p->n;
   g.k = (int32_t)p->k;
   g.b = B;
-  g.ldb = p->rt ? p->k : p->n;
+  g.ldb = ldb_of(p);
   g.c = C;
-  g.ldc = p->n;
+  g.ldc = ldc_of(p);
   g.order.num_rb = (int32_t)cdiv(m_launch, p->bm);
   g.order.num_cb = (int32_t)cdiv(p->n, p->bn);
   g.order.group_m = std::max(1, p->group_m);
@@ -432,6 +442,7 @@ int gather_chunk(agmm_plan* p, const void* const* shards, int64_t row0, int64_t 
   g.src_row0 = row0;
   g.rows = rows;
   g.row_bytes = p->k * (int64_t)elem_bytes(p->dtype);
+  g.src_ld_bytes = lda_of(p) * (int64_t)elem_bytes(p->dtype);
   g.dst = dst;
   g.dst_group_rows = dst_group_rows;
   hipError_t err = agmm::launch_gather(g, max_wgs, s);
@@ -605,6 +616,13 @@ int agmm_plan_set_int(agmm_plan_t p, const char* key, int64_t v) {
   } else if (k == "gemm_streams") {
     if (v < 1 || v > 2) return bad();
     p->gemm_streams = (int)v;
+  } else if (k == "lda" || k == "ldb" || k == "ldc") {
+    // 0 restores the dense default; otherwise at least the row length, and
+    // A / B rows 16-byte aligned for the vector and direct-to-LDS loads
+    const int64_t e = elem_bytes(p->dtype);
+    const int64_t row = k == "lda" ? p->k : k == "ldc" ? p->n : (p->rt ? p->k : p->n);
+    if (v != 0 && (v < row || v >= kDimLimit || (k != "ldc" && (v * e) % 16 != 0))) return bad();
+    (k == "lda" ? p->lda : k == "ldb" ? p->ldb : p->ldc) = v;
   } else if (k == "copy_wgs") {
     if (v < 0 || v > 1 << 20) return bad();
     p->copy_wgs = (int)v;
@@ -635,6 +653,9 @@ int agmm_plan_get_int(agmm_plan_t p, const char* key, int64_t* value) {
   else if (k == "group_m") v = p->group_m;
   else if (k == "xcd_remap") v = p->xcd_remap;
   else if (k == "copy_wgs") v = p->copy_wgs;
+  else if (k == "lda") v = lda_of(p);
+  else if (k == "ldb") v = ldb_of(p);
+  else if (k == "ldc") v = ldc_of(p);
   else if (k == "gemm_streams") v = p->gemm_streams;
   else if (k == "debug_keep_slots") v = p->debug_keep_slots;
   else if (k == "num_chunks") v = p->num_chunks;

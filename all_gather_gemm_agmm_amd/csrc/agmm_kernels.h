@@ -91,14 +91,16 @@ hipError_t launch_gemm_mfma(const GemmProblem& p, int tile_cfg, int dtype, bool 
 hipError_t launch_gemm_f32(const GemmProblem& p, bool rhs_transpose, hipStream_t stream);
 
 // Bit copy of rows into a dense destination:
-//   dst[(g * dst_group_rows + t) * row_bytes ...] = src_group[g][(src_row0 + t) * row_bytes ...]
-// for g < num_groups, t < rows.  row_bytes % 16 == 0, all pointers 16-byte aligned.
+//   dst[(g * dst_group_rows + t) * row_bytes ...] = src_group[g][(src_row0 + t) * src_ld_bytes ...]
+// for g < num_groups, t < rows.  row_bytes % 16 == 0 and src_ld_bytes % 16 == 0
+// (src_ld_bytes == 0: row_bytes), all pointers 16-byte aligned.
 struct GatherProblem {
   const void* src_group[kMaxGroups];
   int32_t num_groups;
   int64_t src_row0;
   int64_t rows;
   int64_t row_bytes;
+  int64_t src_ld_bytes;    // bytes between source rows (0: row_bytes)
   void* dst;
   int64_t dst_group_rows;
 };

@@ -28,6 +28,7 @@ constexpr int kCopyUnroll = 4;
 
 __global__ __launch_bounds__(kCopyThreads) void gather_kernel(GatherProblem p) {
   const int64_t chunks_per_row = p.row_bytes >> 4;
+  const int64_t src_ld = p.src_ld_bytes ? p.src_ld_bytes : p.row_bytes;
   const int64_t chunks_per_group = chunks_per_row * p.rows;
   const int64_t total = chunks_per_group * p.num_groups;
   const int64_t stride = (int64_t)gridDim.x * kCopyThreads;
@@ -46,7 +47,7 @@ __global__ __launch_bounds__(kCopyThreads) void gather_kernel(GatherProblem p) {
         const int64_t t = rem / chunks_per_row;
         const int64_t c = rem - t * chunks_per_row;
         const char* src = static_cast<const char*>(p.src_group[g]) +
-                          (p.src_row0 + t) * p.row_bytes + (c << 4);
+                          (p.src_row0 + t) * src_ld + (c << 4);
         v[q] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(src));
         dst_off[q] = (g * p.dst_group_rows + t) * p.row_bytes + (c << 4);
       }

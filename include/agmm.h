@@ -114,11 +114,16 @@ agmm_plan_t agmm_plan_create(int num_shards, int64_t m_per_shard, int64_t k, int
 
 /*
  * Enqueue C = concat(A_r) @ B (or @ B^T) on `stream`.
- *   shard_ptrs  host array of num_shards device pointers, shard r = [m_per_shard, k];
- *               read during the call only (may be freed on return)
- *   B           device, [k, n_local] or [n_local, k] (rhs_transpose)
- *   C           device, [m, n_local]; must not overlap any input
+ *   shard_ptrs  host array of num_shards device pointers, shard r = [m_per_shard, k]
+ *               with rows "lda" elements apart; read during the call only (may be
+ *               freed on return)
+ *   B           device, [k, n_local] or [n_local, k] (rhs_transpose), rows "ldb"
+ *               elements apart
+ *   C           device, [m, n_local], rows "ldc" elements apart; must not overlap
+ *               any input
  *   stream      hipStream_t as void*
+ * Row strides are the plan's "lda", "ldb", "ldc" settings (default: dense,
+ * i.e. k, n_local or k, n_local); every buffer must hold its last row in full.
  * All device pointers must be 16-byte aligned.
  * Not safe to call concurrently on one plan from two host threads or on two
  * streams at once (the ring and split-K scratch are shared); serial calls on
@@ -194,6 +199,12 @@ int agmm_run_gather_out(agmm_plan_t plan, const void *const *shard_ptrs, const v
  *   "copy_wgs"      >= 0: workgroups of the staged gather copy (0 = auto:
  *                   the first chunk's copy, which has no GEMM to overlap,
  *                   uses the whole GPU; later ones one workgroup per CU)
+ *   "lda", "ldb", "ldc"  0 (dense, the default) or the element stride between
+ *                   rows of the shards, of B as stored and of C: at least the
+ *                   row length; lda and ldb also a multiple of 16 bytes.  The
+ *                   gathered buffers of agmm_gather / agmm_run_gathered /
+ *                   agmm_run_gather_out stay dense [m, k].  get returns the
+ *                   stride in use.
  *   "gemm_streams"  1 or 2 (default 2): staged chunk GEMMs alternate over
  *                   this many streams, so one chunk's workgroups fill the
  *                   CUs the previous chunk's leave (1 with split-K)

@@ -303,6 +303,60 @@ def test_staged_slot_reuse_alternating_streams(dtype, rt):
     check_against_oracle(w, shards, B, out["staged"])
 
 
+def strided(t, ld):
+    """A copy of the 2-D tensor t as a row-strided view (rows ld elements apart)."""
+    big = torch.full((t.shape[0], ld), float("nan"), dtype=t.dtype, device=t.device)
+    big[:, :t.shape[1]] = t
+    return big[:, :t.shape[1]]
+
+
+@pytest.mark.parametrize("variant,dtype,rt,lds", [
+    ("fused", BF16, False, (264, 208, 216)), ("fused", FP16, True, (320, 264, 200)),
+    ("staged", BF16, True, (256, 312, 136)), ("unfused", FP16, False, (248, 144, 200)),
+    ("skinny", BF16, True, (248, 248, 129)), ("fused", FP32, False, (252, 132, 131))])
+def test_strided_inputs(variant, dtype, rt, lds):
+    """Row strides for the shards (lda), B (ldb) and C (ldc) on every path;
+    padding columns hold NaN, so reading them would show in C, and C's own
+    padding must stay untouched."""
+    lda, ldb, ldc = lds
+    m_s = 40 if variant == "skinny" else 200
+    w, shards, B = make_case(3, m_s, 240, 128, dtype, rt, seed=510 + lda)
+    plan = agmm.Plan(3, m_s, 240, 128, dtype, rt, variant=variant,
+                     **({"pvalue": 1, "tile": 14} if variant == "staged" else {}))
+    try:
+        plan.set("lda", lda)
+        plan.set("ldb", ldb)
+        plan.set("ldc", ldc)
+        assert (plan.get("lda"), plan.get("ldb"), plan.get("ldc")) == (lda, ldb, ldc)
+        sd = [strided(to_device(x, dtype), lda) for x in shards]
+        bd = strided(to_device(B, dtype), ldb)
+        c_full = torch.full((w.m, ldc), float("nan"), dtype=sd[0].dtype, device="cuda")
+        C = plan.run(sd, bd, c_full[:, :w.n_local])
+        C2, G = plan.run_gather_out(sd, bd)
+        torch.cuda.synchronize()
+    finally:
+        plan.close()
+    assert C2.stride() == (ldc, 1)
+    assert bool(torch.isnan(c_full[:, w.n_local:].float()).all())   # C's padding untouched
+    assert np.array_equal(to_bits(G), np.concatenate(shards, axis=0))
+    assert np.array_equal(to_bits(C), to_bits(C2))
+    check_against_oracle(w, shards, B, C)
+
+
+def test_stride_keys_validated():
+    plan = agmm.Plan(2, 16, 64, 40, BF16, True)
+    try:
+        for key, bad in (("lda", 63), ("lda", 68), ("ldb", 60), ("ldb", 66), ("ldc", 39)):
+            with pytest.raises(agmm.AgmmError):
+                plan.set(key, bad)
+        plan.set("lda", 72)
+        plan.set("ldc", 41)
+        plan.set("lda", 0)
+        assert plan.get("lda") == 64 and plan.get("ldc") == 41 and plan.get("ldb") == 64
+    finally:
+        plan.close()
+
+
 def test_repeated_runs_fresh_inputs():
     """Back-to-back runs with new inputs (staged ring reuse, split-K counters
     reset): every run matches its own oracle."""
