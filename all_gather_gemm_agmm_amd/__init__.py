@@ -34,6 +34,8 @@ EXPORTS = [
     ("agmm_gather", _ci, [_vp, ctypes.POINTER(_vp), _vp, _vp]),
     ("agmm_run_gathered", _ci, [_vp, _vp, _vp, _vp, _vp]),
     ("agmm_run_gather_out", _ci, [_vp, ctypes.POINTER(_vp), _vp, _vp, _vp, _vp]),
+    ("agmm_plan_autotune", _ci, [_vp, ctypes.POINTER(_vp), _vp, _vp, _vp, _ci,
+                                 ctypes.POINTER(ctypes.c_double)]),
     ("agmm_plan_set_int", _ci, [_vp, _cc, _i64]),
     ("agmm_plan_get_int", _ci, [_vp, _cc, ctypes.POINTER(_i64)]),
     ("agmm_plan_workspace_bytes", ctypes.c_size_t, [_vp]),
@@ -103,6 +105,14 @@ def agmm_plan_create(num_shards, m_per_shard, k, n_local, dtype, rhs_transpose) 
 
 def agmm_run(plan, shard_ptrs: Sequence[int], B: int, C: int, stream: int) -> int:
     return _check(load_library().agmm_run(plan, _ptr_table(shard_ptrs), B, C, stream))
+
+
+def agmm_plan_autotune(plan, shard_ptrs: Sequence[int], B: int, C: int, stream: int,
+                       iters: int = 3) -> float:
+    best = ctypes.c_double(0.0)
+    _check(load_library().agmm_plan_autotune(plan, _ptr_table(shard_ptrs), B, C, stream, iters,
+                                             ctypes.byref(best)))
+    return best.value
 
 
 def agmm_gather(plan, shard_ptrs: Sequence[int], gathered: int, stream: int) -> int:
@@ -272,6 +282,20 @@ class Plan:
         agmm_run_gather_out(self.handle, [s.data_ptr() for s in shards], B.data_ptr(), C.data_ptr(),
                             gathered.data_ptr(), _stream_handle(stream))
         return C, gathered
+
+    def autotune(self, shards, B, C=None, iters=3, stream=None) -> float:
+        """Time candidate settings on these buffers, keep the fastest; returns
+        its mean ms per run (C is overwritten with the product)."""
+        if len(shards) != self.num_shards:
+            raise ValueError(f"expected {self.num_shards} shards, got {len(shards)}")
+        for r, s in enumerate(shards):
+            self._check_tensor(s, (self.m_per_shard, self.k), f"shards[{r}]", "lda")
+        self._check_tensor(B, self.b_shape(), "B", "ldb")
+        if C is None:
+            C = self._new_c(B.device)
+        self._check_tensor(C, (self.m, self.n_local), "C", "ldc")
+        return agmm_plan_autotune(self.handle, [s.data_ptr() for s in shards], B.data_ptr(),
+                                  C.data_ptr(), _stream_handle(stream), iters)
 
     def gather(self, shards, out=None, stream=None):
         import torch

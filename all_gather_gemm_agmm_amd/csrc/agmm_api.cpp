@@ -18,6 +18,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <array>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -693,11 +694,13 @@ int agmm_plan_tile_order(agmm_plan_t p, int chunk, int32_t* out, int capacity) {
   return len;
 }
 
-int agmm_run(agmm_plan_t p, const void* const* shard_ptrs, const void* B, void* C, void* stream) {
-  int rc = check_ptrs(p, shard_ptrs, B, C);
-  if (rc != AGMM_OK) return rc;
-  std::lock_guard<std::mutex> lk(p->mu);
-  hipStream_t s = static_cast<hipStream_t>(stream);
+}  // extern "C"
+
+namespace {
+
+// agmm_run's work, with the plan already locked.
+int run_plan(agmm_plan* p, const void* const* shard_ptrs, const void* B, void* C, hipStream_t s) {
+  int rc;
   switch (p->variant_used) {
     case AGMM_VARIANT_FUSED:
     case AGMM_VARIANT_SKINNY: {
@@ -726,6 +729,98 @@ int agmm_run(agmm_plan_t p, const void* const* shard_ptrs, const void* B, void* 
     default:
       return set_err(AGMM_ERR_INVALID_ARG, "plan has no valid variant");
   }
+}
+
+}  // namespace
+
+extern "C" {
+
+int agmm_run(agmm_plan_t p, const void* const* shard_ptrs, const void* B, void* C, void* stream) {
+  int rc = check_ptrs(p, shard_ptrs, B, C);
+  if (rc != AGMM_OK) return rc;
+  std::lock_guard<std::mutex> lk(p->mu);
+  return run_plan(p, shard_ptrs, B, C, static_cast<hipStream_t>(stream));
+}
+
+int agmm_plan_autotune(agmm_plan_t p, const void* const* shard_ptrs, const void* B, void* C,
+                       void* stream, int iters, double* best_ms) {
+  int rc = check_ptrs(p, shard_ptrs, B, C);
+  if (rc != AGMM_OK) return rc;
+  if (iters < 1 || iters > 1000) return set_err(AGMM_ERR_INVALID_ARG, "iters must be in [1, 1000]");
+  std::lock_guard<std::mutex> lk(p->mu);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  hipError_t err = hipEventCreate(&e0);
+  if (err == hipSuccess) err = hipEventCreate(&e1);
+  if (err != hipSuccess) {
+    if (e0) hipEventDestroy(e0);
+    return hip_err(err, "hipEventCreate");
+  }
+  // time the current configuration: warm-up run, then `iters` runs
+  auto time_current = [&](double& ms) -> int {
+    int r = run_plan(p, shard_ptrs, B, C, s);
+    if (r != AGMM_OK) return r;
+    if (hipEventRecord(e0, s) != hipSuccess) return hip_err(hipGetLastError(), "hipEventRecord");
+    for (int i = 0; i < iters && r == AGMM_OK; ++i) r = run_plan(p, shard_ptrs, B, C, s);
+    if (r != AGMM_OK) return r;
+    if (hipEventRecord(e1, s) != hipSuccess || hipEventSynchronize(e1) != hipSuccess)
+      return hip_err(hipGetLastError(), "hipEventSynchronize");
+    float f = 0.f;
+    hipEventElapsedTime(&f, e0, e1);
+    ms = (double)f / iters;
+    return AGMM_OK;
+  };
+  const int tile0 = p->tile, splits0 = p->splits, group0 = p->group_m;
+  double best = 1e300;
+  int best_tile = tile0, best_splits = splits0, best_group = group0;
+  if (is_f32(p)) {
+    rc = time_current(best);
+  } else {
+    // candidate settings of the plan's variant; configurations that resolve
+    // to the same (tile, splits, group) are timed once
+    std::vector<int> tiles = {agmm::kTile256x256r5, agmm::kTile256x256, agmm::kTile256x256s5,
+                              agmm::kTile256x128, agmm::kTile128x128r5, agmm::kTile128x128};
+    if (p->rt) {
+      tiles.push_back(agmm::kTile128x64r5);
+      tiles.push_back(agmm::kTile128x64);
+      tiles.push_back(agmm::kTile128x64s8);
+    }
+    const int splits_c[] = {0, 1, 2, 4, 8};
+    const int groups_c[] = {4, 8};
+    std::vector<std::array<int, 3>> seen;
+    for (int t : tiles)
+      for (int sp : splits_c)
+        for (int gm : groups_c) {
+          p->tile = t;
+          p->splits = sp;
+          p->group_m = gm;
+          if (configure(p) != AGMM_OK) continue;
+          const std::array<int, 3> key = {p->tile_used, p->splits_used, p->group_m};
+          if (std::find(seen.begin(), seen.end(), key) != seen.end()) continue;
+          seen.push_back(key);
+          double ms = 0;
+          if (time_current(ms) != AGMM_OK) {
+            (void)hipGetLastError();
+            continue;
+          }
+          if (ms < best) {
+            best = ms;
+            best_tile = t;
+            best_splits = sp;
+            best_group = gm;
+          }
+        }
+    p->tile = best_tile;
+    p->splits = best_splits;
+    p->group_m = best_group;
+    rc = configure(p);
+    if (rc == AGMM_OK && best >= 1e300) rc = set_err(AGMM_ERR_HIP, "no candidate configuration ran");
+  }
+  hipEventDestroy(e0);
+  hipEventDestroy(e1);
+  if (rc != AGMM_OK) return rc;
+  if (best_ms) *best_ms = best;
+  return ok();
 }
 
 int agmm_gather(agmm_plan_t p, const void* const* shard_ptrs, void* gathered, void* stream) {

@@ -173,6 +173,24 @@ int agmm_run_gather_out(agmm_plan_t plan, const void *const *shard_ptrs, const v
                         void *gathered, void *stream);
 
 /*
+ * Measure and keep the fastest settings for this plan's problem.  The
+ * tpu-inference kernel picks its block sizes from a tuned table that the page
+ * refers to but does not give; here the plan times its own candidates on the
+ * caller's buffers instead: the compiled bf16/fp16 tile shapes that fit the B
+ * layout, automatic / 1 / 2 / 4 / 8 k-splits and 4 / 8 row blocks walked
+ * together, each configuration that resolves differently timed once (one
+ * warm-up run, then `iters` runs, 1 <= iters <= 1000, with HIP events on
+ * `stream`).  The plan keeps the fastest ("tile", "splits", "group_m" then read
+ * back the choice) and *best_ms (may be NULL) receives its mean time per run.
+ * fp32 plans are only timed.  Same buffers and rules as agmm_run; C is
+ * overwritten with the product; synchronous (returns after the last run);
+ * may reallocate the plan's workspace.  Returns AGMM_OK or the first error of
+ * agmm_run's kinds (AGMM_ERR_HIP when no candidate ran).
+ */
+int agmm_plan_autotune(agmm_plan_t plan, const void *const *shard_ptrs, const void *B, void *C,
+                       void *stream, int iters, double *best_ms);
+
+/*
  * Tune a plan.  Keys (value ranges):
  *   "variant"       agmm_variant
  *   "pvalue"        >= 1: tile-rows of each shard per staged chunk

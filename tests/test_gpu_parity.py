@@ -357,6 +357,29 @@ def test_stride_keys_validated():
         plan.close()
 
 
+@pytest.mark.parametrize("variant,dtype,rt", [("fused", BF16, False), ("skinny", FP16, True),
+                                              ("staged", BF16, True), ("fused", FP32, True)])
+def test_autotune_keeps_a_correct_configuration(variant, dtype, rt):
+    """agmm_plan_autotune times its candidates, keeps one, and the plan then
+    computes the oracle's values (the tuned C too)."""
+    m_s = 24 if variant == "skinny" else 200
+    w, shards, B = make_case(3, m_s, 320, 136, dtype, rt, seed=530 + dtype)
+    sd = [to_device(x, dtype) for x in shards]
+    bd = to_device(B, dtype)
+    plan = agmm.Plan(3, m_s, 320, 136, dtype, rt, variant=variant)
+    try:
+        C_tuned = torch.empty((w.m, w.n_local), dtype=sd[0].dtype, device="cuda")
+        best = plan.autotune(sd, bd, C_tuned, iters=2)
+        assert best > 0
+        assert plan.get("variant_used") == agmm.VARIANTS[variant]
+        C = plan.run(sd, bd)
+        torch.cuda.synchronize()
+    finally:
+        plan.close()
+    check_against_oracle(w, shards, B, C)
+    check_against_oracle(w, shards, B, C_tuned)
+
+
 def test_repeated_runs_fresh_inputs():
     """Back-to-back runs with new inputs (staged ring reuse, split-K counters
     reset): every run matches its own oracle."""
