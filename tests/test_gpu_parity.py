@@ -380,6 +380,48 @@ def test_autotune_keeps_a_correct_configuration(variant, dtype, rt):
     check_against_oracle(w, shards, B, C_tuned)
 
 
+def _random_cases(count, seed):
+    """Seeded random problems across the plan's settings (shapes kept small
+    enough for the oracle)."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < count:
+        dtype = int(rng.choice([BF16, FP16, FP32]))
+        rt = bool(rng.integers(2))
+        N = int(rng.integers(1, 10))
+        m_s = int(rng.choice([1, 2, 7, 16, 33, 64, 100, 129, 256, 300]))
+        k = 8 * int(rng.integers(1, 70))
+        n = int(rng.integers(1, 300))
+        if dtype != FP32 and not rt:
+            n = 8 * max(1, n // 8)
+        variant = str(rng.choice(["auto", "fused", "staged", "unfused", "skinny"]))
+        if variant == "skinny" and (N * m_s > 256 or dtype == FP32):
+            variant = "fused"
+        settings = {"variant": variant}
+        if dtype != FP32 and rng.random() < 0.6:
+            tiles = [0, 1, 2, 3, 4, 5, 6, 7, 9, 10, 12, 13, 14] + ([8, 11, 15] if rt else [])
+            settings["tile"] = int(rng.choice(tiles))
+            if variant in ("fused", "unfused", "skinny", "staged") and rng.random() < 0.5:
+                settings["splits"] = int(rng.integers(1, 6))
+        if variant == "staged":
+            settings["pvalue"] = int(rng.integers(1, 3))
+            settings["nbuf"] = int(rng.integers(1, 4))
+        if N * m_s * k * n > 6e7:
+            continue
+        cases.append((N, m_s, k, n, dtype, rt, settings))
+    return cases
+
+
+@pytest.mark.parametrize("case", _random_cases(48, 2024), ids=lambda c: f"{c[0]}x{c[1]}x{c[2]}x{c[3]}-d{c[4]}-t{int(c[5])}-{c[6]}")
+def test_random_problems(case):
+    """Randomized cross-check of every variant, tile and split setting against
+    the oracle on small ragged problems (fixed seed, so failures reproduce)."""
+    N, m_s, k, n, dtype, rt, settings = case
+    w, shards, B = make_case(N, m_s, k, n, dtype, rt, seed=sum(case[:4]) + dtype)
+    C, _ = run_variant(w, [to_device(x, dtype) for x in shards], to_device(B, dtype), **settings)
+    check_against_oracle(w, shards, B, C)
+
+
 def test_repeated_runs_fresh_inputs():
     """Back-to-back runs with new inputs (staged ring reuse, split-K counters
     reset): every run matches its own oracle."""
@@ -398,6 +440,47 @@ def test_repeated_runs_fresh_inputs():
         finally:
             if plan is not None:
                 plan.close()
+
+
+@pytest.mark.parametrize("variant,settings", [
+    ("fused", {}), ("skinny", {}), ("unfused", {}), ("fused", {"splits": 3}),
+    ("staged", {"pvalue": 1, "tile": 1, "nbuf": 2}),
+    ("staged", {"pvalue": 1, "tile": 14, "nbuf": 2, "splits": 2})])
+def test_graph_capture_replays(variant, settings):
+    """agmm_run captured into a HIP graph (launches, and for the staged plan
+    the copy stream and second GEMM stream joined through events) and
+    replayed on new inputs written into the captured buffers: every replay
+    matches the oracle and is bit-identical to an eager run."""
+    m_s = 24 if variant == "skinny" else 160
+    N, k, n, dtype, rt = 4, 384, 264, BF16, True
+    w, shards, B = make_case(N, m_s, k, n, dtype, rt, seed=900)
+    plan = agmm.Plan(N, m_s, k, n, dtype, rt, variant=variant, **settings)
+    try:
+        sd = [to_device(s, dtype) for s in shards]
+        bd = to_device(B, dtype)
+        C = torch.empty((N * m_s, n), dtype=torch.bfloat16, device="cuda")
+        plan.run(sd, bd, C)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            plan.run(sd, bd, C)
+        torch.cuda.synchronize()
+        for rep in range(3):
+            w2, sh2, B2 = make_case(N, m_s, k, n, dtype, rt, seed=901 + rep)
+            for d, h in zip(sd, sh2):
+                d.copy_(to_device(h, dtype))
+            bd.copy_(to_device(B2, dtype))
+            C.fill_(float("nan"))
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            check_against_oracle(w2, sh2, B2, C)
+            C_eager = plan.run(sd, bd)
+            torch.cuda.synchronize()
+            assert np.array_equal(to_bits(C), to_bits(C_eager))
+        del g
+    finally:
+        plan.close()
 
 
 def test_run_gathered_matches_fused():
