@@ -168,11 +168,11 @@ int64_t ldc_of(const agmm_plan* p) { return p->ldc ? p->ldc : p->n; }
 int choose_tile(const agmm_plan* p, int64_t m) {
   if (p->tile >= 0) return p->tile;
   struct Cand { int cfg; double eff; };
-  // The 256x256 and 128x128 tiles run as the 64-deep part ring unless k is
-  // short (its k-tiles would then be mostly padding).
+  // The 256x256 and 128x128 tiles run as the 64-deep part ring on 16x16x32
+  // MFMAs unless k is short (its k-tiles would then be mostly padding).
   const bool deep = p->k >= 256;
-  const int big = deep ? agmm::kTile256x256r5 : agmm::kTile256x256;
-  const int small = deep ? agmm::kTile128x128r5 : agmm::kTile128x128;
+  const int big = deep ? agmm::kTile256x256m16 : agmm::kTile256x256;
+  const int small = deep ? agmm::kTile128x128m16 : agmm::kTile128x128;
   const Cand cands[] = {{big, 1.0}, {agmm::kTile256x128, 0.9}, {small, 0.8}};
   int best = big;
   double best_cost = 1e300;
@@ -778,8 +778,9 @@ int agmm_plan_autotune(agmm_plan_t p, const void* const* shard_ptrs, const void*
   } else {
     // candidate settings of the plan's variant; configurations that resolve
     // to the same (tile, splits, group) are timed once
-    std::vector<int> tiles = {agmm::kTile256x256r5, agmm::kTile256x256, agmm::kTile256x256s5,
-                              agmm::kTile256x128, agmm::kTile128x128r5, agmm::kTile128x128};
+    std::vector<int> tiles = {agmm::kTile256x256m16, agmm::kTile256x256r5, agmm::kTile256x256,
+                              agmm::kTile256x128,    agmm::kTile128x128m16, agmm::kTile128x128r5,
+                              agmm::kTile128x128};
     if (p->rt) {
       tiles.push_back(agmm::kTile128x64r5);
       tiles.push_back(agmm::kTile128x64);

@@ -73,7 +73,9 @@ enum TileCfg : int {
   kTile256x256r5 = 13,   // 64-deep k-tiles in a ring of 5 operand slots (whole L2 lines per load)
   kTile128x128r5 = 14,   // same ring, 128x128, two workgroups per CU
   kTile128x64r5 = 15,    // same ring, 128x64; B stored n x k only
-  kTileCount = 16,
+  kTile256x256m16 = 16,  // part ring, 256x256, on 16x16x32 MFMAs
+  kTile128x128m16 = 17,  // part ring, 128x128, on 16x16x32 MFMAs
+  kTileCount = 18,
 };
 int tile_bm(int cfg);
 int tile_bn(int cfg);

@@ -777,6 +777,496 @@ void gemm_mfma_kernel(GemmProblem p) {
   }
 }
 
+// acc += B-fragment x A-fragment on one 16x16 block, accumulator tied to its
+// AGPRs.  Written as inline assembly because the compiler gives the builtin
+// for this shape a separate destination and copies every accumulator once
+// per use (four register moves per MFMA); with the operand tied read-write
+// the 64 accumulators of a 128x128 sub-tile stay in place.  Being opaque to
+// the hazard recognizer, the caller keeps the rules the compiler would:
+// fragment registers come straight from LDS reads (waitcnt covers those),
+// and the accumulators are touched by no other instruction between the
+// mfma16_drain() calls around the main loop.
+template <int DT>
+__device__ __forceinline__ void mfma16(f32x4_t& c, const u32x4_t& b, const u32x4_t& a) {
+  if constexpr (DT == kDtypeBf16)
+    asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(b), "v"(a));
+  else
+    asm("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(c) : "v"(b), "v"(a));
+}
+
+template <int DT>
+__device__ __forceinline__ f32x4_t mfma16_builtin(u32x4_t b, u32x4_t a, f32x4_t c) {
+  if constexpr (DT == kDtypeBf16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, b),
+                                                   __builtin_bit_cast(bf16x8_t, a), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, b),
+                                                  __builtin_bit_cast(f16x8_t, a), c, 0, 0, 0);
+}
+
+// Wait states between MFMAs and any other instruction that reads or writes
+// their accumulators (more than the longest MFMA-to-VALU dependency).  The
+// empty statements tie every accumulator on both sides, so no read or write
+// of one can be placed across the wait.
+template <int FM, int FN>
+__device__ __forceinline__ void mfma16_drain(f32x4_t (&acc)[FM][FN]) {
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) asm volatile("" : "+a"(acc[i][j]));
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) asm volatile("" : "+a"(acc[i][j]));
+}
+
+// Part-ring GEMM on v_mfma_f32_16x16x32_{bf16,f16}: the tiles, LDS layouts,
+// part ring, synchronisation, load paths and epilogue of the part-ring form
+// of gemm_mfma_kernel, with each wave's sub-tile computed as 16x16 blocks and
+// a 64-deep k-tile as two k32 steps.  With random bf16 operands the chip is
+// power-limited, and this instruction holds a higher clock than the 32x32x16
+// one for the same work (measured raw MFMA throughput on MI355X: 1.88 against
+// 1.65 PFLOP/s, 1.97 against 1.64 GHz).
+// Fragments (lane l, g = l / 16, i = l % 16), B is the first operand:
+//   A (second operand): A[m = i][k = 8g .. 8g+7] of a 16-row block
+//   B (first operand):  B[k = 8g .. 8g+7][n = i] of a 16-column block
+//   result:             C[m = i][n = 4g .. 4g+3] of the 16x16 block
+template <int BM, int BN, int BK, int DT, bool BT, bool SPLIT, int WAVES, int OCC>
+__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
+void gemm_m16_kernel(GemmProblem p) {
+  using T = GemmTile<BM, BN, BK, DT, BT, 5, WAVES, kLoopParts>;
+  constexpr int kBK = BK;
+  constexpr int FM = T::TM / 16, FN = T::TN / 16;   // 16x16 blocks per wave
+  constexpr int STEPS = BK / 32;                    // k32 steps per k-tile
+  static_assert(BK == 64, "two k32 steps per k-tile");
+  __shared__ __attribute__((aligned(1024))) char smem[T::LDS_BYTES];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / T::WN, wn = wave % T::WN;
+  const int M = p.m, N = p.n, K = p.k;
+  const int ntiles = p.order.num_rb * p.order.num_cb;
+  int wg = blockIdx.x;
+  int split = 0;
+  if constexpr (SPLIT) {
+    split = wg / ntiles;
+    wg -= split * ntiles;
+  }
+  int rb, cb;
+  tile_coords(p.order, wg, ntiles, rb, cb);
+  const int m0 = rb * BM, n0 = cb * BN;
+  int k_begin = 0, k_end = K;
+  if constexpr (SPLIT) {
+    k_begin = split * p.k_per_split;
+    k_end = min(K, k_begin + p.k_per_split);
+  }
+  const int nk = (k_end - k_begin + kBK - 1) / kBK;
+  const char* zero = reinterpret_cast<const char*>(g_zero_chunk);
+
+  // ---- per-lane global sources (same LDS layout as gemm_mfma_kernel) -------
+  const char* a_src[T::A_IPW];
+  int a_kc[T::A_IPW];
+  uint32_t a_ok = 0;
+#pragma unroll
+  for (int j = 0; j < T::A_IPW; ++j) {
+    const int r = (wave * T::A_IPW + j) * T::RPI + lane / T::CPR;
+    const int c = (lane % T::CPR) ^ swz_k<BK>(r);
+    a_kc[j] = c * 8;
+    const int gi = m0 + r;
+    a_src[j] = zero;
+    if (gi < M) {
+      const int g = gi / p.rows.rows_per_group;
+      const int t = gi - g * p.rows.rows_per_group;
+      a_src[j] = static_cast<const char*>(p.rows.a_group[g]) + ((int64_t)t * p.rows.a_ld + c * 8) * 2;
+      a_ok |= 1u << j;
+    }
+  }
+  const char* b_src[T::B_IPW];
+  int b_kc[T::B_IPW];
+  uint32_t b_ok = 0;
+#pragma unroll
+  for (int j = 0; j < T::B_IPW; ++j) {
+    b_src[j] = zero;
+    if constexpr (BT) {
+      const int r = (wave * T::B_IPW + j) * T::RPI + lane / T::CPR;
+      const int c = (lane % T::CPR) ^ swz_k<BK>(r);
+      b_kc[j] = c * 8;
+      const int gn = n0 + r;
+      if (gn < N) {
+        b_src[j] = static_cast<const char*>(p.b) + ((int64_t)gn * p.ldb + c * 8) * 2;
+        b_ok |= 1u << j;
+      }
+    } else {
+      const int byte = (wave * T::B_IPW + j) * 1024 + lane * 16;
+      const int kr = byte / T::B_ROW;
+      const int pos = (byte % T::B_ROW) >> 4;
+      const int c = pos ^ swz_n(kr);
+      b_kc[j] = kr;
+      const int gn = n0 + c * 8;
+      if (gn < N) {
+        b_src[j] = static_cast<const char*>(p.b) + ((int64_t)kr * p.ldb + gn) * 2;
+        b_ok |= 1u << j;
+      }
+    }
+  }
+
+  // ---- LDS fragment offsets --------------------------------------------------
+  const int g4 = lane >> 4, i16 = lane & 15;
+  int a_off[FM], a_x[FM];
+#pragma unroll
+  for (int f = 0; f < FM; ++f) {
+    const int r = wm * T::TM + f * 16 + i16;
+    a_off[f] = r * T::KROW;
+    a_x[f] = g4 ^ swz_k<BK>(r);          // chunk (4*step + g4) sits at (4*step) ^ a_x
+  }
+  int b_off[FN], b_x[FN];
+  if constexpr (BT) {
+#pragma unroll
+    for (int f = 0; f < FN; ++f) {
+      const int r = wn * T::TN + f * 16 + i16;
+      b_off[f] = r * T::KROW;
+      b_x[f] = g4 ^ swz_k<BK>(r);
+    }
+  }
+  // k x n B: lane i of 16-lane group G reads k-row 32*step + 8G + 4*half + i/4,
+  // columns nb + 4*(i%4) .. +3; ds_read_b64_tr_b16 then hands lane 16G + j
+  // element e of B[32*step + 8G + 4*half + e][nb + j]
+  const int tr_krow = 8 * g4 + (i16 >> 2);
+  const int tr_swz = swz_n(tr_krow);
+  int tr_n[FN];
+#pragma unroll
+  for (int f = 0; f < FN; ++f) tr_n[f] = wn * T::TN + f * 16 + 4 * (i16 & 3);
+
+  f32x4_t acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[i][j][e] = 0.0f;
+
+  // A fragments of k32 step `st`, and B fragments of column blocks
+  // 4h .. 4h+3 (one half of the wave's columns) of step `st`
+  auto read_a = [&](const char* sa, int st, u32x4_t* af) {
+#pragma unroll
+    for (int f = 0; f < FM; ++f)
+      af[f] = *reinterpret_cast<const u32x4_t*>(sa + a_off[f] + (((4 * st) ^ a_x[f]) << 4));
+  };
+  constexpr int FH = FN / 2;   // column blocks per half
+  static_assert(FN % 2 == 0, "two halves of column blocks");
+  auto read_b = [&](const char* sb, int st, int h, u32x4_t* bfr) {
+#pragma unroll
+    for (int q = 0; q < FH; ++q) {
+      const int f = h * FH + q;
+      if constexpr (BT) {
+        bfr[q] = *reinterpret_cast<const u32x4_t*>(sb + b_off[f] + (((4 * st) ^ b_x[f]) << 4));
+      } else {
+        const int n = tr_n[f];
+        const int pos = (n >> 3) ^ tr_swz;
+        const char* p0 = sb + (32 * st + tr_krow) * T::B_ROW + (pos << 4) + (n & 7) * 2;
+        const u32x2_t lo = read_tr(p0);
+        const u32x2_t hi2 = read_tr(p0 + 4 * T::B_ROW);
+        bfr[q] = u32x4_t{lo[0], lo[1], hi2[0], hi2[1]};
+      }
+    }
+  };
+  auto read_a_one = [&](const char* sa, int st, int f) -> u32x4_t {
+    return *reinterpret_cast<const u32x4_t*>(sa + a_off[f] + (((4 * st) ^ a_x[f]) << 4));
+  };
+  auto read_b_one = [&](const char* sb, int st, int f) -> u32x4_t {
+    if constexpr (BT) {
+      return *reinterpret_cast<const u32x4_t*>(sb + b_off[f] + (((4 * st) ^ b_x[f]) << 4));
+    } else {
+      const int n = tr_n[f];
+      const int pos = (n >> 3) ^ tr_swz;
+      const char* p0 = sb + (32 * st + tr_krow) * T::B_ROW + (pos << 4) + (n & 7) * 2;
+      const u32x2_t lo = read_tr(p0);
+      const u32x2_t hi2 = read_tr(p0 + 4 * T::B_ROW);
+      return u32x4_t{lo[0], lo[1], hi2[0], hi2[1]};
+    }
+  };
+  // Interior tiles of the one-workgroup-per-CU shape, whose accumulators fill
+  // the AGPRs, use the tied form; edge tiles (more live registers for their
+  // masks) and the smaller shape the builtin, whose hazards the compiler
+  // tracks itself.
+  constexpr bool kTied = OCC == 1;
+  auto mfma_half = [&](auto tied, const u32x4_t* af, const u32x4_t* bfr, int h) {
+#pragma unroll
+    for (int q = 0; q < FH; ++q)
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        if constexpr (kTied && decltype(tied)::value) mfma16<DT>(acc[i][h * FH + q], bfr[q], af[i]);
+        else acc[i][h * FH + q] = mfma16_builtin<DT>(bfr[q], af[i], acc[i][h * FH + q]);
+      }
+  };
+  constexpr int kMfmaPerHalf = FM * FH;
+
+  // ---- main loop: the part ring (see gemm_mfma_kernel) -----------------------
+  constexpr int L = T::A_IPW;
+  constexpr int LB = T::B_IPW;
+  constexpr int PB = T::PART_BYTES;
+  constexpr int SPREAD = STEPS - 1;
+  const bool interior = (m0 + BM <= M) && (n0 + BN <= N) && ((k_end - k_begin) % kBK == 0) && nk > 0;
+  auto ring = [&](auto tag) {
+    constexpr bool FAST = decltype(tag)::value;
+    auto a_addr = [&](int j, int t) -> const char* {
+      if constexpr (FAST) {
+        const int kk = k_begin + (t < nk ? t : nk - 1) * kBK;
+        return a_src[j] + (int64_t)kk * 2;
+      } else {
+        const int kk = k_begin + t * kBK;
+        const bool ok = ((a_ok >> j) & 1) && (kk + a_kc[j] < k_end);
+        return ok ? a_src[j] + (int64_t)kk * 2 : zero;
+      }
+    };
+    auto b_addr = [&](int j, int t) -> const char* {
+      if constexpr (FAST) {
+        const int kk = k_begin + (t < nk ? t : nk - 1) * kBK;
+        return b_src[j] + (BT ? (int64_t)kk * 2 : (int64_t)kk * p.ldb * 2);
+      } else {
+        const int kk = k_begin + t * kBK;
+        const bool ok = ((b_ok >> j) & 1) && (kk + b_kc[j] < k_end);
+        return ok ? b_src[j] + (BT ? (int64_t)kk * 2 : (int64_t)kk * p.ldb * 2) : zero;
+      }
+    };
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_char_t*)smem;
+    const uint32_t lds_a = lds0 + wave * (T::A_IPW * 1024);
+    const uint32_t lds_b = lds0 + wave * (T::B_IPW * 1024);
+    auto put_a = [&](int slot, int t, int j0, int j1) {
+#pragma unroll
+      for (int j = j0; j < j1; ++j) load_lds16_at(a_addr(j, t), lds_a + slot * PB + j * 1024);
+    };
+    auto put_b = [&](int slot, int t) {
+#pragma unroll
+      for (int j = 0; j < T::B_IPW; ++j) load_lds16_at(b_addr(j, t), lds_b + slot * PB + j * 1024);
+    };
+    auto put_b_one = [&](int slot, int t, int j) { load_lds16_at(b_addr(j, t), lds_b + slot * PB + j * 1024); };
+    // Four half-steps per k-tile, (step, half) = (0,0) (0,1) (1,0) (1,1):
+    //   (0,0) MFMAs A0 x Ba; reads Bb = B(step 0, half 1)
+    //   (0,1) MFMAs A0 x Bb; reads A1 = A(step 1), Ba = B(step 1, half 0)
+    //   (1,0) MFMAs A1 x Ba; reads Bb = B(step 1, half 1)
+    //   (1,1) sync; MFMAs A1 x Bb; reads A0, Ba of the next k-tile
+    // Every read of this k-tile's slots is issued before the sync, which also
+    // waits for them (lgkmcnt), so the loads after it may overwrite them.
+    // A part loads ride on half-steps 0-2, the B part on half-step 3.
+    u32x4_t A0[FM], A1[FM], Ba[FH], Bb[FH];
+    if constexpr (kTied && FAST) mfma16_drain(acc);
+    put_a(0, 0, 0, L);
+    put_b(1, 0);
+    put_a(2, 1, 0, L);
+    put_b(3, 1);
+    wait_vmcnt<L + LB>();
+    block_barrier();
+    read_b(smem + PB, 0, 0, Ba);
+    read_a(smem, 0, A0);
+    int sa_slot = 0, sb_slot = 1;
+    auto interleave = [&](int nread, int nload) {
+      // MFMA / LDS read pairs first (the next half-step waits on the reads),
+      // then the global->LDS loads spread over the remaining MFMAs
+      const int nr = nread < kMfmaPerHalf ? nread : kMfmaPerHalf;
+      const int left = kMfmaPerHalf - nr;
+#pragma unroll
+      for (int q = 0; q < nr; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+#pragma unroll
+      for (int q = 0; q < left; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+#pragma unroll
+        for (int r = q * nload / left; r < (q + 1) * nload / left; ++r)
+          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      }
+    };
+    constexpr int kReadsB = BT ? FH : 2 * FH;   // LDS read instructions per B half
+    if constexpr (kTied && FAST) {
+      // The compiler cannot see the tied MFMAs as MFMAs, so the interleaving
+      // is written out and pinned: after MFMA number x of a half-step comes
+      // its share of the other work (an LDS fragment read per MFMA first,
+      // the next half-step needs them; then the global->LDS loads spread
+      // over the remaining MFMAs), each group fenced from the next.
+      auto half = [&](const u32x4_t* af, const u32x4_t* bfr, int h, int nread, int nload, auto&& op) {
+#pragma unroll
+        for (int q = 0; q < FH; ++q)
+#pragma unroll
+          for (int i = 0; i < FM; ++i) {
+            const int x = q * FM + i;
+            mfma16<DT>(acc[i][h * FH + q], bfr[q], af[i]);
+            if (x < nread) {
+              op(x);
+            } else {
+              const int left = kMfmaPerHalf - nread, y = x - nread;
+#pragma unroll
+              for (int r = y * nload / left; r < (y + 1) * nload / left; ++r) op(nread + r);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+          }
+      };
+      constexpr int L0 = L / 3, L1 = (2 * L) / 3 - L / 3, L2 = L - (2 * L) / 3;
+      static_assert(FM + FH <= kMfmaPerHalf, "one read per MFMA");
+      for (int it = 0; it < nk; ++it) {
+        const char* sa = smem + sa_slot * PB;
+        const char* sb = smem + sb_slot * PB;
+        const int a_new = sb_slot + 3 >= 5 ? sb_slot - 2 : sb_slot + 3;   // slot of B of it-1
+        const int na = sa_slot + 2 >= 5 ? sa_slot - 3 : sa_slot + 2;
+        const int nb = sb_slot + 2 >= 5 ? sb_slot - 3 : sb_slot + 2;
+        // (0,0): MFMAs A0 x Ba; reads Bb (step 0, half 1); A loads 0 .. L0-1
+        half(A0, Ba, 0, FH, L0, [&](int k) {
+          if (k < FH) Bb[k] = read_b_one(sb, 0, FH + k);
+          else put_a(a_new, it + 2, k - FH, k - FH + 1);
+        });
+        // (0,1): MFMAs A0 x Bb; reads A1 (step 1), Ba (step 1, half 0); A loads L0 ..
+        half(A0, Bb, 1, FM + FH, L1, [&](int k) {
+          if (k < FM) A1[k] = read_a_one(sa, 1, k);
+          else if (k < FM + FH) Ba[k - FM] = read_b_one(sb, 1, k - FM);
+          else put_a(a_new, it + 2, L0 + k - FM - FH, L0 + k - FM - FH + 1);
+        });
+        // (1,0): MFMAs A1 x Ba; reads Bb (step 1, half 1); the last A loads
+        half(A1, Ba, 0, FH, L2, [&](int k) {
+          if (k < FH) Bb[k] = read_b_one(sb, 1, FH + k);
+          else put_a(a_new, it + 2, L0 + L1 + k - FH, L0 + L1 + k - FH + 1);
+        });
+        // (1,1): sync; MFMAs A1 x Bb; reads Ba, A0 of the next k-tile; B loads
+        wait_vmcnt<L>();
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        block_barrier();
+        const char* sa2 = smem + na * PB;
+        const char* sb2 = smem + nb * PB;
+        half(A1, Bb, 1, FH + FM, LB, [&](int k) {
+          if (k < FH) Ba[k] = read_b_one(sb2, 0, k);
+          else if (k < FH + FM) A0[k - FH] = read_a_one(sa2, 0, k - FH);
+          else put_b_one(sa_slot, it + 2, k - FH - FM);
+        });
+        sa_slot = na;
+        sb_slot = nb;
+      }
+    } else
+    for (int it = 0; it < nk; ++it) {
+      const char* sa = smem + sa_slot * PB;
+      const char* sb = smem + sb_slot * PB;
+      const int a_new = sb_slot + 3 >= 5 ? sb_slot - 2 : sb_slot + 3;   // slot of B of it-1
+      const int na = sa_slot + 2 >= 5 ? sa_slot - 3 : sa_slot + 2;
+      const int nb = sb_slot + 2 >= 5 ? sb_slot - 3 : sb_slot + 2;
+      constexpr int L0 = L / 3, L1 = (2 * L) / 3 - L / 3, L2 = L - (2 * L) / 3;
+      // (0,0)
+      read_b(sb, 0, 1, Bb);
+      put_a(a_new, it + 2, 0, L0);
+      mfma_half(tag, A0, Ba, 0);
+      interleave(kReadsB, L0);
+      // (0,1)
+      read_a(sa, 1, A1);
+      read_b(sb, 1, 0, Ba);
+      put_a(a_new, it + 2, L0, L0 + L1);
+      mfma_half(tag, A0, Bb, 1);
+      interleave(FM + kReadsB, L1);
+      // (1,0)
+      read_b(sb, 1, 1, Bb);
+      put_a(a_new, it + 2, L0 + L1, L);
+      mfma_half(tag, A1, Ba, 0);
+      interleave(kReadsB, L2);
+      // (1,1)
+      wait_vmcnt<L>();
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      block_barrier();
+      read_b(smem + nb * PB, 0, 0, Ba);
+      read_a(smem + na * PB, 0, A0);
+      put_b(sa_slot, it + 2);
+      mfma_half(tag, A1, Bb, 1);
+      interleave(kReadsB + FM, LB);
+      sa_slot = na;
+      sb_slot = nb;
+    }
+    if constexpr (kTied && FAST) mfma16_drain(acc);
+  };
+  if (interior) ring(BoolTag<true>{});
+  else ring(BoolTag<false>{});
+  wait_vmcnt<0>();
+
+  // ---- epilogue: acc[i][j][e] = C[m0 + wm*TM + 16i + i16][n0 + wn*TN + 16j + 4g4 + e]
+  const int hi = g4 & 1;   // which half of a 16-byte (8-column) chunk
+  constexpr int kRowB = BN * 2;
+  constexpr int kChunks = kRowB / 16;
+  static_assert(T::LDS_BYTES >= BM * kRowB, "LDS too small to stage the C tile");
+  bool staged = false;
+  if constexpr (!SPLIT) {
+    staged = (m0 + BM <= M) && (n0 + BN <= N) && (p.ldc % 8) == 0 &&
+             ((reinterpret_cast<uintptr_t>(p.c) & 15) == 0);
+  }
+  if (staged) {
+    block_barrier();
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int r = wm * T::TM + i * 16 + i16;
+      char* row = smem + r * kRowB;
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int c = wn * T::TN + j * 16 + 4 * g4;
+        const int pos = (c >> 3) ^ (r & (kChunks - 1));
+        u32x2_t v;
+        v[0] = pack2<DT>(acc[i][j][0], acc[i][j][1]);
+        v[1] = pack2<DT>(acc[i][j][2], acc[i][j][3]);
+        *reinterpret_cast<u32x2_t*>(row + pos * 16 + hi * 8) = v;
+      }
+    }
+    block_barrier();
+    constexpr int kRowsPerPass = T::THREADS / kChunks;
+    const int ch = tid % kChunks;
+    int r = tid / kChunks;
+    int gi = m0 + r;
+    int g = gi / p.rows.rows_per_group;
+    int t = gi - g * p.rows.rows_per_group;
+    uint16_t* cbase = static_cast<uint16_t*>(p.c) + n0 + ch * 8;
+#pragma unroll 4
+    for (; r < BM; r += kRowsPerPass) {
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(smem + r * kRowB + ((ch ^ (r & (kChunks - 1))) << 4));
+      const int64_t crow = (int64_t)g * p.rows.c_group_rows + p.rows.c_row_off + t;
+      __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(cbase + crow * p.ldc));
+      t += kRowsPerPass;
+      while (t >= p.rows.rows_per_group) {
+        t -= p.rows.rows_per_group;
+        ++g;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int gi = m0 + wm * T::TM + i * 16 + i16;
+      if (gi >= M) continue;
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int gn = n0 + wn * T::TN + j * 16 + 4 * g4;
+        const f32x4_t& a = acc[i][j];
+        if constexpr (SPLIT) {
+          float* prow = p.partials + ((int64_t)split * M + gi) * N;
+          if ((N % 4) == 0 && gn + 3 < N) {
+            *reinterpret_cast<f32x4_t*>(prow + gn) = a;
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (gn + e < N) prow[gn + e] = a[e];
+          }
+        } else {
+          const int g = gi / p.rows.rows_per_group;
+          const int t = gi - g * p.rows.rows_per_group;
+          uint16_t* cp = static_cast<uint16_t*>(p.c) + ((int64_t)g * p.rows.c_group_rows + p.rows.c_row_off + t) * p.ldc;
+          if ((N % 4) == 0 && (p.ldc % 4) == 0 && gn + 3 < N) {
+            u32x2_t v;
+            v[0] = pack2<DT>(a[0], a[1]);
+            v[1] = pack2<DT>(a[2], a[3]);
+            *reinterpret_cast<u32x2_t*>(cp + gn) = v;
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (gn + e < N) cp[gn + e] = cvt1<DT>(a[e]);
+          }
+        }
+      }
+    }
+  }
+}
+
 // Sum of the split-K partials in split order 0, 1, ..., S-1 (fixed, so the
 // result does not depend on which workgroup finished first), cast to the
 // output dtype, scattered to C rows through the row map.  Four consecutive
@@ -852,6 +1342,33 @@ hipError_t launch_tile(const GemmProblem& p, int dtype, bool bt, hipStream_t s) 
             : launch_one<BM, BN, BK, kDtypeFp16, false, NST, WAVES, OCC, LOOP>(p, s);
 }
 
+template <int BM, int BN, int BK, int DT, bool BT, int WAVES, int OCC>
+hipError_t launch_m16_one(const GemmProblem& p, hipStream_t stream) {
+  const int ntiles = p.order.num_rb * p.order.num_cb;
+  if (p.splits > 1) {
+    hipLaunchKernelGGL((gemm_m16_kernel<BM, BN, BK, DT, BT, true, WAVES, OCC>),
+                       dim3(ntiles * p.splits), dim3(64 * WAVES), 0, stream, p);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    const int64_t work = (int64_t)p.m * ((p.n + 3) / 4);
+    hipLaunchKernelGGL((splitk_reduce_kernel<DT>), dim3((unsigned)((work + 255) / 256)), dim3(256),
+                       0, stream, p);
+  } else {
+    hipLaunchKernelGGL((gemm_m16_kernel<BM, BN, BK, DT, BT, false, WAVES, OCC>),
+                       dim3(ntiles), dim3(64 * WAVES), 0, stream, p);
+  }
+  return hipGetLastError();
+}
+
+template <int BM, int BN, int BK, int WAVES, int OCC>
+hipError_t launch_m16(const GemmProblem& p, int dtype, bool bt, hipStream_t s) {
+  if (dtype == kDtypeBf16)
+    return bt ? launch_m16_one<BM, BN, BK, kDtypeBf16, true, WAVES, OCC>(p, s)
+              : launch_m16_one<BM, BN, BK, kDtypeBf16, false, WAVES, OCC>(p, s);
+  return bt ? launch_m16_one<BM, BN, BK, kDtypeFp16, true, WAVES, OCC>(p, s)
+            : launch_m16_one<BM, BN, BK, kDtypeFp16, false, WAVES, OCC>(p, s);
+}
+
 }  // namespace
 
 // Compiled tile configurations: output tile, k-depth of an LDS stage,
@@ -874,6 +1391,8 @@ constexpr TileInfo kTiles[kTileCount] = {
     {256, 256, 64, 5, 4, 1},   // kTile256x256r5:    160 KiB part ring, 64-deep k-tiles
     {128, 128, 64, 5, 4, 2},   // kTile128x128r5:    80 KiB part ring, two workgroups per CU
     {128, 64, 64, 5, 4, 2},    // kTile128x64r5:     80 KiB part ring; B stored n x k only
+    {256, 256, 64, 5, 4, 1},   // kTile256x256m16:   part ring on 16x16x32 MFMAs
+    {128, 128, 64, 5, 4, 2},   // kTile128x128m16:   same, two workgroups per CU
 };
 
 int tile_bm(int cfg) { return kTiles[cfg].bm; }
@@ -913,6 +1432,8 @@ hipError_t launch_gemm_mfma(const GemmProblem& p, int tile_cfg, int dtype, bool 
       if (!rhs_transpose) return hipErrorInvalidValue;
       return dtype == kDtypeBf16 ? launch_one<128, 64, 64, kDtypeBf16, true, 5, 4, 2, kLoopParts>(p, stream)
                                  : launch_one<128, 64, 64, kDtypeFp16, true, 5, 4, 2, kLoopParts>(p, stream);
+    case kTile256x256m16: return launch_m16<256, 256, 64, 4, 1>(p, dtype, rhs_transpose, stream);
+    case kTile128x128m16: return launch_m16<128, 128, 64, 4, 2>(p, dtype, rhs_transpose, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -95,7 +95,8 @@ def _csv_rows(d, suffix):
 
 
 def _short(name: str) -> str:
-    for key in ("gemm_mfma_kernel", "splitk_reduce_kernel", "gather_kernel", "gemm_f32_kernel"):
+    for key in ("gemm_m16_kernel", "gemm_mfma_kernel", "splitk_reduce_kernel", "gather_kernel",
+                "gemm_f32_kernel"):
         if key in name:
             return key
     return name[:48]
@@ -152,7 +153,7 @@ def summarize_traffic(args, w, variant):
     # the gather copy reads and writes exactly m*k*elem bytes
     f_scale = copy_bytes / (fetch["gather_kernel"] * 1024.0)
     w_scale = copy_bytes / (write["gather_kernel"] * 1024.0)
-    main = "gemm_mfma_kernel" if "gemm_mfma_kernel" in fetch else "gemm_f32_kernel"
+    main = next(k for k in ("gemm_m16_kernel", "gemm_mfma_kernel", "gemm_f32_kernel") if k in fetch)
     fb = fetch[main] * 1024.0 * f_scale
     wb = write[main] * 1024.0 * w_scale
     extra = {}

@@ -203,8 +203,10 @@ int agmm_plan_autotune(agmm_plan_t plan, const void *const *shard_ptrs, const vo
  *                   9 256x256 (8 waves, ping-pong), 10 128x128 (8 stages),
  *                   11 128x64 (8 stages, rhs_transpose only), 12 256x256
  *                   (5 stages), 13 256x256 (64-deep k-tiles in a 5-slot
- *                   operand ring; the automatic choice for k >= 256), 14 128x128 and
- *                   15 128x64 (rhs_transpose only) in the same ring
+ *                   operand ring), 14 128x128 and 15 128x64
+ *                   (rhs_transpose only) in the same ring, 16 256x256 and
+ *                   17 128x128 in the same ring on 16x16x32 MFMAs (the
+ *                   automatic choices for k >= 256)
  *   "splits"        0: automatic, else k-splits (fp32 partial sums, then a
  *                   fixed-order reduction) of every bf16/fp16 launch (for the
  *                   staged variant: of each chunk's launch); automatic splits

@@ -81,7 +81,7 @@ def test_small_ragged(case, variant):
     check_against_oracle(w, shards, B, C)
 
 
-@pytest.mark.parametrize("tile", list(range(16)))
+@pytest.mark.parametrize("tile", list(range(18)))
 @pytest.mark.parametrize("dtype,rt", [(BF16, False), (BF16, True), (FP16, False), (FP16, True)])
 @pytest.mark.parametrize("k", [328, 384])
 def test_tiles_ragged(tile, dtype, rt, k):
@@ -260,6 +260,19 @@ def test_split_k_ragged(tile, splits):
     check_against_oracle(w, shards, B, C)
 
 
+@pytest.mark.parametrize("tile", [16, 17])
+@pytest.mark.parametrize("dtype,rt", [(BF16, False), (BF16, True), (FP16, False), (FP16, True)])
+@pytest.mark.parametrize("splits,k", [(1, 1024), (3, 1024), (1, 1000)])
+def test_mfma16_tiles(tile, dtype, rt, splits, k):
+    """The 16x16x32-MFMA tiles on whole interior tiles (m, n multiples of the
+    tile, whole k-tiles in every k range: the unmasked loop with its pinned
+    interleave), with split-K, and with a ragged k (masked loop)."""
+    w, shards, B = make_case(2, 512, k, 512, dtype, rt, seed=1600 + tile + splits + k)
+    C, _ = run_variant(w, [to_device(s, dtype) for s in shards], to_device(B, dtype), "fused",
+                       tile=tile, splits=splits)
+    check_against_oracle(w, shards, B, C)
+
+
 @pytest.mark.parametrize("variant,tile,splits,rt,pvalue", [
     ("fused", 13, 3, False, None), ("fused", 1, 0, False, None), ("unfused", 5, 2, True, None),
     ("fused", 0, 2, True, None), ("fused", 13, 0, True, None),
@@ -399,7 +412,7 @@ def _random_cases(count, seed):
             variant = "fused"
         settings = {"variant": variant}
         if dtype != FP32 and rng.random() < 0.6:
-            tiles = [0, 1, 2, 3, 4, 5, 6, 7, 9, 10, 12, 13, 14] + ([8, 11, 15] if rt else [])
+            tiles = [0, 1, 2, 3, 4, 5, 6, 7, 9, 10, 12, 13, 14, 16, 17] + ([8, 11, 15] if rt else [])
             settings["tile"] = int(rng.choice(tiles))
             if variant in ("fused", "unfused", "skinny", "staged") and rng.random() < 0.5:
                 settings["splits"] = int(rng.integers(1, 6))
