@@ -75,6 +75,28 @@ __device__ __forceinline__ int swz_n(int krow) {
   return (r << 2) ^ ((r >> 1) << 1);
 }
 
+// Swizzles of the 16x16x32-MFMA kernel.  Its fragment reads differ from the
+// 32x32x16 ones: a ds_read_b128 covers 16 rows x 4 chunks (lane 16g + i
+// reads row i, chunk g) instead of 32 rows x 2 chunks, and a transposed B
+// read covers k-rows 8g + 0..3 for g = 0..3.  Rocprof counters showed the
+// 32x32 swizzles costing this kernel LDS bank-conflict stalls on ~16% of
+// its cycles (against 0.3% in the 32x32 kernel).  Both patterns agree with
+// the LDS serving a b128 read in passes of lanes 8p..8p+7 with
+// 32+8p..32+8p+7, and a b64 read in passes of 32 lanes.  Under that
+// grouping:
+//  * k-contiguous rows of 128 bytes: chunk c of row r at c ^ swz_k16(r).
+//    A pass reads 8 consecutive rows x chunks {g, g ^ 2}; the 4 rows of one
+//    parity (one 128-byte bank half) get swizzles 0, 1, 4, 5 (first 8 rows
+//    of 16) or 2, 3, 6, 7 (last 8), so the 8 chunks they need are distinct.
+//    Any 16 consecutive rows use 8 distinct swizzles per parity as well.
+//  * n-contiguous B k-rows: the 32x32 swizzle of k-row r (by r % 4), plus
+//    a flip of chunk bit 1 for k-rows with bit 3 set, which puts k-rows r
+//    and r + 8 (read in the same pass) on disjoint bank sets.
+__device__ __forceinline__ int swz_k16(int row) {
+  return ((row >> 1) & 1) | (row & 4) | ((row >> 2) & 2);
+}
+__device__ __forceinline__ int swz_n16(int krow) { return swz_n(krow) ^ ((krow >> 2) & 2); }
+
 template <int DT>
 __device__ __forceinline__ f32x16_t mfma32(u32x4_t a, u32x4_t b, f32x16_t c) {
   if constexpr (DT == kDtypeBf16) {
@@ -872,7 +894,7 @@ void gemm_m16_kernel(GemmProblem p) {
 #pragma unroll
   for (int j = 0; j < T::A_IPW; ++j) {
     const int r = (wave * T::A_IPW + j) * T::RPI + lane / T::CPR;
-    const int c = (lane % T::CPR) ^ swz_k<BK>(r);
+    const int c = (lane % T::CPR) ^ swz_k16(r);
     a_kc[j] = c * 8;
     const int gi = m0 + r;
     a_src[j] = zero;
@@ -891,7 +913,7 @@ void gemm_m16_kernel(GemmProblem p) {
     b_src[j] = zero;
     if constexpr (BT) {
       const int r = (wave * T::B_IPW + j) * T::RPI + lane / T::CPR;
-      const int c = (lane % T::CPR) ^ swz_k<BK>(r);
+      const int c = (lane % T::CPR) ^ swz_k16(r);
       b_kc[j] = c * 8;
       const int gn = n0 + r;
       if (gn < N) {
@@ -902,7 +924,7 @@ void gemm_m16_kernel(GemmProblem p) {
       const int byte = (wave * T::B_IPW + j) * 1024 + lane * 16;
       const int kr = byte / T::B_ROW;
       const int pos = (byte % T::B_ROW) >> 4;
-      const int c = pos ^ swz_n(kr);
+      const int c = pos ^ swz_n16(kr);
       b_kc[j] = kr;
       const int gn = n0 + c * 8;
       if (gn < N) {
@@ -919,7 +941,7 @@ void gemm_m16_kernel(GemmProblem p) {
   for (int f = 0; f < FM; ++f) {
     const int r = wm * T::TM + f * 16 + i16;
     a_off[f] = r * T::KROW;
-    a_x[f] = g4 ^ swz_k<BK>(r);          // chunk (4*step + g4) sits at (4*step) ^ a_x
+    a_x[f] = g4 ^ swz_k16(r);          // chunk (4*step + g4) sits at (4*step) ^ a_x
   }
   int b_off[FN], b_x[FN];
   if constexpr (BT) {
@@ -927,14 +949,14 @@ void gemm_m16_kernel(GemmProblem p) {
     for (int f = 0; f < FN; ++f) {
       const int r = wn * T::TN + f * 16 + i16;
       b_off[f] = r * T::KROW;
-      b_x[f] = g4 ^ swz_k<BK>(r);
+      b_x[f] = g4 ^ swz_k16(r);
     }
   }
   // k x n B: lane i of 16-lane group G reads k-row 32*step + 8G + 4*half + i/4,
   // columns nb + 4*(i%4) .. +3; ds_read_b64_tr_b16 then hands lane 16G + j
   // element e of B[32*step + 8G + 4*half + e][nb + j]
   const int tr_krow = 8 * g4 + (i16 >> 2);
-  const int tr_swz = swz_n(tr_krow);
+  const int tr_swz = swz_n16(tr_krow);
   int tr_n[FN];
 #pragma unroll
   for (int f = 0; f < FN; ++f) tr_n[f] = wn * T::TN + f * 16 + 4 * (i16 & 3);
