@@ -119,6 +119,7 @@ struct agmm_plan {
   int group_m = 4;
   int xcd_remap = 1;
   int copy_wgs = 0;
+  int copy_engine = 0;   // copies beside a GEMM: 0 gather kernel (CUs), 1 SDMA engines
   // element strides between rows of the caller's buffers (0: dense)
   int64_t lda = 0, ldb = 0, ldc = 0;
   int gemm_streams = 2;   // staged: chunk GEMMs alternate over this many streams (1 or 2)
@@ -451,6 +452,40 @@ int gather_chunk(agmm_plan* p, const void* const* shards, int64_t row0, int64_t 
   return AGMM_OK;
 }
 
+// The same bit copy on the SDMA engines (hipMemcpyDeviceToDeviceNoCU): no
+// compute unit takes part, so it runs beside a GEMM that fills every CU's
+// register file without slowing it.  Needs dense shard rows (each shard's
+// chunk is then one contiguous range).
+int gather_chunk_sdma(agmm_plan* p, const void* const* shards, int64_t row0, int64_t rows,
+                      void* dst, int64_t dst_group_rows, hipStream_t s) {
+  const size_t row_bytes = (size_t)p->k * elem_bytes(p->dtype);
+  for (int g = 0; g < p->N; ++g) {
+    const char* src = static_cast<const char*>(shards[g]) + (size_t)row0 * row_bytes;
+    char* d = static_cast<char*>(dst) + (size_t)g * dst_group_rows * row_bytes;
+    hipError_t err = hipMemcpyAsync(d, src, (size_t)rows * row_bytes, hipMemcpyDeviceToDeviceNoCU, s);
+    if (err != hipSuccess) return hip_err(err, "hipMemcpyAsync(gather on SDMA)");
+  }
+  return AGMM_OK;
+}
+
+// Whether a copy goes to the SDMA engines: only when the plan asks for them
+// (copy_engine 1), the copy runs beside a GEMM (`overlaps`), the shard rows
+// are dense and the caller's stream is not being captured into a graph (the
+// capture keeps the kernel copy, whose graph form is tested).  Measured on
+// MI355X: alone, an SDMA copy moves ~1.16 TB/s and leaves the CUs free; but
+// in the staged pipeline beside the chunk GEMMs the chunks arrive too late
+// (workload 5: 5.26 ms against 3.47 ms with the kernel copy), so the kernel
+// copy stays the default.
+bool copy_on_sdma(const agmm_plan* p, hipStream_t caller, bool overlaps) {
+  if (p->copy_engine != 1 || !overlaps || lda_of(p) != p->k) return false;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(caller, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) {
+    (void)hipGetLastError();
+    return false;
+  }
+  return true;
+}
+
 // Staged pipeline.  With `gathered` == nullptr the chunks go through the
 // plan's ring of slots; otherwise each chunk is copied to its final place in
 // the caller's [m, k] buffer (no slot is reused, so no copy waits for a GEMM).
@@ -482,10 +517,15 @@ int run_staged(agmm_plan* p, const void* const* shards, const void* B, void* C, 
       if (err != hipSuccess) return hip_err(err, "hipStreamWaitEvent(free)");
     }
     // chunk 0's copy has no GEMM to overlap and gets the whole GPU; later
-    // copies run next to a GEMM and are held to one workgroup per CU (unless
-    // the plan sets copy_wgs)
-    const int wgs = (c == 0 && p->copy_wgs == 0) ? 0 : copy_wgs;
-    int rc = gather_chunk(p, shards, row0, rows_c, dst, dst_group_rows, wgs, p->copy_stream);
+    // copies run next to a GEMM: on the SDMA engines, or as the gather
+    // kernel held to one workgroup per CU (unless the plan sets copy_wgs)
+    int rc;
+    if (copy_on_sdma(p, s, c > 0)) {
+      rc = gather_chunk_sdma(p, shards, row0, rows_c, dst, dst_group_rows, p->copy_stream);
+    } else {
+      const int wgs = (c == 0 && p->copy_wgs == 0) ? 0 : copy_wgs;
+      rc = gather_chunk(p, shards, row0, rows_c, dst, dst_group_rows, wgs, p->copy_stream);
+    }
     if (rc != AGMM_OK) return rc;
     if ((err = hipEventRecord(p->ev_ready[slot], p->copy_stream)) != hipSuccess)
       return hip_err(err, "hipEventRecord(ready)");
@@ -627,6 +667,9 @@ int agmm_plan_set_int(agmm_plan_t p, const char* key, int64_t v) {
   } else if (k == "copy_wgs") {
     if (v < 0 || v > 1 << 20) return bad();
     p->copy_wgs = (int)v;
+  } else if (k == "copy_engine") {
+    if (v < 0 || v > 1) return bad();
+    p->copy_engine = (int)v;
   } else if (k == "debug_keep_slots") {
     if (v != 0 && v != 1) return bad();
     p->debug_keep_slots = (int)v;
@@ -654,6 +697,7 @@ int agmm_plan_get_int(agmm_plan_t p, const char* key, int64_t* value) {
   else if (k == "group_m") v = p->group_m;
   else if (k == "xcd_remap") v = p->xcd_remap;
   else if (k == "copy_wgs") v = p->copy_wgs;
+  else if (k == "copy_engine") v = p->copy_engine;
   else if (k == "lda") v = lda_of(p);
   else if (k == "ldb") v = ldb_of(p);
   else if (k == "ldc") v = ldc_of(p);
@@ -898,7 +942,9 @@ int agmm_run_gather_out(agmm_plan_t p, const void* const* shard_ptrs, const void
       hipError_t err = hipEventRecord(p->ev_entry, s);
       if (err == hipSuccess) err = hipStreamWaitEvent(p->copy_stream, p->ev_entry, 0);
       if (err != hipSuccess) return hip_err(err, "stream fork");
-      rc = gather_chunk(p, shard_ptrs, 0, p->m_s, gathered, p->m_s, copy_wgs, p->copy_stream);
+      rc = copy_on_sdma(p, s, true)
+               ? gather_chunk_sdma(p, shard_ptrs, 0, p->m_s, gathered, p->m_s, p->copy_stream)
+               : gather_chunk(p, shard_ptrs, 0, p->m_s, gathered, p->m_s, copy_wgs, p->copy_stream);
       if (rc != AGMM_OK) return rc;
       if ((err = hipEventRecord(p->ev_side, p->copy_stream)) != hipSuccess)
         return hip_err(err, "hipEventRecord(side)");

@@ -371,21 +371,43 @@ def main():
                   "traffic_GB_s": round(2 * payload / (g_ms * 1e-3) / 1e9, 1),
                   "frac_hbm": round(2 * payload / (g_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
         gplan.close()
+        # C plus the gathered operand from one call (agmm_run_gather_out), the
+        # side copy on the gather kernel or on the SDMA engines
+        if not args.no_compare:
+            for ce in (0, 1):
+                log(f"gather_out copy_engine={ce}")
+                op = agmm.Plan(w.num_shards, w.m_per_shard, w.k, w.n_local, w.dtype,
+                               w.rhs_transpose, variant=variant, copy_engine=ce, **settings)
+                sh0, B0, C0 = sets[0]
+                op.run_gather_out(sh0, B0, C0, G, stream=stream)
+                torch.cuda.synchronize()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                nst = max(5, args.steps // 2)
+                e0.record(stream)
+                for i in range(nst):
+                    sh, Bt, C = sets[i % nsets]
+                    op.run_gather_out(sh, Bt, C, G, stream=stream)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                gather["gather_out_ms_" + ("sdma" if ce else "kernel")] = round(e0.elapsed_time(e1) / nst, 5)
+                op.close()
         del G
 
     # the same problem through the other paths (overlap accounting)
     variants_ms = None
     if not args.no_compare:
         variants_ms = {}
-        for v in ("fused", "staged", "unfused", "skinny"):
+        for v in ("fused", "staged", "staged_sdma", "unfused", "skinny"):
             if v == "skinny" and (w.dtype == 2 or w.m > 1024):
                 continue
-            if v in ("staged", "unfused") and (w.k * w.elem_bytes) % 16:
+            if v in ("staged", "staged_sdma", "unfused") and (w.k * w.elem_bytes) % 16:
                 continue
-            st = {"pvalue": w.pvalue or 2, "nbuf": w.nbuf or 2} if v == "staged" else {}
+            st = {"pvalue": w.pvalue or 2, "nbuf": w.nbuf or 2} if v.startswith("staged") else {}
+            if v == "staged_sdma":
+                st["copy_engine"] = 1   # chunk copies after the first on the SDMA engines
             log(f"variant {v}")
             vp = agmm.Plan(w.num_shards, w.m_per_shard, w.k, w.n_local, w.dtype,
-                           w.rhs_transpose, variant=v, **st)
+                           w.rhs_transpose, variant=v.split("_")[0], **st)
 
             def vrun(i, s, vp=vp):
                 sh, Bt, C = sets[i % nsets]

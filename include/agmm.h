@@ -219,6 +219,13 @@ int agmm_plan_autotune(agmm_plan_t plan, const void *const *shard_ptrs, const vo
  *   "copy_wgs"      >= 0: workgroups of the staged gather copy (0 = auto:
  *                   the first chunk's copy, which has no GEMM to overlap,
  *                   uses the whole GPU; later ones one workgroup per CU)
+ *   "copy_engine"   0 (default) or 1: what performs the copies that run
+ *                   beside a GEMM (staged chunks after the first, the side
+ *                   gather of agmm_run_gather_out).  0: the gather kernel on
+ *                   the CUs.  1: the SDMA engines (hipMemcpyDeviceToDeviceNoCU),
+ *                   used only for dense shard rows (lda == k) and never while
+ *                   the caller's stream is being captured into a graph (the
+ *                   kernel copies then).  Both are bit copies.
  *   "lda", "ldb", "ldc"  0 (dense, the default) or the element stride between
  *                   rows of the shards, of B as stored and of C: at least the
  *                   row length; lda and ldb also a multiple of 16 bytes.  The

@@ -159,14 +159,16 @@ def test_gather_bit_exact(dtype):
     assert np.array_equal(to_bits(G), oracle.gather(shards, dtype))
 
 
-def test_staged_slots_bit_exact():
+@pytest.mark.parametrize("copy_engine", [0, 1])
+def test_staged_slots_bit_exact(copy_engine):
     """debug_keep_slots: every chunk keeps its own slot; each equals the
-    oracle gather's rows of that chunk."""
+    oracle gather's rows of that chunk, whether the gather kernel or the
+    SDMA engines copied it."""
     w, shards, B = make_case(3, 300, 128, 64, BF16, True, seed=78)
     sd = [to_device(s, BF16) for s in shards]
     bd = to_device(B, BF16)
     plan = agmm.Plan(3, 300, 128, 64, BF16, True, variant="staged", pvalue=1, tile=1,
-                     debug_keep_slots=1)
+                     debug_keep_slots=1, copy_engine=copy_engine)
     try:
         C = plan.run(sd, bd)
         torch.cuda.synchronize()
@@ -514,7 +516,9 @@ def test_run_gathered_matches_fused():
 
 @pytest.mark.parametrize("variant,dtype,rt,settings", [
     ("fused", BF16, False, {"tile": 14}), ("staged", FP16, True, {"pvalue": 1, "tile": 14}),
-    ("unfused", BF16, True, {}), ("skinny", BF16, True, {}), ("fused", FP32, False, {})])
+    ("unfused", BF16, True, {}), ("skinny", BF16, True, {}), ("fused", FP32, False, {}),
+    ("fused", BF16, True, {"copy_engine": 1}), ("staged", BF16, False, {"pvalue": 1, "copy_engine": 1}),
+    ("unfused", BF16, False, {"copy_engine": 1})])
 def test_run_gather_out(variant, dtype, rt, settings):
     """C and the gathered operand from one call: the gathered buffer is the
     bit-exact concatenation, C is bit-identical to agmm_run's, and the
@@ -537,6 +541,43 @@ def test_run_gather_out(variant, dtype, rt, settings):
     assert np.array_equal(to_bits(C), to_bits(C_ref))
     check_against_oracle(w, shards, B, C)
     check_against_oracle(w, shards, B2, C2)
+
+
+@pytest.mark.parametrize("copy_engine", [0, 1])
+@pytest.mark.parametrize("nbuf", [1, 2, 3])
+def test_staged_copy_engines(copy_engine, nbuf):
+    """The staged pipeline with its chunk copies on the gather kernel or the
+    SDMA engines, ring slots reused (more chunks than slots), two calls in a
+    row: the oracle's values, and the same bits whichever engine copied."""
+    w, shards, B = make_case(3, 520, 256, 200, BF16, True, seed=480 + nbuf)
+    sd = [to_device(x, BF16) for x in shards]
+    bd = to_device(B, BF16)
+    outs = []
+    for ce in (0, copy_engine):
+        plan = agmm.Plan(3, 520, 256, 200, BF16, True, variant="staged", pvalue=1, tile=14,
+                         nbuf=nbuf, copy_engine=ce)
+        try:
+            assert plan.get("num_chunks") == 5 and plan.get("copy_engine") == ce
+            for _ in range(2):
+                C = plan.run(sd, bd)
+            torch.cuda.synchronize()
+            outs.append(to_bits(C))
+        finally:
+            plan.close()
+    assert np.array_equal(outs[0], outs[1])
+    check_against_oracle(w, shards, B, C)
+
+
+def test_copy_engine_validated():
+    plan = agmm.Plan(2, 64, 64, 64, BF16, True, variant="staged")
+    try:
+        for bad in (-1, 2):
+            with pytest.raises(agmm.AgmmError):
+                plan.set("copy_engine", bad)
+        plan.set("copy_engine", 1)
+        assert plan.get("copy_engine") == 1
+    finally:
+        plan.close()
 
 
 def test_run_rejects_misaligned_pointer():
