@@ -248,9 +248,12 @@ int configure(agmm_plan* p) {
     p->bm = p->bn = 64;
   } else if (v == AGMM_VARIANT_SKINNY) {
     // all of m in one row block; narrow column blocks so that enough
-    // workgroups stream B (the 64-wide tile needs B stored n x k)
+    // workgroups stream B (the 64-wide tiles need B stored n x k).  Of the
+    // 128x64 forms the part ring (64-deep k-tiles, whole L2 lines per load)
+    // measured fastest on the 8 x 16 x 4096 -> 1792 workload (graph replay,
+    // 8 k ranges: 16.4 us against 16.9 for the 32-deep stage ring)
     p->tile_used = p->tile >= 0 ? p->tile
-                   : (p->m <= 128 ? (p->rt ? agmm::kTile128x64 : agmm::kTile128x128)
+                   : (p->m <= 128 ? (p->rt ? agmm::kTile128x64r5 : agmm::kTile128x128)
                                   : agmm::kTile256x128);
     p->bm = agmm::tile_bm(p->tile_used);
     p->bn = agmm::tile_bn(p->tile_used);
