@@ -303,7 +303,7 @@ def main():
     # longer steps keep the eager timing, which those workloads have been
     # measured with (a graph-timed run of the largest workload crashed the
     # process and is not used until that crash is understood).
-    use_graph = not args.eager and eager_ms_per_step < GRAPH_MAX_STEP_MS
+    use_graph = not args.eager and not args.only_run and eager_ms_per_step < GRAPH_MAX_STEP_MS
     log(f"eager {eager_ms_per_step:.4f} ms/step; timing {'graph' if use_graph else 'eager'}")
     ms_per_step = graph_ms(step, args.steps) if use_graph else eager_ms_per_step
     log("timed steps done")
