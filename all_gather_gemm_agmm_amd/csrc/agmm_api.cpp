@@ -506,7 +506,6 @@ int run_staged(agmm_plan* p, const void* const* shards, const void* B, void* C, 
   if (alt && (err = hipStreamWaitEvent(p->compute2, p->ev_entry, 0)) != hipSuccess)
     return hip_err(err, "hipStreamWaitEvent");
   const int64_t e = elem_bytes(p->dtype);
-  const int copy_wgs = p->copy_wgs > 0 ? p->copy_wgs : p->cu_count;
   for (int c = 0; c < p->num_chunks; ++c) {
     const int slot = c % p->nslots;
     const int64_t row0 = (int64_t)c * p->rows_per_chunk;
@@ -519,15 +518,17 @@ int run_staged(agmm_plan* p, const void* const* shards, const void* B, void* C, 
       err = hipStreamWaitEvent(p->copy_stream, p->ev_free[slot], 0);
       if (err != hipSuccess) return hip_err(err, "hipStreamWaitEvent(free)");
     }
-    // chunk 0's copy has no GEMM to overlap and gets the whole GPU; later
-    // copies run next to a GEMM: on the SDMA engines, or as the gather
-    // kernel held to one workgroup per CU (unless the plan sets copy_wgs)
+    // Every chunk's copy is sized to the whole GPU unless the plan sets
+    // copy_wgs: the GEMM holds all of a CU's registers, so a copy held to
+    // one workgroup per CU mostly waits for CUs the GEMM leaves idle
+    // (measured: 496 -> ~467 us on the 8x1024x8192 -> 3584 workload, 3244
+    // -> ~3180 us on 8x4096x8192 -> 7168, pvalue 2, two slots).  With
+    // copy_engine 1 the copies after the first go to the SDMA engines.
     int rc;
     if (copy_on_sdma(p, s, c > 0)) {
       rc = gather_chunk_sdma(p, shards, row0, rows_c, dst, dst_group_rows, p->copy_stream);
     } else {
-      const int wgs = (c == 0 && p->copy_wgs == 0) ? 0 : copy_wgs;
-      rc = gather_chunk(p, shards, row0, rows_c, dst, dst_group_rows, wgs, p->copy_stream);
+      rc = gather_chunk(p, shards, row0, rows_c, dst, dst_group_rows, p->copy_wgs, p->copy_stream);
     }
     if (rc != AGMM_OK) return rc;
     if ((err = hipEventRecord(p->ev_ready[slot], p->copy_stream)) != hipSuccess)

@@ -216,9 +216,9 @@ int agmm_plan_autotune(agmm_plan_t plan, const void *const *shard_ptrs, const vo
  *   "order"         0: ring order from local_shard, 1: natural order
  *   "group_m"       >= 1: row blocks walked together (L2 reuse)
  *   "xcd_remap"     0/1: keep consecutive tiles on one XCD
- *   "copy_wgs"      >= 0: workgroups of the staged gather copy (0 = auto:
- *                   the first chunk's copy, which has no GEMM to overlap,
- *                   uses the whole GPU; later ones one workgroup per CU)
+ *   "copy_wgs"      >= 0: workgroups of each staged chunk copy (0 = auto:
+ *                   sized to the whole GPU) and of the side gather of
+ *                   agmm_run_gather_out (0 = one per CU)
  *   "copy_engine"   0 (default) or 1: what performs the copies that run
  *                   beside a GEMM (staged chunks after the first, the side
  *                   gather of agmm_run_gather_out).  0: the gather kernel on
