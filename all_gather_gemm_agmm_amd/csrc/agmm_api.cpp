@@ -299,11 +299,19 @@ int configure(agmm_plan* p) {
     int64_t want = p->splits;
     if (want <= 0) {
       want = 1;
-      if (v == AGMM_VARIANT_SKINNY || 2 * tiles <= p->cu_count) {
+      // workgroup slots: the CUs times the workgroups of this tile one CU
+      // holds (the skinny rule keeps one per CU: more k ranges there only
+      // add partial sums, measured slower on the 8x16x4096->1792 workload;
+      // counting both slots of the two-per-CU 128x128 tile measured 37.5 ->
+      // 34.9 us on 4x512x4096->1024)
+      const int64_t slots = v == AGMM_VARIANT_SKINNY
+                                ? p->cu_count
+                                : (int64_t)p->cu_count * agmm::tile_occ(p->tile_used);
+      if (v == AGMM_VARIANT_SKINNY || 2 * tiles <= slots) {
         // long enough k ranges that the partial sums stay small next to the
         // operand traffic (skinny problems have no other way to fill the GPU)
         const int64_t min_k = v == AGMM_VARIANT_SKINNY ? agmm::kTileBK : 1024;
-        while (want * 2 * tiles <= p->cu_count && p->k / (want * 2) >= min_k) want *= 2;
+        while (want * 2 * tiles <= slots && p->k / (want * 2) >= min_k) want *= 2;
       }
     }
     want = std::max<int64_t>(1, std::min<int64_t>(want, cdiv(p->k, agmm::kTileBK)));

@@ -80,6 +80,7 @@ enum TileCfg : int {
 int tile_bm(int cfg);
 int tile_bn(int cfg);
 int tile_bk(int cfg);
+int tile_occ(int cfg);   // workgroups of this tile that fit on one CU
 // k granularity of split-K ranges (a multiple of every configuration's depth)
 constexpr int kTileBK = 64;
 

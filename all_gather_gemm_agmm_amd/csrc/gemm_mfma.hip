@@ -1420,6 +1420,7 @@ constexpr TileInfo kTiles[kTileCount] = {
 int tile_bm(int cfg) { return kTiles[cfg].bm; }
 int tile_bn(int cfg) { return kTiles[cfg].bn; }
 int tile_bk(int cfg) { return kTiles[cfg].bk; }
+int tile_occ(int cfg) { return kTiles[cfg].occ; }
 
 hipError_t launch_gemm_mfma(const GemmProblem& p, int tile_cfg, int dtype, bool rhs_transpose,
                             hipStream_t stream) {
