@@ -214,7 +214,9 @@ int agmm_plan_autotune(agmm_plan_t plan, const void *const *shard_ptrs, const vo
  *                   output tiles fill at most half of the CUs
  *   "local_shard"   0 .. num_shards-1: where the ring order starts
  *   "order"         0: ring order from local_shard, 1: natural order
- *   "group_m"       >= 1: row blocks walked together (L2 reuse)
+ *   "group_m"       row blocks walked together (L2 reuse); 0 (default):
+ *                   chosen per launch shape, the count whose tiles on one XCD
+ *                   touch the fewest A row blocks plus B column blocks
  *   "xcd_remap"     0/1: keep consecutive tiles on one XCD
  *   "copy_wgs"      >= 0: workgroups of each staged chunk copy (0 = auto:
  *                   sized to the whole GPU) and of the side gather of
@@ -244,7 +246,8 @@ int agmm_plan_autotune(agmm_plan_t plan, const void *const *shard_ptrs, const vo
 int agmm_plan_set_int(agmm_plan_t plan, const char *key, int64_t value);
 
 /* Read a plan setting (keys above, plus "num_chunks", "rows_per_chunk",
- * "tile_bm", "tile_bn", "num_row_blocks" and the resolved "variant_used").
+ * "tile_bm", "tile_bn", "num_row_blocks", the resolved "variant_used", and
+ * "group_m_used": the row-block group a launch over the whole problem uses).
  * value: host pointer.  Returns AGMM_OK or AGMM_ERR_INVALID_ARG. */
 int agmm_plan_get_int(agmm_plan_t plan, const char *key, int64_t *value);
 

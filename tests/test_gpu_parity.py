@@ -568,6 +568,22 @@ def test_staged_copy_engines(copy_engine, nbuf):
     check_against_oracle(w, shards, B, C)
 
 
+@pytest.mark.parametrize("shape,want", [((8, 1024, 8192, 3584, FP16, True), 8),
+                                        ((8, 4096, 8192, 7168, BF16, False), 4)])
+def test_group_m_automatic(shape, want):
+    """The automatic row-block group: the count whose tiles on one XCD touch
+    the fewest A row blocks plus B column blocks (8 for 32 x 14 tiles of
+    256 x 256, 4 on ties); an explicit setting wins."""
+    plan = agmm.Plan(*shape, variant="fused")
+    try:
+        assert plan.get("group_m") == 0
+        assert plan.get("group_m_used") == want
+        plan.set("group_m", 2)
+        assert plan.get("group_m_used") == 2
+    finally:
+        plan.close()
+
+
 def test_copy_engine_validated():
     plan = agmm.Plan(2, 64, 64, 64, BF16, True, variant="staged")
     try:
