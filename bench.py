@@ -9,7 +9,9 @@ synthetic inputs already resident in HBM.  Prints ONE JSON line.
 
 value      : 2*m*k*n_local / (wall time per step), TFLOP/s, timed with events
              around exactly K steps replayed from one HIP graph (--eager: K
-             eager calls; the eager time is reported either way).
+             eager calls; the eager time is reported either way).  Before the
+             timed region: W warmup steps, then untimed steps for SETTLE_S of
+             wall time (the clocks' ramp; reported as settle_steps).
 roofline   : the dominant kernel (the MFMA GEMM, with its split-K reduction
              when it has one) timed per launch with HIP events on the stream
              it is launched on, against the MI355X dense bf16/fp16 MFMA peak
@@ -182,6 +184,10 @@ def summarize_traffic(args, w, variant):
 
 
 GRAPH_MAX_STEP_MS = 0.25
+# After the W warmup steps, untimed steps continue until this much wall time
+# has passed: the GPU's clocks take more than ~10 ms of load to settle, and a
+# short timed region would otherwise measure the ramp, not the kernels.
+SETTLE_S = 0.2
 
 
 def log(msg):
@@ -269,8 +275,12 @@ def main():
                 for i in range(count):
                     run_one(i, side)
         torch.cuda.synchronize()
-        g.replay()
-        torch.cuda.synchronize()
+        t_settle = time.time()
+        while True:   # untimed replays until the clocks have settled
+            g.replay()
+            torch.cuda.synchronize()
+            if time.time() - t_settle >= SETTLE_S / 2:
+                break
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         cur = torch.cuda.current_stream()
         e0.record(cur)
@@ -284,7 +294,15 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    log(f"warmup done ({used})")
+    settle_steps = 0
+    t_settle = time.time()
+    while time.time() - t_settle < SETTLE_S:
+        step(settle_steps)
+        settle_steps += 1
+        if settle_steps % 8 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    log(f"warmup done ({used}; {settle_steps} settle steps)")
 
     # exactly K eager steps, nothing else recorded on the stream
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -474,6 +492,7 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "timing": "one HIP-graph replay of the K steps" if use_graph else "eager calls",
+        "settle_steps": settle_steps,
         "eager_ms_per_step": round(eager_ms_per_step, 5),
         "dtype": I.DTYPE_NAMES[w.dtype], "data": "synthetic (seeded, N(0,1/sqrt(k)) or U[-1,1])",
         "config": {**w.describe(), "variant": used, "buffer_sets": nsets},
