@@ -19,6 +19,7 @@
 
 #include <algorithm>
 #include <array>
+#include <chrono>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -877,6 +878,22 @@ int agmm_plan_autotune(agmm_plan_t p, const void* const* shard_ptrs, const void*
     ms = (double)f / iters;
     return AGMM_OK;
   };
+  // let the clocks settle before the first candidate is timed (they take
+  // more than ~10 ms of load to ramp; the first timing would otherwise lose)
+  {
+    const auto t0 = std::chrono::steady_clock::now();
+    do {
+      rc = run_plan(p, shard_ptrs, B, C, s);
+      if (rc == AGMM_OK && hipStreamSynchronize(s) != hipSuccess)
+        rc = hip_err(hipGetLastError(), "hipStreamSynchronize");
+    } while (rc == AGMM_OK &&
+             std::chrono::steady_clock::now() - t0 < std::chrono::milliseconds(100));
+    if (rc != AGMM_OK) {
+      hipEventDestroy(e0);
+      hipEventDestroy(e1);
+      return rc;
+    }
+  }
   const int tile0 = p->tile, splits0 = p->splits, group0 = p->group_m;
   double best = 1e300;
   int best_tile = tile0, best_splits = splits0, best_group = group0;
