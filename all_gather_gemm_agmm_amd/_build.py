@@ -34,6 +34,7 @@ SOURCES = {
     "agmm_api.cpp": [],
     "gather_f32.hip": [],
     "gemm_mfma.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
+    "skinny.hip": [],
 }
 
 

@@ -120,6 +120,7 @@ struct agmm_plan {
   int group_m = 0;  // 0: chosen per launch shape (pick_group_m)
   int xcd_remap = 1;
   int copy_wgs = 0;
+  int skinny_shape = 1;  // tile shape of the whole-k skinny kernel (launch_skinny_fullk): 32 x 32
   int copy_engine = 0;   // copies beside a GEMM: 0 gather kernel (CUs), 1 SDMA engines
   // element strides between rows of the caller's buffers (0: dense)
   int64_t lda = 0, ldb = 0, ldc = 0;
@@ -288,13 +289,14 @@ int configure(agmm_plan* p) {
     p->tile_used = -1;
     p->bm = p->bn = 64;
   } else if (v == AGMM_VARIANT_SKINNY) {
-    // all of m in one row block; narrow column blocks so that enough
-    // workgroups stream B (the 64-wide tiles need B stored n x k).  Of the
-    // 128x64 forms the part ring (64-deep k-tiles, whole L2 lines per load)
-    // measured fastest on the 8 x 16 x 4096 -> 1792 workload (graph replay,
-    // 8 k ranges: 16.4 us against 16.9 for the 32-deep stage ring)
+    // B stored n x k, m <= 128: the whole-k skinny kernel (32 x 32 tiles,
+    // one launch, no partial sums): 11.8 us per call on the 8 x 16 x 4096 ->
+    // 1792 workload in graph replay, against 16.4 for the best split-K tile
+    // (the 128x64 part ring, 8 k ranges) and 13.5 for its 64 x 16 shape.
+    // Otherwise all of m in one row block with split-K over narrow column
+    // blocks, so that enough workgroups stream B.
     p->tile_used = p->tile >= 0 ? p->tile
-                   : (p->m <= 128 ? (p->rt ? agmm::kTile128x64r5 : agmm::kTile128x128)
+                   : (p->m <= 128 ? (p->rt ? agmm::kTileSkinny : agmm::kTile128x128)
                                   : agmm::kTile256x128);
     p->bm = agmm::tile_bm(p->tile_used);
     p->bn = agmm::tile_bn(p->tile_used);
@@ -309,6 +311,9 @@ int configure(agmm_plan* p) {
     p->bm = agmm::tile_bm(p->tile_used);
     p->bn = agmm::tile_bn(p->tile_used);
   }
+
+  if (!is_f32(p) && p->tile_used == agmm::kTileSkinny && !p->rt)
+    return set_err(AGMM_ERR_UNSUPPORTED, "tile %d (skinny, whole k) needs B stored n x k", agmm::kTileSkinny);
 
   // chunking (staged) / split-K (skinny)
   p->rows_per_chunk = p->m_s;
@@ -338,6 +343,7 @@ int configure(agmm_plan* p) {
     const int64_t launch_m = v == AGMM_VARIANT_STAGED ? (int64_t)p->N * p->rows_per_chunk : p->m;
     const int64_t tiles = cdiv(launch_m, p->bm) * cdiv(p->n, p->bn);
     int64_t want = p->splits;
+    if (p->tile_used == agmm::kTileSkinny) want = 1;   // whole k per workgroup, no partials
     if (want <= 0) {
       want = 1;
       // workgroup slots: the CUs times the workgroups of this tile one CU
@@ -473,6 +479,8 @@ int launch_gemm(agmm_plan* p, agmm::GemmProblem& g, hipStream_t s) {
   if (timed) hipEventRecord(p->tev[p->tev_used], s);
   hipError_t err;
   if (is_f32(p)) err = agmm::launch_gemm_f32(g, p->rt != 0, s);
+  else if (p->tile_used == agmm::kTileSkinny)
+    err = agmm::launch_skinny_fullk(g, p->dtype, p->skinny_shape, s);
   else err = agmm::launch_gemm_mfma(g, p->tile_used, p->dtype, p->rt != 0, s);
   if (err != hipSuccess) return hip_err(err, "GEMM launch");
   if (timed) {
@@ -729,6 +737,9 @@ int agmm_plan_set_int(agmm_plan_t p, const char* key, int64_t v) {
   } else if (k == "copy_wgs") {
     if (v < 0 || v > 1 << 20) return bad();
     p->copy_wgs = (int)v;
+  } else if (k == "skinny_shape") {
+    if (v < 0 || v > 4) return bad();
+    p->skinny_shape = (int)v;
   } else if (k == "copy_engine") {
     if (v < 0 || v > 1) return bad();
     p->copy_engine = (int)v;
@@ -762,6 +773,7 @@ int agmm_plan_get_int(agmm_plan_t p, const char* key, int64_t* value) {
   else if (k == "xcd_remap") v = p->xcd_remap;
   else if (k == "copy_wgs") v = p->copy_wgs;
   else if (k == "copy_engine") v = p->copy_engine;
+  else if (k == "skinny_shape") v = p->skinny_shape;
   else if (k == "lda") v = lda_of(p);
   else if (k == "ldb") v = ldb_of(p);
   else if (k == "ldc") v = ldc_of(p);
@@ -906,6 +918,7 @@ int agmm_plan_autotune(agmm_plan_t p, const void* const* shard_ptrs, const void*
                               agmm::kTile256x128,    agmm::kTile128x128m16, agmm::kTile128x128r5,
                               agmm::kTile128x128};
     if (p->rt) {
+      tiles.insert(tiles.begin(), agmm::kTileSkinny);
       tiles.push_back(agmm::kTile128x64r5);
       tiles.push_back(agmm::kTile128x64);
       tiles.push_back(agmm::kTile128x64s8);

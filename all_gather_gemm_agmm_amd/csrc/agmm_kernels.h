@@ -75,7 +75,8 @@ enum TileCfg : int {
   kTile128x64r5 = 15,    // same ring, 128x64; B stored n x k only
   kTile256x256m16 = 16,  // part ring, 256x256, on 16x16x32 MFMAs
   kTile128x128m16 = 17,  // part ring, 128x128, on 16x16x32 MFMAs
-  kTileCount = 18,
+  kTileSkinny = 18,      // 64x16 over the whole k, wave-private LDS rings (launch_skinny_fullk); B n x k only
+  kTileCount = 19,
 };
 int tile_bm(int cfg);
 int tile_bn(int cfg);
@@ -89,6 +90,13 @@ constexpr int kTileBK = 64;
 // k range, then their fixed-order sum and cast.
 hipError_t launch_gemm_mfma(const GemmProblem& p, int tile_cfg, int dtype, bool rhs_transpose,
                             hipStream_t stream);
+
+// Skinny-m kernel (tile kTileSkinny, B stored n x k): 64 x 16 output tiles,
+// each over the whole of k in one workgroup (no split, one launch; p.splits
+// is ignored).  C rows through the row map.
+// `shape` selects the tile: 0: 64 x 16, 1: 32 x 32, 2: 32 x 16, 3: 16 x 32,
+// 4: 64 x 32 (rows x columns).
+hipError_t launch_skinny_fullk(const GemmProblem& p, int dtype, int shape, hipStream_t stream);
 
 // fp32 inputs, fp64 accumulate, fp32 output (any shape).
 hipError_t launch_gemm_f32(const GemmProblem& p, bool rhs_transpose, hipStream_t stream);

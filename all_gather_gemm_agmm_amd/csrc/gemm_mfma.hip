@@ -1415,6 +1415,7 @@ constexpr TileInfo kTiles[kTileCount] = {
     {128, 64, 64, 5, 4, 2},    // kTile128x64r5:     80 KiB part ring; B stored n x k only
     {256, 256, 64, 5, 4, 1},   // kTile256x256m16:   part ring on 16x16x32 MFMAs
     {128, 128, 64, 5, 4, 2},   // kTile128x128m16:   same, two workgroups per CU
+    {64, 16, 64, 4, 4, 1},     // kTileSkinny:       skinny kernel, whole k (launch_skinny_fullk)
 };
 
 int tile_bm(int cfg) { return kTiles[cfg].bm; }

@@ -70,7 +70,7 @@ def parse():
 
 def kernel_source_sha() -> str:
     h = hashlib.sha256()
-    for f in ("gemm_mfma.hip", "gather_f32.hip", "agmm_kernels.h"):
+    for f in ("gemm_mfma.hip", "skinny.hip", "gather_f32.hip", "agmm_kernels.h"):
         with open(os.path.join(ROOT, "all_gather_gemm_agmm_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -104,8 +104,8 @@ def _csv_rows(d, suffix):
 
 
 def _short(name: str) -> str:
-    for key in ("gemm_m16_kernel", "gemm_mfma_kernel", "splitk_reduce_kernel", "gather_kernel",
-                "gemm_f32_kernel"):
+    for key in ("gemm_m16_kernel", "gemm_mfma_kernel", "skinny_fullk_kernel", "splitk_reduce_kernel",
+                "gather_kernel", "gemm_f32_kernel"):
         if key in name:
             return key
     return name[:48]
@@ -162,7 +162,8 @@ def summarize_traffic(args, w, variant):
     # the gather copy reads and writes exactly m*k*elem bytes
     f_scale = copy_bytes / (fetch["gather_kernel"] * 1024.0)
     w_scale = copy_bytes / (write["gather_kernel"] * 1024.0)
-    main = next(k for k in ("gemm_m16_kernel", "gemm_mfma_kernel", "gemm_f32_kernel") if k in fetch)
+    main = next(k for k in ("gemm_m16_kernel", "gemm_mfma_kernel", "skinny_fullk_kernel", "gemm_f32_kernel")
+                if k in fetch)
     fb = fetch[main] * 1024.0 * f_scale
     wb = write[main] * 1024.0 * w_scale
     extra = {}

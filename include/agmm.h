@@ -206,12 +206,15 @@ int agmm_plan_autotune(agmm_plan_t plan, const void *const *shard_ptrs, const vo
  *                   operand ring), 14 128x128 and 15 128x64
  *                   (rhs_transpose only) in the same ring, 16 256x256 and
  *                   17 128x128 in the same ring on 16x16x32 MFMAs (the
- *                   automatic choices for k >= 256)
+ *                   automatic choices for k >= 256), 18 the whole-k skinny
+ *                   kernel (rhs_transpose only; tile from "skinny_shape"; no
+ *                   k split; the automatic skinny choice for m <= 128)
  *   "splits"        0: automatic, else k-splits (fp32 partial sums, then a
  *                   fixed-order reduction) of every bf16/fp16 launch (for the
  *                   staged variant: of each chunk's launch); automatic splits
- *                   are used by the skinny variant and by launches whose
- *                   output tiles fill at most half of the CUs
+ *                   are used by the split-K skinny tiles and by launches
+ *                   whose output tiles fill at most half of the workgroup
+ *                   slots; tile 18 ignores it
  *   "local_shard"   0 .. num_shards-1: where the ring order starts
  *   "order"         0: ring order from local_shard, 1: natural order
  *   "group_m"       row blocks walked together (L2 reuse); 0 (default):
@@ -221,6 +224,9 @@ int agmm_plan_autotune(agmm_plan_t plan, const void *const *shard_ptrs, const vo
  *   "copy_wgs"      >= 0: workgroups of each staged chunk copy (0 = auto:
  *                   sized to the whole GPU) and of the side gather of
  *                   agmm_run_gather_out (0 = one per CU)
+ *   "skinny_shape"  0..4: output tile of the whole-k skinny kernel (tile 18):
+ *                   0: 64 x 16, 1: 32 x 32 (default), 2: 32 x 16, 3: 16 x 32,
+ *                   4: 64 x 32 rows x columns
  *   "copy_engine"   0 (default) or 1: what performs the copies that run
  *                   beside a GEMM (staged chunks after the first, the side
  *                   gather of agmm_run_gather_out).  0: the gather kernel on

@@ -81,19 +81,85 @@ def test_small_ragged(case, variant):
     check_against_oracle(w, shards, B, C)
 
 
-@pytest.mark.parametrize("tile", list(range(18)))
+@pytest.mark.parametrize("tile", list(range(19)))
 @pytest.mark.parametrize("dtype,rt", [(BF16, False), (BF16, True), (FP16, False), (FP16, True)])
 @pytest.mark.parametrize("k", [328, 384])
 def test_tiles_ragged(tile, dtype, rt, k):
     """Every tile shape against the oracle on ragged m and n; k = 328 leaves a
     ragged last k-tile, k = 384 is whole 64-deep k-tiles, so interior tiles
     take the unmasked load path."""
-    if tile in (8, 11, 15) and not rt:
-        pytest.skip("the 128x64 tile takes B stored n x k only")
+    if tile in (8, 11, 15, 18) and not rt:
+        pytest.skip("the 128x64 and skinny whole-k tiles take B stored n x k only")
     w, shards, B = make_case(3, 200, k, 392, dtype, rt, seed=900 + tile + k)
     shards_d = [to_device(s, dtype) for s in shards]
     B_d = to_device(B, dtype)
     C, _ = run_variant(w, shards_d, B_d, "fused", tile=tile)
+    check_against_oracle(w, shards, B, C)
+
+
+# ------------------------------------------------- skinny kernel, whole k
+SKINNY_FULLK = [
+    # N, m_s, k, n, dtype, extra plan settings
+    (3, 50, 1000, 200, FP16, {}),       # 3 row blocks of 64 (the last ragged), ragged k-tile, ragged n
+    (1, 7, 72, 33, BF16, {}),           # a single short k-tile: waves 2, 3 have none
+    (8, 16, 4096, 1792, BF16, {}),      # the decode-like workload's shape
+    (9, 30, 640, 130, FP16, {}),        # 9 shards, row blocks across shard boundaries
+    (2, 100, 3000, 520, BF16, {"splits": 4}),   # splits ignored: whole k per workgroup
+    (3, 40, 264, 100, BF16, {"lda": 272, "ldb": 280, "ldc": 103}),
+    (5, 13, 8, 16, BF16, {}),           # k = 8: one chunk of one k-tile
+]
+
+
+@pytest.mark.parametrize("shape", [0, 1, 2, 3, 4])
+@pytest.mark.parametrize("case", SKINNY_FULLK, ids=lambda c: f"{c[0]}x{c[1]}x{c[2]}x{c[3]}-d{c[4]}-{len(c[5])}")
+def test_skinny_fullk_tile(case, shape):
+    """Tile 18 (tiles over the whole of k, wave-private LDS rings), every
+    tile shape (64x16, 32x32, 32x16, 16x32, 64x32), against the oracle on
+    ragged m, n and k, strided operands; C's row padding untouched; a second
+    run bit-identical."""
+    N, m_s, k, n, dtype, extra = case
+    w, shards, B = make_case(N, m_s, k, n, dtype, True, seed=2200 + N + m_s + k + n)
+    lda, ldb, ldc = extra.get("lda", k), extra.get("ldb", k), extra.get("ldc", n)
+    dt = torch_dtype(dtype)
+    sd = []
+    for x in shards:
+        buf = torch.full((m_s, lda), float("nan"), dtype=dt, device="cuda")
+        buf[:, :k] = to_device(x, dtype)
+        sd.append(buf[:, :k])
+    bfull = torch.full((n, ldb), float("nan"), dtype=dt, device="cuda")
+    bfull[:, :k] = to_device(B, dtype)
+    C = torch.full((N * m_s, ldc), float("nan"), dtype=dt, device="cuda")
+    plan = agmm.Plan(N, m_s, k, n, dtype, True, variant="skinny", tile=18, skinny_shape=shape, **extra)
+    try:
+        assert plan.get("tile") == 18 and plan.get("splits") == 1 and plan.get("skinny_shape") == shape
+        plan.run(sd, bfull[:, :k], C[:, :n])
+        torch.cuda.synchronize()
+        first = to_bits(C[:, :n])
+        check_against_oracle(w, shards, B, C[:, :n])
+        if ldc > n:
+            assert torch.isnan(C[:, n:].float()).all(), "wrote past n into the row padding"
+        plan.run(sd, bfull[:, :k], C[:, :n])
+        torch.cuda.synchronize()
+        assert np.array_equal(first, to_bits(C[:, :n]))
+    finally:
+        plan.close()
+
+
+def test_skinny_fullk_needs_transposed_b():
+    plan = agmm.Plan(2, 16, 64, 64, BF16, False, variant="skinny")
+    try:
+        with pytest.raises(agmm.AgmmError):
+            plan.set("tile", 18)
+    finally:
+        plan.close()
+
+
+def test_skinny_fullk_in_staged_chunks():
+    """Tile 18 under the staged variant: chunk launches map their rows to C
+    through the chunk's row offset."""
+    w, shards, B = make_case(3, 200, 384, 130, BF16, True, seed=2300)
+    C, _ = run_variant(w, [to_device(x, BF16) for x in shards], to_device(B, BF16), "staged",
+                       pvalue=1, tile=18)
     check_against_oracle(w, shards, B, C)
 
 
@@ -414,7 +480,7 @@ def _random_cases(count, seed):
             variant = "fused"
         settings = {"variant": variant}
         if dtype != FP32 and rng.random() < 0.6:
-            tiles = [0, 1, 2, 3, 4, 5, 6, 7, 9, 10, 12, 13, 14, 16, 17] + ([8, 11, 15] if rt else [])
+            tiles = [0, 1, 2, 3, 4, 5, 6, 7, 9, 10, 12, 13, 14, 16, 17] + ([8, 11, 15, 18] if rt else [])
             settings["tile"] = int(rng.choice(tiles))
             if variant in ("fused", "unfused", "skinny", "staged") and rng.random() < 0.5:
                 settings["splits"] = int(rng.integers(1, 6))
