@@ -120,7 +120,8 @@ struct agmm_plan {
   int group_m = 0;  // 0: chosen per launch shape (pick_group_m)
   int xcd_remap = 1;
   int copy_wgs = 0;
-  int skinny_shape = 1;  // tile shape of the whole-k skinny kernel (launch_skinny_fullk): 32 x 32
+  int skinny_shape = -1;  // tile shape of the whole-k skinny kernel (launch_skinny_fullk); -1 auto
+  int skinny_shape_used = 1;
   int copy_engine = 0;   // copies beside a GEMM: 0 gather kernel (CUs), 1 SDMA engines
   // element strides between rows of the caller's buffers (0: dense)
   int64_t lda = 0, ldb = 0, ldc = 0;
@@ -289,15 +290,17 @@ int configure(agmm_plan* p) {
     p->tile_used = -1;
     p->bm = p->bn = 64;
   } else if (v == AGMM_VARIANT_SKINNY) {
-    // B stored n x k, m <= 128: the whole-k skinny kernel (32 x 32 tiles,
-    // one launch, no partial sums): 11.8 us per call on the 8 x 16 x 4096 ->
-    // 1792 workload in graph replay, against 16.4 for the best split-K tile
-    // (the 128x64 part ring, 8 k ranges) and 13.5 for its 64 x 16 shape.
-    // Otherwise all of m in one row block with split-K over narrow column
-    // blocks, so that enough workgroups stream B.
-    p->tile_used = p->tile >= 0 ? p->tile
-                   : (p->m <= 128 ? (p->rt ? agmm::kTileSkinny : agmm::kTile128x128)
-                                  : agmm::kTile256x128);
+    // B stored n x k, m <= 128: the whole-k skinny kernel (one launch, no
+    // partial sums).  Measured per call in graph replay (us, whole-k against
+    // the best split-K tile): m 128, n 1792, k 4096: 11.8 / 16.4; m 128,
+    // n 512: 8.6 / 14.4; m 64, n 3584, k 8192: 21.6 / 32.3.  For m 256 the
+    // split-K 128x64 part ring was fastest (19.7 against 20.7 whole-k and
+    // 24.8 for the 256x128 tile).  Split-K tiles put all of m in one row
+    // block and split k over narrow column blocks, so that enough
+    // workgroups stream B.
+    if (p->tile >= 0) p->tile_used = p->tile;
+    else if (p->rt) p->tile_used = p->m <= 128 ? agmm::kTileSkinny : agmm::kTile128x64r5;
+    else p->tile_used = p->m <= 128 ? agmm::kTile128x128 : agmm::kTile256x128;
     p->bm = agmm::tile_bm(p->tile_used);
     p->bn = agmm::tile_bn(p->tile_used);
   } else if (v == AGMM_VARIANT_STAGED) {
@@ -312,6 +315,14 @@ int configure(agmm_plan* p) {
     p->bn = agmm::tile_bn(p->tile_used);
   }
 
+  // whole-k skinny tile shape: 32 x 32 unless 64 x 16 gives more workgroups
+  // (small m: m 32, n 1024, k 4096 measured 10.0 us against 11.1)
+  if (p->skinny_shape >= 0) {
+    p->skinny_shape_used = p->skinny_shape;
+  } else {
+    const int64_t t32 = cdiv(p->m, 32) * cdiv(p->n, 32), t64 = cdiv(p->m, 64) * cdiv(p->n, 16);
+    p->skinny_shape_used = t64 > t32 ? 0 : 1;
+  }
   if (!is_f32(p) && p->tile_used == agmm::kTileSkinny && !p->rt)
     return set_err(AGMM_ERR_UNSUPPORTED, "tile %d (skinny, whole k) needs B stored n x k", agmm::kTileSkinny);
 
@@ -480,7 +491,7 @@ int launch_gemm(agmm_plan* p, agmm::GemmProblem& g, hipStream_t s) {
   hipError_t err;
   if (is_f32(p)) err = agmm::launch_gemm_f32(g, p->rt != 0, s);
   else if (p->tile_used == agmm::kTileSkinny)
-    err = agmm::launch_skinny_fullk(g, p->dtype, p->skinny_shape, s);
+    err = agmm::launch_skinny_fullk(g, p->dtype, p->skinny_shape_used, s);
   else err = agmm::launch_gemm_mfma(g, p->tile_used, p->dtype, p->rt != 0, s);
   if (err != hipSuccess) return hip_err(err, "GEMM launch");
   if (timed) {
@@ -738,7 +749,7 @@ int agmm_plan_set_int(agmm_plan_t p, const char* key, int64_t v) {
     if (v < 0 || v > 1 << 20) return bad();
     p->copy_wgs = (int)v;
   } else if (k == "skinny_shape") {
-    if (v < 0 || v > 4) return bad();
+    if (v < -1 || v > 4) return bad();
     p->skinny_shape = (int)v;
   } else if (k == "copy_engine") {
     if (v < 0 || v > 1) return bad();
@@ -773,7 +784,7 @@ int agmm_plan_get_int(agmm_plan_t p, const char* key, int64_t* value) {
   else if (k == "xcd_remap") v = p->xcd_remap;
   else if (k == "copy_wgs") v = p->copy_wgs;
   else if (k == "copy_engine") v = p->copy_engine;
-  else if (k == "skinny_shape") v = p->skinny_shape;
+  else if (k == "skinny_shape") v = p->skinny_shape_used;
   else if (k == "lda") v = lda_of(p);
   else if (k == "ldb") v = ldb_of(p);
   else if (k == "ldc") v = ldc_of(p);

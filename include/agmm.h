@@ -208,7 +208,8 @@ int agmm_plan_autotune(agmm_plan_t plan, const void *const *shard_ptrs, const vo
  *                   17 128x128 in the same ring on 16x16x32 MFMAs (the
  *                   automatic choices for k >= 256), 18 the whole-k skinny
  *                   kernel (rhs_transpose only; tile from "skinny_shape"; no
- *                   k split; the automatic skinny choice for m <= 128)
+ *                   k split; the automatic skinny choice for m <= 128; 15
+ *                   for 128 < m <= 256)
  *   "splits"        0: automatic, else k-splits (fp32 partial sums, then a
  *                   fixed-order reduction) of every bf16/fp16 launch (for the
  *                   staged variant: of each chunk's launch); automatic splits
@@ -224,9 +225,11 @@ int agmm_plan_autotune(agmm_plan_t plan, const void *const *shard_ptrs, const vo
  *   "copy_wgs"      >= 0: workgroups of each staged chunk copy (0 = auto:
  *                   sized to the whole GPU) and of the side gather of
  *                   agmm_run_gather_out (0 = one per CU)
- *   "skinny_shape"  0..4: output tile of the whole-k skinny kernel (tile 18):
- *                   0: 64 x 16, 1: 32 x 32 (default), 2: 32 x 16, 3: 16 x 32,
- *                   4: 64 x 32 rows x columns
+ *   "skinny_shape"  -1 (automatic: 32 x 32, or 64 x 16 when that gives
+ *                   more workgroups) or 0..4: output tile of the whole-k
+ *                   skinny kernel (tile 18): 0: 64 x 16, 1: 32 x 32,
+ *                   2: 32 x 16, 3: 16 x 32, 4: 64 x 32 rows x columns
+ *                   (reads back the shape in use)
  *   "copy_engine"   0 (default) or 1: what performs the copies that run
  *                   beside a GEMM (staged chunks after the first, the side
  *                   gather of agmm_run_gather_out).  0: the gather kernel on

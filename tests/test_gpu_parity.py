@@ -145,6 +145,21 @@ def test_skinny_fullk_tile(case, shape):
         plan.close()
 
 
+@pytest.mark.parametrize("shape,tile,skinny_shape", [
+    ((8, 16, 4096, 1792), 18, 1), ((2, 16, 4096, 1024), 18, 0), ((16, 16, 4096, 1792), 15, None)])
+def test_skinny_automatic_choice(shape, tile, skinny_shape):
+    """The skinny variant's automatic tile: the whole-k kernel for m <= 128
+    (64 x 16 when that gives more workgroups than 32 x 32), the split-K
+    128x64 part ring for 128 < m <= 256."""
+    plan = agmm.Plan(*shape, BF16, True, variant="skinny")
+    try:
+        assert plan.get("tile") == tile
+        if skinny_shape is not None:
+            assert plan.get("skinny_shape") == skinny_shape
+    finally:
+        plan.close()
+
+
 def test_skinny_fullk_needs_transposed_b():
     plan = agmm.Plan(2, 16, 64, 64, BF16, False, variant="skinny")
     try:
