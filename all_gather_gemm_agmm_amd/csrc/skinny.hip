@@ -7,15 +7,18 @@
 // At these shapes the work is one pass over B.  The split-K tiles spread B
 // over the CUs by splitting k, which costs fp32 partial sums and a second,
 // reduction launch.  Here every workgroup takes the whole of k for a narrow
-// tile instead: 64 rows x 16 columns, so m = 128, n = 1792 gives 224
-// workgroups, each reading 128 KiB of B (from HBM) and 512 KiB of A (from
-// L2: all workgroups share the 1 MiB of A).  No partials, one launch.
+// tile instead (32 x 32 by default), so m = 128, n = 1792 gives 224
+// workgroups, each reading 256 KiB of B and 256 KiB of A (A's 1 MiB is
+// shared by all workgroups through L2; B comes from HBM once, its column
+// block shared by the 4 row blocks on one XCD).  No partials, one launch.
 //
 //  * The 4 waves take the k-tiles (64 deep) round robin and accumulate
-//    separately; each streams its own k-tiles through a private ring of 4
-//    LDS slots (A 8 KiB + B 2 KiB per slot) with global -> LDS DMA, so the
+//    separately; each streams its own k-tiles through a private ring of LDS
+//    slots (40 KiB per wave; e.g. 5 slots of A 4 KiB + B 4 KiB for the
+//    32 x 32 tile) with global -> LDS DMA, so the
 //    main loop has no workgroup barrier: each wave waits only for its own
-//    loads (vmcnt), with up to 3 k-tiles (30 KiB) in flight.
+//    loads (vmcnt), and every slot is in flight (a slot is refilled as soon
+//    as its k-tile has been read into registers).
 //  * v_mfma_f32_16x16x32 with the B fragment first: each 16-lane group g
 //    holds k elements [8g, 8g + 8) of a k32 step; 4 row blocks x 1 column
 //    block per wave.  LDS rows of 128 bytes, chunk c of row r at
@@ -63,7 +66,7 @@ struct Shape {
   static_assert(ROWS % 16 == 0 && COLS % 16 == 0, "16x16 MFMA blocks");
   static_assert(kSlots >= 2, "ring");
   static_assert(kWaves * kWaveBytes <= 160 * 1024, "LDS");
-  static_assert((kSlots - 1) * kLoads < 64, "loads in flight exceed vmcnt");
+  static_assert(kSlots * kLoads < 64, "loads in flight exceed vmcnt");
 };
 
 template <int DT>
@@ -127,7 +130,7 @@ __device__ __forceinline__ void split_row(int r, int rpg, float inv, int& g, int
   if (t >= rpg) { ++g; t -= rpg; }
 }
 
-// vmcnt(after * kLoads) for a wave-uniform `after` in [0, kSlots - 2]
+// vmcnt(after * kLoads) for a wave-uniform `after` in [0, kMax]
 template <int kLoads, int kMax>
 __device__ __forceinline__ void wait_tiles(int after) {
   if constexpr (kMax <= 0) {
@@ -251,15 +254,13 @@ void skinny_fullk_kernel(GemmProblem p) {
 
   __builtin_amdgcn_sched_barrier(0);
   asm volatile("" ::: "memory");
-  const int pre = nt < kSlots - 1 ? nt : kSlots - 1;
+  // every slot in flight: k-tiles 0 .. kSlots-1 first, then slot j % kSlots
+  // is refilled with k-tile j + kSlots as soon as k-tile j has been read
+  const int pre = nt < kSlots ? nt : kSlots;
   for (int j = 0; j < pre; ++j) issue(j);
   for (int j = 0; j < nt; ++j) {
     // k-tiles issued after j and still allowed in flight
-    wait_tiles<kLoads, kSlots - 2>(min(kSlots - 2, nt - 1 - j));
-    if (j + kSlots - 1 < nt) {
-      lds_reads_done();   // the slot about to be refilled was read at j - 1
-      issue(j + kSlots - 1);
-    }
+    wait_tiles<kLoads, kSlots - 1>(min(kSlots - 1, nt - 1 - j));
     const char* slot = ring + (j % kSlots) * kSlotBytes;
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
@@ -273,6 +274,10 @@ void skinny_fullk_kernel(GemmProblem p) {
 #pragma unroll
         for (int f = 0; f < FN; ++f) acc[i][f] = mfma16<DT>(bf[f], af, acc[i][f]);
       }
+    }
+    if (j + kSlots < nt) {
+      lds_reads_done();   // k-tile j's fragments are in registers: its slot is free
+      issue(j + kSlots);
     }
   }
   wait_vmcnt<0>();
