@@ -121,7 +121,7 @@ struct agmm_plan {
   int xcd_remap = 1;
   int copy_wgs = 0;
   int skinny_shape = -1;  // tile shape of the whole-k skinny kernel (launch_skinny_fullk); -1 auto
-  int skinny_shape_used = 1;
+  int skinny_shape_used = 5;
   int copy_engine = 0;   // copies beside a GEMM: 0 gather kernel (CUs), 1 SDMA engines
   // element strides between rows of the caller's buffers (0: dense)
   int64_t lda = 0, ldb = 0, ldc = 0;
@@ -315,13 +315,14 @@ int configure(agmm_plan* p) {
     p->bn = agmm::tile_bn(p->tile_used);
   }
 
-  // whole-k skinny tile shape: 32 x 32 unless 64 x 16 gives more workgroups
-  // (small m: m 32, n 1024, k 4096 measured 10.0 us against 11.1)
+  // whole-k skinny tile shape: 32 x 32 with 8 waves (2-3% faster than 4 on
+  // four skinny shapes) unless 64 x 16 gives more workgroups (small m: m 32,
+  // n 1024, k 4096 measured 10.1 us against 10.9)
   if (p->skinny_shape >= 0) {
     p->skinny_shape_used = p->skinny_shape;
   } else {
     const int64_t t32 = cdiv(p->m, 32) * cdiv(p->n, 32), t64 = cdiv(p->m, 64) * cdiv(p->n, 16);
-    p->skinny_shape_used = t64 > t32 ? 0 : 1;
+    p->skinny_shape_used = t64 > t32 ? 0 : 5;
   }
   if (!is_f32(p) && p->tile_used == agmm::kTileSkinny && !p->rt)
     return set_err(AGMM_ERR_UNSUPPORTED, "tile %d (skinny, whole k) needs B stored n x k", agmm::kTileSkinny);
@@ -749,7 +750,7 @@ int agmm_plan_set_int(agmm_plan_t p, const char* key, int64_t v) {
     if (v < 0 || v > 1 << 20) return bad();
     p->copy_wgs = (int)v;
   } else if (k == "skinny_shape") {
-    if (v < -1 || v > 4) return bad();
+    if (v < -1 || v > 6) return bad();
     p->skinny_shape = (int)v;
   } else if (k == "copy_engine") {
     if (v < 0 || v > 1) return bad();

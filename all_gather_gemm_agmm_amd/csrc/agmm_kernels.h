@@ -95,7 +95,8 @@ hipError_t launch_gemm_mfma(const GemmProblem& p, int tile_cfg, int dtype, bool 
 // each over the whole of k in one workgroup (no split, one launch; p.splits
 // is ignored).  C rows through the row map.
 // `shape` selects the tile: 0: 64 x 16, 1: 32 x 32, 2: 32 x 16, 3: 16 x 32,
-// 4: 64 x 32 (rows x columns).
+// 4: 64 x 32 (rows x columns) with 4 waves; 5: 32 x 32 and 6: 64 x 16 with
+// 8 waves (the LDS shared out over twice as many, half as deep, rings).
 hipError_t launch_skinny_fullk(const GemmProblem& p, int dtype, int shape, hipStream_t stream);
 
 // fp32 inputs, fp64 accumulate, fp32 output (any shape).

@@ -12,10 +12,10 @@
 // shared by all workgroups through L2; B comes from HBM once, its column
 // block shared by the 4 row blocks on one XCD).  No partials, one launch.
 //
-//  * The 4 waves take the k-tiles (64 deep) round robin and accumulate
-//    separately; each streams its own k-tiles through a private ring of LDS
-//    slots (40 KiB per wave; e.g. 5 slots of A 4 KiB + B 4 KiB for the
-//    32 x 32 tile) with global -> LDS DMA, so the
+//  * The waves (4 or 8) take the k-tiles (64 deep) round robin and
+//    accumulate separately; each streams its own k-tiles through a private
+//    ring of LDS slots (160 KiB shared out; e.g. 5 slots of A 4 KiB + B 4 KiB
+//    per wave for the 32 x 32 tile with 4 waves) with global -> LDS DMA, so the
 //    main loop has no workgroup barrier: each wave waits only for its own
 //    loads (vmcnt), and every slot is in flight (a slot is refilled as soon
 //    as its k-tile has been read into registers).
@@ -27,7 +27,7 @@
 //  * The two row halves of a column block sit on the same XCD (workgroups
 //    are dispatched round robin over the 8 XCDs; each XCD gets a contiguous
 //    range of logical tiles), so B is fetched from HBM once.
-//  * The 4 wave partials are summed in LDS in wave order (fixed), cast with
+//  * The wave partials are summed in LDS in wave order (fixed), cast with
 //    round-to-nearest-even and stored through the row map.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -49,14 +49,14 @@ typedef __attribute__((address_space(3))) char lds_char_t;
 __device__ __attribute__((aligned(64))) const uint32_t sk_zero16[16] = {0};
 
 constexpr int kKT = 64;                   // k elements per k-tile
-constexpr int kWaves = 4;
-constexpr int kWaveLds = 40 * 1024;       // LDS per wave (4 waves: all 160 KiB)
 
 // Shape of one tile configuration: ROWS x COLS outputs, 1 KiB DMAs per
 // k-tile (8 rows of 128 bytes each), as many ring slots as fit in a wave's
 // LDS share.
-template <int ROWS, int COLS>
+template <int ROWS, int COLS, int WAVES>
 struct Shape {
+  static constexpr int kWaves = WAVES;
+  static constexpr int kWaveLds = 160 * 1024 / WAVES;   // LDS per wave: all 160 KiB shared out
   static constexpr int kRows = ROWS, kCols = COLS;
   static constexpr int kALoads = ROWS / 8, kBLoads = COLS / 8;
   static constexpr int kLoads = kALoads + kBLoads;
@@ -141,10 +141,11 @@ __device__ __forceinline__ void wait_tiles(int after) {
   }
 }
 
-template <int DT, int ROWS, int COLS>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+template <int DT, int ROWS, int COLS, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(WAVES / 4, WAVES / 4)))
 void skinny_fullk_kernel(GemmProblem p) {
-  using S = Shape<ROWS, COLS>;
+  using S = Shape<ROWS, COLS, WAVES>;
+  constexpr int kWaves = S::kWaves, kThreads = 64 * WAVES;
   constexpr int kRows = S::kRows, kCols = S::kCols, kALoads = S::kALoads, kBLoads = S::kBLoads;
   constexpr int kLoads = S::kLoads, kSlotBytes = S::kSlotBytes, kSlots = S::kSlots;
   constexpr int kWaveBytes = S::kWaveBytes;
@@ -297,7 +298,7 @@ void skinny_fullk_kernel(GemmProblem p) {
   // ROWS x COLS outputs, 4 consecutive columns per thread and pass
   constexpr int E4 = kRows * kCols / 4;
 #pragma unroll
-  for (int e4 = tid; e4 < E4; e4 += 256) {
+  for (int e4 = tid; e4 < E4; e4 += kThreads) {
   const int row = e4 / (kCols / 4), c4 = (e4 % (kCols / 4)) * 4;
   f32x4_t v = *reinterpret_cast<const f32x4_t*>(reinterpret_cast<const float*>(smem) + row * RLD + c4);
 #pragma unroll
@@ -325,15 +326,15 @@ void skinny_fullk_kernel(GemmProblem p) {
 
 }  // namespace
 
-template <int ROWS, int COLS>
+template <int ROWS, int COLS, int WAVES = 4>
 hipError_t launch_shape(const GemmProblem& p, int dtype, hipStream_t stream) {
   const int64_t tiles = (int64_t)((p.m + ROWS - 1) / ROWS) * ((p.n + COLS - 1) / COLS);
   if (tiles > (int64_t(1) << 30)) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)tiles), block(256);
+  const dim3 grid((unsigned)tiles), block(64 * WAVES);
   if (dtype == kDtypeBf16)
-    hipLaunchKernelGGL((skinny_fullk_kernel<kDtypeBf16, ROWS, COLS>), grid, block, 0, stream, p);
+    hipLaunchKernelGGL((skinny_fullk_kernel<kDtypeBf16, ROWS, COLS, WAVES>), grid, block, 0, stream, p);
   else
-    hipLaunchKernelGGL((skinny_fullk_kernel<kDtypeFp16, ROWS, COLS>), grid, block, 0, stream, p);
+    hipLaunchKernelGGL((skinny_fullk_kernel<kDtypeFp16, ROWS, COLS, WAVES>), grid, block, 0, stream, p);
   return hipGetLastError();
 }
 
@@ -348,6 +349,8 @@ hipError_t launch_skinny_fullk(const GemmProblem& p, int dtype, int shape, hipSt
     case 2: return launch_shape<32, 16>(p, dtype, stream);
     case 3: return launch_shape<16, 32>(p, dtype, stream);
     case 4: return launch_shape<64, 32>(p, dtype, stream);
+    case 5: return launch_shape<32, 32, 8>(p, dtype, stream);
+    case 6: return launch_shape<64, 16, 8>(p, dtype, stream);
     default: return hipErrorInvalidValue;
   }
 }

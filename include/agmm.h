@@ -225,11 +225,12 @@ int agmm_plan_autotune(agmm_plan_t plan, const void *const *shard_ptrs, const vo
  *   "copy_wgs"      >= 0: workgroups of each staged chunk copy (0 = auto:
  *                   sized to the whole GPU) and of the side gather of
  *                   agmm_run_gather_out (0 = one per CU)
- *   "skinny_shape"  -1 (automatic: 32 x 32, or 64 x 16 when that gives
- *                   more workgroups) or 0..4: output tile of the whole-k
- *                   skinny kernel (tile 18): 0: 64 x 16, 1: 32 x 32,
- *                   2: 32 x 16, 3: 16 x 32, 4: 64 x 32 rows x columns
- *                   (reads back the shape in use)
+ *   "skinny_shape"  -1 (automatic: 5, or 0 when 64 x 16 gives more
+ *                   workgroups than 32 x 32) or 0..6: output tile of the
+ *                   whole-k skinny kernel (tile 18), rows x columns: 0 64 x 16,
+ *                   1 32 x 32, 2 32 x 16, 3 16 x 32, 4 64 x 32 (4 waves);
+ *                   5 32 x 32, 6 64 x 16 (8 waves).  Reads back the shape in
+ *                   use.
  *   "copy_engine"   0 (default) or 1: what performs the copies that run
  *                   beside a GEMM (staged chunks after the first, the side
  *                   gather of agmm_run_gather_out).  0: the gather kernel on

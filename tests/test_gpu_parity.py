@@ -110,7 +110,7 @@ SKINNY_FULLK = [
 ]
 
 
-@pytest.mark.parametrize("shape", [0, 1, 2, 3, 4])
+@pytest.mark.parametrize("shape", [0, 1, 2, 3, 4, 5, 6])
 @pytest.mark.parametrize("case", SKINNY_FULLK, ids=lambda c: f"{c[0]}x{c[1]}x{c[2]}x{c[3]}-d{c[4]}-{len(c[5])}")
 def test_skinny_fullk_tile(case, shape):
     """Tile 18 (tiles over the whole of k, wave-private LDS rings), every
@@ -146,7 +146,7 @@ def test_skinny_fullk_tile(case, shape):
 
 
 @pytest.mark.parametrize("shape,tile,skinny_shape", [
-    ((8, 16, 4096, 1792), 18, 1), ((2, 16, 4096, 1024), 18, 0), ((16, 16, 4096, 1792), 15, None)])
+    ((8, 16, 4096, 1792), 18, 5), ((2, 16, 4096, 1024), 18, 0), ((16, 16, 4096, 1792), 15, None)])
 def test_skinny_automatic_choice(shape, tile, skinny_shape):
     """The skinny variant's automatic tile: the whole-k kernel for m <= 128
     (64 x 16 when that gives more workgroups than 32 x 32), the split-K
