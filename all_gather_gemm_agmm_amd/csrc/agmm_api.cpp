@@ -126,6 +126,7 @@ struct agmm_plan {
   // element strides between rows of the caller's buffers (0: dense)
   int64_t lda = 0, ldb = 0, ldc = 0;
   int gemm_streams = 2;   // staged: chunk GEMMs alternate over this many streams (1 or 2)
+  int local_first = 1;    // staged: the local shard's rows first, straight from its buffer
   int debug_keep_slots = 0;
   // derived
   int variant_used = AGMM_VARIANT_FUSED;
@@ -376,7 +377,9 @@ int configure(agmm_plan* p) {
     want = std::max<int64_t>(1, std::min<int64_t>(want, cdiv(p->k, agmm::kTileBK)));
     p->k_per_split = cdiv(cdiv(p->k, want), agmm::kTileBK) * agmm::kTileBK;
     p->splits_used = (int)cdiv(p->k, p->k_per_split);
-    if (p->splits_used > 1) part_bytes = (size_t)p->splits_used * launch_m * p->n * sizeof(float);
+    // a staged plan's launches: its chunks and (local_first) the local shard's rows
+    const int64_t part_m = v == AGMM_VARIANT_STAGED ? std::max<int64_t>(launch_m, p->m_s) : launch_m;
+    if (p->splits_used > 1) part_bytes = (size_t)p->splits_used * part_m * p->n * sizeof(float);
   }
 
   // tile orders (one table per chunk)
@@ -580,10 +583,30 @@ int run_staged(agmm_plan* p, const void* const* shards, const void* B, void* C, 
   // take the CUs chunk c's workgroups leave (each chunk's launch is usually
   // a partial round); only the ring-slot events order them.  With split-K the
   // chunks share one partials buffer and stay on the caller's stream.
-  const bool alt = p->gemm_streams == 2 && p->splits_used == 1 && p->num_chunks > 1;
+  // The local shard's rows need no copy (tpu-inference `all_gather_matmul`:
+  // a device multiplies its own x block while the ring brings the others):
+  // with local_first their GEMM runs first, from the shard buffer, on the
+  // caller's stream beside chunk 0's copy, and the chunk GEMMs cover the
+  // other shards' rows only.
+  const bool local_first = p->local_first && p->N > 1;
+  const bool alt = p->gemm_streams == 2 && p->splits_used == 1 && (p->num_chunks > 1 || local_first);
   if (alt && (err = hipStreamWaitEvent(p->compute2, p->ev_entry, 0)) != hipSuccess)
     return hip_err(err, "hipStreamWaitEvent");
   const int64_t e = elem_bytes(p->dtype);
+  const int r0 = p->local_shard;
+  if (local_first) {
+    agmm::RowMap rm{};
+    rm.a_group[0] = shards[r0];
+    rm.a_ld = lda_of(p);
+    rm.rows_per_group = (int32_t)p->m_s;
+    rm.num_groups = 1;
+    rm.c_group_rows = 0;
+    rm.c_row_off = (int64_t)r0 * p->m_s;
+    agmm::GemmProblem g = base_problem(p, rm, p->m_s, B, C, -1);
+    with_splits(p, g);
+    const int rc = launch_gemm(p, g, s);
+    if (rc != AGMM_OK) return rc;
+  }
   for (int c = 0; c < p->num_chunks; ++c) {
     const int slot = c % p->nslots;
     const int64_t row0 = (int64_t)c * p->rows_per_chunk;
@@ -611,20 +634,43 @@ int run_staged(agmm_plan* p, const void* const* shards, const void* B, void* C, 
     if (rc != AGMM_OK) return rc;
     if ((err = hipEventRecord(p->ev_ready[slot], p->copy_stream)) != hipSuccess)
       return hip_err(err, "hipEventRecord(ready)");
-    hipStream_t cs = (alt && (c & 1)) ? p->compute2 : s;
+    // chunks alternate streams; with local_first chunk 0 takes the second
+    // stream, beside the local GEMM on the caller's
+    hipStream_t cs = (alt && ((c & 1) == (local_first ? 0 : 1))) ? p->compute2 : s;
     if ((err = hipStreamWaitEvent(cs, p->ev_ready[slot], 0)) != hipSuccess)
       return hip_err(err, "hipStreamWaitEvent(ready)");
-    agmm::RowMap rm{};
-    for (int g = 0; g < p->N; ++g) rm.a_group[g] = dst + (size_t)g * dst_group_rows * p->k * e;
-    rm.a_ld = p->k;
-    rm.rows_per_group = (int32_t)rows_c;
-    rm.num_groups = p->N;
-    rm.c_group_rows = p->m_s;
-    rm.c_row_off = row0;
-    agmm::GemmProblem g = base_problem(p, rm, rows_c * p->N, B, C, c);
-    with_splits(p, g);
-    rc = launch_gemm(p, g, cs);
-    if (rc != AGMM_OK) return rc;
+    if (!local_first) {
+      agmm::RowMap rm{};
+      for (int g = 0; g < p->N; ++g) rm.a_group[g] = dst + (size_t)g * dst_group_rows * p->k * e;
+      rm.a_ld = p->k;
+      rm.rows_per_group = (int32_t)rows_c;
+      rm.num_groups = p->N;
+      rm.c_group_rows = p->m_s;
+      rm.c_row_off = row0;
+      agmm::GemmProblem g = base_problem(p, rm, rows_c * p->N, B, C, c);
+      with_splits(p, g);
+      rc = launch_gemm(p, g, cs);
+      if (rc != AGMM_OK) return rc;
+    } else {
+      // the other shards, as the runs [0, r0) and (r0, N) of consecutive
+      // shards (C rows are linear in the shard index within a run)
+      const int lo_hi[2][2] = {{0, r0}, {r0 + 1, p->N}};
+      for (const auto& run : lo_hi) {
+        const int lo = run[0], cnt = run[1] - run[0];
+        if (cnt <= 0) continue;
+        agmm::RowMap rm{};
+        for (int j = 0; j < cnt; ++j) rm.a_group[j] = dst + (size_t)(lo + j) * dst_group_rows * p->k * e;
+        rm.a_ld = p->k;
+        rm.rows_per_group = (int32_t)rows_c;
+        rm.num_groups = cnt;
+        rm.c_group_rows = p->m_s;
+        rm.c_row_off = (int64_t)lo * p->m_s + row0;
+        agmm::GemmProblem g = base_problem(p, rm, rows_c * cnt, B, C, -1);
+        with_splits(p, g);
+        rc = launch_gemm(p, g, cs);
+        if (rc != AGMM_OK) return rc;
+      }
+    }
     if (!gathered && (err = hipEventRecord(p->ev_free[slot], cs)) != hipSuccess)
       return hip_err(err, "hipEventRecord(free)");
   }
@@ -736,6 +782,9 @@ int agmm_plan_set_int(agmm_plan_t p, const char* key, int64_t v) {
   } else if (k == "xcd_remap") {
     if (v != 0 && v != 1) return bad();
     p->xcd_remap = (int)v;
+  } else if (k == "local_first") {
+    if (v != 0 && v != 1) return bad();
+    p->local_first = (int)v;
   } else if (k == "gemm_streams") {
     if (v < 1 || v > 2) return bad();
     p->gemm_streams = (int)v;
@@ -790,6 +839,7 @@ int agmm_plan_get_int(agmm_plan_t p, const char* key, int64_t* value) {
   else if (k == "ldb") v = ldb_of(p);
   else if (k == "ldc") v = ldc_of(p);
   else if (k == "gemm_streams") v = p->gemm_streams;
+  else if (k == "local_first") v = p->local_first;
   else if (k == "debug_keep_slots") v = p->debug_keep_slots;
   else if (k == "num_chunks") v = p->num_chunks;
   else if (k == "rows_per_chunk") v = p->rows_per_chunk;

@@ -247,6 +247,12 @@ int agmm_plan_autotune(agmm_plan_t plan, const void *const *shard_ptrs, const vo
  *   "gemm_streams"  1 or 2 (default 2): staged chunk GEMMs alternate over
  *                   this many streams, so one chunk's workgroups fill the
  *                   CUs the previous chunk's leave (1 with split-K)
+ *   "local_first"   0/1 (default 1): the staged variant computes the local
+ *                   shard's rows (shard "local_shard") first, straight from
+ *                   its buffer and beside the first chunk's copy (it needs no
+ *                   copy: tpu-inference `all_gather_matmul`, a device's own
+ *                   x block); the chunk GEMMs then cover the other shards'
+ *                   rows.  The ring slots still hold every shard's rows.
  *   "debug_keep_slots" 0/1: staged variant uses one slot per chunk (nothing
  *                   is overwritten; for inspection by agmm_plan_slot_ptr)
  * Changing a key that affects the workspace reallocates it (synchronously).

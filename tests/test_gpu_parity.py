@@ -665,6 +665,37 @@ def test_group_m_automatic(shape, want):
         plan.close()
 
 
+@pytest.mark.parametrize("local_shard", [0, 1, 3])
+@pytest.mark.parametrize("settings", [{"pvalue": 1, "nbuf": 2, "tile": 14},
+                                      {"pvalue": 2, "nbuf": 1, "tile": 1},
+                                      {"pvalue": 1, "nbuf": 2, "tile": 14, "splits": 2},
+                                      {"pvalue": 1, "nbuf": 3, "tile": 14, "gemm_streams": 1}])
+def test_staged_local_first(local_shard, settings):
+    """The staged variant with the local shard's rows computed first from
+    its own buffer (local_first 1) against the same plan without (0): the
+    same bits (same tile, same k order per element), and the oracle's
+    values; C from agmm_run_gather_out too, with its gathered operand."""
+    w, shards, B = make_case(4, 300, 256, 136, BF16, True, seed=2400 + local_shard)
+    sd = [to_device(x, BF16) for x in shards]
+    bd = to_device(B, BF16)
+    outs = []
+    for lf in (0, 1):
+        plan = agmm.Plan(4, 300, 256, 136, BF16, True, variant="staged", local_shard=local_shard,
+                         local_first=lf, **settings)
+        try:
+            assert plan.get("local_first") == lf
+            C = plan.run(sd, bd)
+            C2, G = plan.run_gather_out(sd, bd)
+            torch.cuda.synchronize()
+            assert np.array_equal(to_bits(C), to_bits(C2))
+            assert np.array_equal(to_bits(G), np.concatenate(shards, axis=0))
+            outs.append(to_bits(C))
+        finally:
+            plan.close()
+    assert np.array_equal(outs[0], outs[1])
+    check_against_oracle(w, shards, B, C)
+
+
 def test_copy_engine_validated():
     plan = agmm.Plan(2, 64, 64, 64, BF16, True, variant="staged")
     try:
