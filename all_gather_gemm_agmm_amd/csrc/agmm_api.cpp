@@ -126,7 +126,7 @@ struct agmm_plan {
   // element strides between rows of the caller's buffers (0: dense)
   int64_t lda = 0, ldb = 0, ldc = 0;
   int gemm_streams = 2;   // staged: chunk GEMMs alternate over this many streams (1 or 2)
-  int local_first = 1;    // staged: the local shard's rows first, straight from its buffer
+  int local_first = 0;    // staged: the local shard's rows first, straight from its buffer
   int debug_keep_slots = 0;
   // derived
   int variant_used = AGMM_VARIANT_FUSED;
@@ -588,7 +588,11 @@ int run_staged(agmm_plan* p, const void* const* shards, const void* B, void* C, 
   // with local_first their GEMM runs first, from the shard buffer, on the
   // caller's stream beside chunk 0's copy, and the chunk GEMMs cover the
   // other shards' rows only.
-  const bool local_first = p->local_first && p->N > 1;
+  // Off by default: measured neutral on 8x1024x8192 -> 3584 (435 us), 1%
+  // faster on 8x4096x8192 -> 7168, slower where the launches are small
+  // (4x512x4096 -> 1024: 62 -> 75 us; with one chunk, 28 -> 43 us on
+  // 8x16x4096 -> 1792, so it is never used with a single chunk).
+  const bool local_first = p->local_first && p->N > 1 && p->num_chunks > 1;
   const bool alt = p->gemm_streams == 2 && p->splits_used == 1 && (p->num_chunks > 1 || local_first);
   if (alt && (err = hipStreamWaitEvent(p->compute2, p->ev_entry, 0)) != hipSuccess)
     return hip_err(err, "hipStreamWaitEvent");

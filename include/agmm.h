@@ -247,7 +247,8 @@ int agmm_plan_autotune(agmm_plan_t plan, const void *const *shard_ptrs, const vo
  *   "gemm_streams"  1 or 2 (default 2): staged chunk GEMMs alternate over
  *                   this many streams, so one chunk's workgroups fill the
  *                   CUs the previous chunk's leave (1 with split-K)
- *   "local_first"   0/1 (default 1): the staged variant computes the local
+ *   "local_first"   0 (default) or 1: with two or more chunks, the staged
+ *                   variant computes the local
  *                   shard's rows (shard "local_shard") first, straight from
  *                   its buffer and beside the first chunk's copy (it needs no
  *                   copy: tpu-inference `all_gather_matmul`, a device's own
