@@ -240,6 +240,29 @@ def test_gather_bit_exact(dtype):
     assert np.array_equal(to_bits(G), oracle.gather(shards, dtype))
 
 
+def test_gather_larger_than_mall_bit_exact():
+    """A gather above 256 MiB (workload 5's 8 shards x 4096 x 8192 bf16 =
+    512 MiB; the copy then uses non-temporal stores): bit-exact against the
+    concatenation, checked in full on the device and on sampled rows
+    against the host inputs."""
+    w = I.WORKLOADS[5]
+    shards, _ = I.make_inputs(w)
+    sd = [to_device(x, w.dtype) for x in shards]
+    G = torch.empty((w.m, w.k), dtype=torch_dtype(w.dtype), device="cuda")
+    G.fill_(float("nan"))
+    plan = agmm.Plan(w.num_shards, w.m_per_shard, w.k, w.n_local, w.dtype, w.rhs_transpose)
+    try:
+        plan.gather(sd, G)
+        torch.cuda.synchronize()
+    finally:
+        plan.close()
+    assert torch.equal(G.view(torch.int16), torch.cat(sd, 0).view(torch.int16))
+    for r in sample_rows(w.num_shards, w.m_per_shard, per_shard=2, seed=5):
+        s_, i = divmod(r, w.m_per_shard)
+        assert np.array_equal(to_bits(G[r:r + 1])[0], shards[s_][i])
+    del G, sd
+
+
 @pytest.mark.parametrize("copy_engine", [0, 1])
 def test_staged_slots_bit_exact(copy_engine):
     """debug_keep_slots: every chunk keeps its own slot; each equals the
