@@ -70,7 +70,7 @@ typedef enum {
 
 /* Paths an agmm_run can take (key "variant" of agmm_plan_set_int). */
 typedef enum {
-  AGMM_VARIANT_AUTO = 0,    /* plan picks: fused, or split-K for skinny m */
+  AGMM_VARIANT_AUTO = 0,    /* plan picks: fused, or skinny for m <= 256 */
   AGMM_VARIANT_FUSED = 1,   /* GEMM reads A rows straight from the shard
                                buffers; no gathered copy (Ascend tutorial,
                                "AllGather + GEMM (Fused Distributed Kernel)":
@@ -81,8 +81,11 @@ typedef enum {
                                Buffering" and "pvalue Parameter") */
   AGMM_VARIANT_UNFUSED = 3, /* gather all of A, then one GEMM, one stream (the
                                decomposed approach the tutorial compares to) */
-  AGMM_VARIANT_SKINNY = 4   /* split-K GEMM from the shard buffers with an
-                               in-kernel fixed-order reduction (small m) */
+  AGMM_VARIANT_SKINNY = 4   /* small m, from the shard buffers: with B
+                               stored n x k and m <= 128 a kernel that takes
+                               all of k per workgroup (no k split, one
+                               launch); otherwise split-K with a fixed-order
+                               reduction launch (tpu-inference `grid_k`) */
 } agmm_variant;
 
 /*
