@@ -64,6 +64,8 @@ class Oracle:
         lib.agmm_oracle_f64.restype = ci
         lib.agmm_oracle_num_threads.argtypes = []
         lib.agmm_oracle_num_threads.restype = ci
+        lib.agmm_oracle_set_threads.argtypes = [ci]
+        lib.agmm_oracle_set_threads.restype = None
         self.lib = lib
         self.path = lib_path
 
@@ -129,6 +131,10 @@ class Oracle:
     def num_threads(self) -> int:
         return int(self.lib.agmm_oracle_num_threads())
 
+    def set_threads(self, n: int) -> None:
+        """Threads of later calls (timing on one core; results are the same)."""
+        self.lib.agmm_oracle_set_threads(int(n))
+
 
 _default: Optional[Oracle] = None
 
@@ -155,3 +161,7 @@ def agmm_f64(shards: Sequence[np.ndarray], B: np.ndarray, dtype: int,
 
 def num_threads() -> int:
     return default().num_threads()
+
+
+def set_threads(n: int) -> None:
+    default().set_threads(n)

@@ -195,3 +195,14 @@ int agmm_oracle_num_threads(void) {
   return 1;
 #endif
 }
+
+/* Threads the following oracle calls use (n >= 1); for timing the oracle on
+ * one host core as well as on all of them.  Does not change what it computes:
+ * every output element is one sequential sum in either case. */
+void agmm_oracle_set_threads(int n) {
+#ifdef _OPENMP
+  if (n >= 1) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
