@@ -15,6 +15,14 @@
 // stream once the copy is done (event `ready`).  These two events per slot
 // take the place of the tutorial's barrier_all per chunk and of the
 // semaphores of the tpu-inference kernel.
+//
+// Calls on one plan are ordered with each other wherever they are enqueued:
+// every call ends by recording the plan's `done` event on the caller's
+// stream (after the internal streams have joined it), and the next call's
+// stream waits on that event before any of its work, so no call overwrites
+// ring slots or split-K partial sums a previous call on another stream is
+// still reading (the tutorial's rule that a slot is not refilled before the
+// chunk that reads it has been consumed).
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -95,9 +103,49 @@ int validate(int N, int64_t m_s, int64_t k, int64_t n, int dtype, int rt) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-int64_t lda_of(const agmm_plan* p);
-int64_t ldb_of(const agmm_plan* p);
-int64_t ldc_of(const agmm_plan* p);
+// What the caller can set (agmm_plan_set_int keys).
+struct Settings {
+  int variant = AGMM_VARIANT_AUTO;
+  int pvalue = 2;
+  int nbuf = 2;
+  int tile = -1;          // -1: automatic
+  int splits = 0;         // 0: automatic
+  int local_shard = 0;
+  int order = 0;
+  int group_m = 0;        // 0: chosen per launch shape (pick_group_m)
+  int xcd_remap = 1;
+  int copy_wgs = 0;
+  int skinny_shape = -1;  // tile shape of the whole-k skinny kernel; -1 automatic
+  int copy_engine = 0;    // copies beside a GEMM: 0 gather kernel (CUs), 1 SDMA engines
+  int64_t lda = 0, ldb = 0, ldc = 0;   // element strides between rows (0: dense)
+  int gemm_streams = 2;   // staged: chunk GEMMs alternate over this many streams (1 or 2)
+  int local_first = 0;    // staged: the local shard's rows first, straight from its buffer
+  int debug_keep_slots = 0;
+};
+
+// Everything derived from the problem and the settings.
+struct Layout {
+  int variant_used = AGMM_VARIANT_FUSED;
+  int tile_used = agmm::kTile256x256;
+  int bm = 256, bn = 256;
+  int skinny_shape_used = 5;
+  int64_t rows_per_chunk = 0;
+  int num_chunks = 1;
+  int nslots = 0;
+  int splits_used = 1;
+  int64_t k_per_split = 0;
+  size_t slot_bytes = 0, ring_bytes = 0, part_bytes = 0;
+  std::vector<int32_t> h_order;     // concatenated per-chunk row-block orders
+  std::vector<int64_t> order_off;   // offset of chunk c's table
+  std::vector<int32_t> order_len;
+
+  static size_t up(size_t x) { return (x + 255) & ~size_t(255); }
+  size_t order_bytes() const { return h_order.size() * sizeof(int32_t); }
+  size_t total_bytes() const { return up(ring_bytes) + up(part_bytes) + up(order_bytes()); }
+};
+
+// Where the plan's previous call recorded its `done` event.
+enum DoneState { kDoneNone = 0, kDoneEager = 1, kDoneCaptured = 2 };
 
 }  // namespace
 
@@ -109,56 +157,34 @@ struct agmm_plan {
   int64_t m_s = 0, k = 0, n = 0, m = 0;
   int dtype = 0;
   int rt = 0;
-  // settings
-  int variant = AGMM_VARIANT_AUTO;
-  int pvalue = 2;
-  int nbuf = 2;
-  int tile = -1;  // -1: auto
-  int splits = 0; // 0: auto
-  int local_shard = 0;
-  int order = 0;
-  int group_m = 0;  // 0: chosen per launch shape (pick_group_m)
-  int xcd_remap = 1;
-  int copy_wgs = 0;
-  int skinny_shape = -1;  // tile shape of the whole-k skinny kernel (launch_skinny_fullk); -1 auto
-  int skinny_shape_used = 5;
-  int copy_engine = 0;   // copies beside a GEMM: 0 gather kernel (CUs), 1 SDMA engines
-  // element strides between rows of the caller's buffers (0: dense)
-  int64_t lda = 0, ldb = 0, ldc = 0;
-  int gemm_streams = 2;   // staged: chunk GEMMs alternate over this many streams (1 or 2)
-  int local_first = 0;    // staged: the local shard's rows first, straight from its buffer
-  int debug_keep_slots = 0;
-  // derived
-  int variant_used = AGMM_VARIANT_FUSED;
-  int tile_used = agmm::kTile256x256;
-  int bm = 256, bn = 256;
-  int64_t rows_per_chunk = 0;
-  int num_chunks = 1;
-  int nslots = 0;
-  int splits_used = 1;
-  int64_t k_per_split = 0;
-  // device resources
+  Settings s;
+  Layout L;
+  // device resources: one allocation, 256-byte aligned pieces
   char* ws = nullptr;
-  size_t ws_bytes = 0;
+  size_t ws_cap = 0;
   char* ring = nullptr;
-  size_t slot_bytes = 0;
   float* partials = nullptr;
   int32_t* d_order = nullptr;
   // last automatic group_m choice, keyed by the launch's block counts
   int64_t group_key_rb = -1, group_key_cb = -1;
   int group_auto = 4;
-  std::vector<int32_t> h_order;     // concatenated per-chunk orders
-  std::vector<int64_t> order_off;   // offset of chunk c's table
-  std::vector<int32_t> order_len;
   hipStream_t copy_stream = nullptr;
   hipStream_t compute2 = nullptr;   // second GEMM stream: staged chunks alternate
-  hipEvent_t ev_entry = nullptr;
-  hipEvent_t ev_side = nullptr;   // end of a side gather on the copy stream
-  hipEvent_t ev_c2 = nullptr;     // end of the second GEMM stream's chunks
+  hipEvent_t ev_entry = nullptr;    // start of a call on the caller's stream
+  hipEvent_t ev_side = nullptr;     // end of the copy stream's work
+  hipEvent_t ev_c2 = nullptr;       // end of the second GEMM stream's work
+  hipEvent_t ev_done = nullptr;     // end of the plan's previous call
   std::vector<hipEvent_t> ev_ready, ev_free;
+  // ordering between calls
+  int done_state = kDoneNone;
+  unsigned long long done_capture_id = 0;
+  hipStream_t done_stream = nullptr;
+  bool captured = false;            // some call was captured into a graph
+  int broken = AGMM_OK;             // status that left the plan unusable, or AGMM_OK
+  std::string broken_msg;
   // timing
   bool timing = false;
-  std::vector<hipEvent_t> tev;  // 2 * kTimingPairs
+  std::vector<hipEvent_t> tev;      // 2 * kTimingPairs
   int tev_used = 0;
   std::mutex mu;
 };
@@ -167,14 +193,14 @@ namespace {
 
 bool is_f32(const agmm_plan* p) { return p->dtype == AGMM_FP32; }
 
-// Tile choice for the MFMA path: fewest "tile waves" weighted by the
-// per-tile efficiency of the larger shapes.
-int64_t lda_of(const agmm_plan* p) { return p->lda ? p->lda : p->k; }
-int64_t ldb_of(const agmm_plan* p) { return p->ldb ? p->ldb : (p->rt ? p->k : p->n); }
-int64_t ldc_of(const agmm_plan* p) { return p->ldc ? p->ldc : p->n; }
+int64_t lda_of(const agmm_plan* p) { return p->s.lda ? p->s.lda : p->k; }
+int64_t ldb_of(const agmm_plan* p) { return p->s.ldb ? p->s.ldb : (p->rt ? p->k : p->n); }
+int64_t ldc_of(const agmm_plan* p) { return p->s.ldc ? p->s.ldc : p->n; }
 
-int choose_tile(const agmm_plan* p, int64_t m) {
-  if (p->tile >= 0) return p->tile;
+// Tile choice for the MFMA path: fewest rounds of workgroups over the CUs,
+// weighted by the per-tile efficiency of the larger shapes.
+int choose_tile(const agmm_plan* p, const Settings& s, int64_t m) {
+  if (s.tile >= 0) return s.tile;
   struct Cand { int cfg; double eff; };
   // The 256x256 and 128x128 tiles run as the 64-deep part ring on 16x16x32
   // MFMAs unless k is short (its k-tiles would then be mostly padding).
@@ -236,16 +262,16 @@ int pick_group_m(int64_t nrb, int64_t ncb) {
 
 // Row-block visit order for a launch covering `groups` groups of `rpg` rows
 // each, whose position t inside a group is shard row `row_off + t`.
-void ring_order(const agmm_plan* p, int64_t rpg, int64_t row_off, int bm, int order_mode,
+void ring_order(const agmm_plan* p, const Settings& s, int64_t rpg, int64_t row_off, int bm,
                 std::vector<int32_t>& out) {
   const int64_t rows = rpg * p->N;
   const int64_t nrb = cdiv(rows, bm);
   out.resize(nrb);
   for (int64_t b = 0; b < nrb; ++b) out[b] = (int32_t)b;
-  if (order_mode != 0 || p->N == 1) return;
+  if (s.order != 0 || p->N == 1) return;
   const int64_t half = (p->m_s + 1) / 2;  // first half of a shard: rows [0, half)
   std::vector<int64_t> key(nrb, 0);
-  const int64_t N = p->N, r0 = p->local_shard;
+  const int64_t N = p->N, r0 = s.local_shard;
   for (int64_t b = 0; b < nrb; ++b) {
     int64_t kmax = -1;
     const int64_t lo = b * bm, hi = std::min(rows, lo + bm);
@@ -261,20 +287,13 @@ void ring_order(const agmm_plan* p, int64_t rpg, int64_t row_off, int bm, int or
   std::stable_sort(out.begin(), out.end(), [&](int32_t a, int32_t b) { return key[a] < key[b]; });
 }
 
-void free_resources(agmm_plan* p) {
-  if (p->ws) hipFree(p->ws);
-  p->ws = nullptr;
-  p->ws_bytes = 0;
-  p->ring = nullptr;
-  p->partials = nullptr;
-  p->d_order = nullptr;
-}
-
-// (Re)derive everything from the settings and (re)allocate the workspace.
-int configure(agmm_plan* p) {
+// Derive the layout of a plan from its problem and the settings: variant,
+// tiles, chunks, split-K, sizes and tile orders.  Host only; touches
+// nothing of the plan.
+int derive(const agmm_plan* p, const Settings& s, Layout& L) {
   const int64_t e = elem_bytes(p->dtype);
   // variant
-  int v = p->variant;
+  int v = s.variant;
   if (v == AGMM_VARIANT_AUTO) {
     if (is_f32(p)) v = AGMM_VARIANT_FUSED;
     else if (p->m <= 256) v = AGMM_VARIANT_SKINNY;
@@ -284,67 +303,65 @@ int configure(agmm_plan* p) {
   if ((v == AGMM_VARIANT_STAGED || v == AGMM_VARIANT_UNFUSED) && (p->k * e) % 16 != 0)
     return set_err(AGMM_ERR_UNSUPPORTED,
                    "the gather copy needs 16-byte rows (k * elem_bytes %% 16 == 0)");
-  p->variant_used = v;
+  L.variant_used = v;
 
   // tiles
+  if (!is_f32(p) && s.tile >= 0 && agmm::tile_needs_bt(s.tile) && !p->rt)
+    return set_err(AGMM_ERR_UNSUPPORTED, "tile %d needs B stored n x k (rhs_transpose)", s.tile);
   if (is_f32(p)) {
-    p->tile_used = -1;
-    p->bm = p->bn = 64;
-  } else if (v == AGMM_VARIANT_SKINNY) {
-    // B stored n x k, m <= 128: the whole-k skinny kernel (one launch, no
-    // partial sums).  Measured per call in graph replay (us, whole-k against
-    // the best split-K tile): m 128, n 1792, k 4096: 11.8 / 16.4; m 128,
-    // n 512: 8.6 / 14.4; m 64, n 3584, k 8192: 21.6 / 32.3.  For m 256 the
-    // split-K 128x64 part ring was fastest (19.7 against 20.7 whole-k and
-    // 24.8 for the 256x128 tile).  Split-K tiles put all of m in one row
-    // block and split k over narrow column blocks, so that enough
-    // workgroups stream B.
-    if (p->tile >= 0) p->tile_used = p->tile;
-    else if (p->rt) p->tile_used = p->m <= 128 ? agmm::kTileSkinny : agmm::kTile128x64r5;
-    else p->tile_used = p->m <= 128 ? agmm::kTile128x128 : agmm::kTile256x128;
-    p->bm = agmm::tile_bm(p->tile_used);
-    p->bn = agmm::tile_bn(p->tile_used);
-  } else if (v == AGMM_VARIANT_STAGED) {
-    // tile chosen for one chunk's launch (pvalue tile-rows of every shard)
-    const int64_t chunk_m = (int64_t)p->N * std::min<int64_t>(p->m_s, (int64_t)p->pvalue * 256);
-    p->tile_used = choose_tile(p, chunk_m);
-    p->bm = agmm::tile_bm(p->tile_used);
-    p->bn = agmm::tile_bn(p->tile_used);
+    L.tile_used = -1;
+    L.bm = L.bn = 64;
   } else {
-    p->tile_used = choose_tile(p, p->m);
-    p->bm = agmm::tile_bm(p->tile_used);
-    p->bn = agmm::tile_bn(p->tile_used);
+    if (v == AGMM_VARIANT_SKINNY) {
+      // B stored n x k, m <= 128: the whole-k skinny kernel (one launch, no
+      // partial sums).  Measured per call in graph replay (us, whole-k against
+      // the best split-K tile): m 128, n 1792, k 4096: 11.8 / 16.4; m 128,
+      // n 512: 8.6 / 14.4; m 64, n 3584, k 8192: 21.6 / 32.3.  For m 256 the
+      // split-K 128x64 part ring was fastest (19.7 against 20.7 whole-k and
+      // 24.8 for the 256x128 tile).  Split-K tiles put all of m in one row
+      // block and split k over narrow column blocks, so that enough
+      // workgroups stream B.
+      if (s.tile >= 0) L.tile_used = s.tile;
+      else if (p->rt) L.tile_used = p->m <= 128 ? agmm::kTileSkinny : agmm::kTile128x64r5;
+      else L.tile_used = p->m <= 128 ? agmm::kTile128x128 : agmm::kTile256x128;
+    } else if (v == AGMM_VARIANT_STAGED) {
+      // tile chosen for one chunk's launch (pvalue tile-rows of every shard)
+      const int64_t chunk_m = (int64_t)p->N * std::min<int64_t>(p->m_s, (int64_t)s.pvalue * 256);
+      L.tile_used = choose_tile(p, s, chunk_m);
+    } else {
+      L.tile_used = choose_tile(p, s, p->m);
+    }
+    L.bm = agmm::tile_bm(L.tile_used);
+    L.bn = agmm::tile_bn(L.tile_used);
   }
 
   // whole-k skinny tile shape: 32 x 32 with 8 waves (2-3% faster than 4 on
   // four skinny shapes) unless 64 x 16 gives more workgroups (small m: m 32,
   // n 1024, k 4096 measured 10.1 us against 10.9)
-  if (p->skinny_shape >= 0) {
-    p->skinny_shape_used = p->skinny_shape;
+  if (s.skinny_shape >= 0) {
+    L.skinny_shape_used = s.skinny_shape;
   } else {
     const int64_t t32 = cdiv(p->m, 32) * cdiv(p->n, 32), t64 = cdiv(p->m, 64) * cdiv(p->n, 16);
-    p->skinny_shape_used = t64 > t32 ? 0 : 5;
+    L.skinny_shape_used = t64 > t32 ? 0 : 5;
   }
-  if (!is_f32(p) && p->tile_used == agmm::kTileSkinny && !p->rt)
-    return set_err(AGMM_ERR_UNSUPPORTED, "tile %d (skinny, whole k) needs B stored n x k", agmm::kTileSkinny);
 
-  // chunking (staged) / split-K (skinny)
-  p->rows_per_chunk = p->m_s;
-  p->num_chunks = 1;
-  p->nslots = 0;
-  p->splits_used = 1;
-  p->k_per_split = p->k;
-  size_t ring_bytes = 0, part_bytes = 0;
+  // chunking (staged) / split-K
+  L.rows_per_chunk = p->m_s;
+  L.num_chunks = 1;
+  L.nslots = 0;
+  L.splits_used = 1;
+  L.k_per_split = p->k;
+  L.ring_bytes = L.part_bytes = L.slot_bytes = 0;
   if (v == AGMM_VARIANT_STAGED) {
-    p->rows_per_chunk = std::min<int64_t>(p->m_s, (int64_t)p->pvalue * p->bm);
-    p->num_chunks = (int)cdiv(p->m_s, p->rows_per_chunk);
-    p->nslots = p->debug_keep_slots ? p->num_chunks : std::min(p->nbuf, p->num_chunks);
-    p->slot_bytes = (size_t)p->N * p->rows_per_chunk * p->k * e;
-    ring_bytes = p->slot_bytes * p->nslots;
+    L.rows_per_chunk = std::min<int64_t>(p->m_s, (int64_t)s.pvalue * L.bm);
+    L.num_chunks = (int)cdiv(p->m_s, L.rows_per_chunk);
+    L.nslots = s.debug_keep_slots ? L.num_chunks : std::min(s.nbuf, L.num_chunks);
+    L.slot_bytes = (size_t)p->N * L.rows_per_chunk * p->k * e;
+    L.ring_bytes = L.slot_bytes * L.nslots;
   } else if (v == AGMM_VARIANT_UNFUSED) {
-    p->nslots = 1;
-    p->slot_bytes = (size_t)p->m * p->k * e;
-    ring_bytes = p->slot_bytes;
+    L.nslots = 1;
+    L.slot_bytes = (size_t)p->m * p->k * e;
+    L.ring_bytes = L.slot_bytes;
   }
   // split-K: skinny problems always, the other variants when one launch has
   // too few output tiles to give every CU a workgroup.  A power of two of k
@@ -353,10 +370,10 @@ int configure(agmm_plan* p) {
   // A staged plan's launches are its chunks, which run one after another on
   // the caller's stream and share one partials buffer.
   if (!is_f32(p)) {
-    const int64_t launch_m = v == AGMM_VARIANT_STAGED ? (int64_t)p->N * p->rows_per_chunk : p->m;
-    const int64_t tiles = cdiv(launch_m, p->bm) * cdiv(p->n, p->bn);
-    int64_t want = p->splits;
-    if (p->tile_used == agmm::kTileSkinny) want = 1;   // whole k per workgroup, no partials
+    const int64_t launch_m = v == AGMM_VARIANT_STAGED ? (int64_t)p->N * L.rows_per_chunk : p->m;
+    const int64_t tiles = cdiv(launch_m, L.bm) * cdiv(p->n, L.bn);
+    int64_t want = s.splits;
+    if (L.tile_used == agmm::kTileSkinny) want = 1;   // whole k per workgroup, no partials
     if (want <= 0) {
       want = 1;
       // workgroup slots: the CUs times the workgroups of this tile one CU
@@ -366,7 +383,7 @@ int configure(agmm_plan* p) {
       // 34.9 us on 4x512x4096->1024)
       const int64_t slots = v == AGMM_VARIANT_SKINNY
                                 ? p->cu_count
-                                : (int64_t)p->cu_count * agmm::tile_occ(p->tile_used);
+                                : (int64_t)p->cu_count * agmm::tile_occ(L.tile_used);
       if (v == AGMM_VARIANT_SKINNY || 2 * tiles <= slots) {
         // long enough k ranges that the partial sums stay small next to the
         // operand traffic (skinny problems have no other way to fill the GPU)
@@ -375,55 +392,123 @@ int configure(agmm_plan* p) {
       }
     }
     want = std::max<int64_t>(1, std::min<int64_t>(want, cdiv(p->k, agmm::kTileBK)));
-    p->k_per_split = cdiv(cdiv(p->k, want), agmm::kTileBK) * agmm::kTileBK;
-    p->splits_used = (int)cdiv(p->k, p->k_per_split);
+    L.k_per_split = cdiv(cdiv(p->k, want), agmm::kTileBK) * agmm::kTileBK;
+    L.splits_used = (int)cdiv(p->k, L.k_per_split);
     // a staged plan's launches: its chunks and (local_first) the local shard's rows
     const int64_t part_m = v == AGMM_VARIANT_STAGED ? std::max<int64_t>(launch_m, p->m_s) : launch_m;
-    if (p->splits_used > 1) part_bytes = (size_t)p->splits_used * part_m * p->n * sizeof(float);
+    if (L.splits_used > 1) L.part_bytes = (size_t)L.splits_used * part_m * p->n * sizeof(float);
   }
 
   // tile orders (one table per chunk)
-  p->h_order.clear();
-  p->order_off.clear();
-  p->order_len.clear();
+  L.h_order.clear();
+  L.order_off.clear();
+  L.order_len.clear();
   std::vector<int32_t> tmp;
-  for (int c = 0; c < p->num_chunks; ++c) {
-    const int64_t rows_c = std::min<int64_t>(p->rows_per_chunk, p->m_s - (int64_t)c * p->rows_per_chunk);
-    ring_order(p, rows_c, (int64_t)c * p->rows_per_chunk, p->bm, p->order, tmp);
-    p->order_off.push_back((int64_t)p->h_order.size());
-    p->order_len.push_back((int32_t)tmp.size());
-    p->h_order.insert(p->h_order.end(), tmp.begin(), tmp.end());
+  for (int c = 0; c < L.num_chunks; ++c) {
+    const int64_t rows_c = std::min<int64_t>(L.rows_per_chunk, p->m_s - (int64_t)c * L.rows_per_chunk);
+    ring_order(p, s, rows_c, (int64_t)c * L.rows_per_chunk, L.bm, tmp);
+    L.order_off.push_back((int64_t)L.h_order.size());
+    L.order_len.push_back((int32_t)tmp.size());
+    L.h_order.insert(L.h_order.end(), tmp.begin(), tmp.end());
   }
-  const size_t order_bytes = p->h_order.size() * sizeof(int32_t);
+  return AGMM_OK;
+}
 
-  // one allocation, 256-byte aligned pieces
-  auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
-  const size_t total = up(ring_bytes) + up(part_bytes) + up(order_bytes);
-  free_resources(p);
-  if (total > 0) {
-    if (std::getenv("AGMM_TEST_FAIL_ALLOC"))
+// Wait until no enqueued work of the plan can still use its workspace.
+int wait_idle(agmm_plan* p) {
+  if (p->done_state == kDoneEager) {
+    const hipError_t err = hipEventSynchronize(p->ev_done);
+    if (err != hipSuccess) return hip_err(err, "hipEventSynchronize(done)");
+  }
+  return AGMM_OK;
+}
+
+int alloc_ws(agmm_plan* p, size_t bytes) {
+  if (bytes == 0) return AGMM_OK;
+  // test hook: AGMM_TEST_FAIL_ALLOC=<n> makes every workspace allocation of
+  // more than n bytes fail (n = 0 or 1: all of them)
+  if (const char* hook = std::getenv("AGMM_TEST_FAIL_ALLOC")) {
+    const long long limit = std::atoll(hook);
+    if (limit <= 1 || (long long)bytes > limit)
       return set_err(AGMM_ERR_OOM, "workspace allocation of %zu bytes failed (forced by test hook)",
-                     total);
-    hipError_t err = hipMalloc(&p->ws, total);
-    if (err != hipSuccess) {
-      p->ws = nullptr;
-      (void)hipGetLastError();
-      return set_err(AGMM_ERR_OOM, "workspace allocation of %zu bytes failed: %s", total,
-                     hipGetErrorString(err));
-    }
-    p->ws_bytes = total;
-    char* q = p->ws;
-    if (ring_bytes) { p->ring = q; q += up(ring_bytes); }
-    if (part_bytes) { p->partials = reinterpret_cast<float*>(q); q += up(part_bytes); }
-    if (order_bytes) {
-      p->d_order = reinterpret_cast<int32_t*>(q);
-      err = hipMemcpy(p->d_order, p->h_order.data(), order_bytes, hipMemcpyHostToDevice);
-      if (err != hipSuccess) return hip_err(err, "hipMemcpy(tile order)");
+                     bytes);
+  }
+  hipError_t err = hipMalloc(&p->ws, bytes);
+  if (err != hipSuccess) {
+    p->ws = nullptr;
+    (void)hipGetLastError();
+    return set_err(AGMM_ERR_OOM, "workspace allocation of %zu bytes failed: %s", bytes,
+                   hipGetErrorString(err));
+  }
+  p->ws_cap = bytes;
+  return AGMM_OK;
+}
+
+// Give the plan a new layout: derive it, make room in the workspace (the
+// existing allocation is kept when the new layout fits in it), then commit
+// the settings and layout and upload the tile-order tables.  On an error
+// before the commit the plan keeps its previous settings, layout and a
+// workspace of the previous size; if even that cannot be restored the plan
+// is marked unusable and every later call on it fails.
+int apply(agmm_plan* p, const Settings& s) {
+  Layout L;
+  int rc = derive(p, s, L);
+  if (rc != AGMM_OK) return rc;
+  rc = wait_idle(p);   // the previous call may still read the workspace
+  if (rc != AGMM_OK) return rc;
+  const size_t total = L.total_bytes();
+  if (total > p->ws_cap) {
+    const size_t old_cap = p->ws_cap;
+    if (p->ws) hipFree(p->ws);
+    p->ws = nullptr;
+    p->ws_cap = 0;
+    p->ring = nullptr;
+    p->partials = nullptr;
+    p->d_order = nullptr;
+    rc = alloc_ws(p, total);
+    if (rc != AGMM_OK) {
+      const int st = g_status;
+      const std::string msg = g_msg;
+      // Restore a workspace for the layout the plan still has.
+      if (alloc_ws(p, old_cap) != AGMM_OK) {
+        p->broken = st;
+        p->broken_msg = msg + "; the previous workspace could not be restored either";
+      } else {
+        char* q = p->ws;
+        if (p->L.ring_bytes) { p->ring = q; q += Layout::up(p->L.ring_bytes); }
+        if (p->L.part_bytes) { p->partials = reinterpret_cast<float*>(q); q += Layout::up(p->L.part_bytes); }
+        if (p->L.order_bytes()) {
+          p->d_order = reinterpret_cast<int32_t*>(q);
+          if (hipMemcpy(p->d_order, p->L.h_order.data(), p->L.order_bytes(), hipMemcpyHostToDevice) != hipSuccess) {
+            (void)hipGetLastError();
+            p->broken = AGMM_ERR_HIP;
+            p->broken_msg = msg + "; re-uploading the tile order failed";
+          }
+        }
+      }
+      return set_err(st, "%s", msg.c_str());
     }
   }
-
+  // commit
+  p->s = s;
+  p->L = std::move(L);
+  p->ring = nullptr;
+  p->partials = nullptr;
+  p->d_order = nullptr;
+  char* q = p->ws;
+  if (p->L.ring_bytes) { p->ring = q; q += Layout::up(p->L.ring_bytes); }
+  if (p->L.part_bytes) { p->partials = reinterpret_cast<float*>(q); q += Layout::up(p->L.part_bytes); }
+  if (p->L.order_bytes()) {
+    p->d_order = reinterpret_cast<int32_t*>(q);
+    const hipError_t err = hipMemcpy(p->d_order, p->L.h_order.data(), p->L.order_bytes(), hipMemcpyHostToDevice);
+    if (err != hipSuccess) {
+      p->broken = AGMM_ERR_HIP;
+      p->broken_msg = std::string("uploading the tile order failed: ") + hipGetErrorString(err);
+      return hip_err(err, "hipMemcpy(tile order)");
+    }
+  }
   // events for the ring
-  const size_t want_ev = (size_t)std::max(p->nslots, 1);
+  const size_t want_ev = (size_t)std::max(p->L.nslots, 1);
   while (p->ev_ready.size() < want_ev) {
     hipEvent_t a, b;
     hipError_t err = hipEventCreateWithFlags(&a, hipEventDisableTiming);
@@ -436,6 +521,52 @@ int configure(agmm_plan* p) {
   return ok();
 }
 
+// One call's view of the caller's stream.
+struct Call {
+  hipStream_t s = nullptr;
+  bool capturing = false;
+  unsigned long long capture_id = 0;
+};
+
+// Start a call: refuse an unusable plan, find out whether the stream is being
+// captured into a graph, and order the call after the plan's previous one.
+// Across a capture boundary (a call captured into a graph after eager calls,
+// or an eager call after a captured one) no event links them: waiting on an
+// event recorded on the other side of the boundary is not allowed while a
+// stream is capturing, and a captured call's work happens at each replay;
+// the caller's streams order graph replays against other work.
+int enter(agmm_plan* p, hipStream_t s, Call& c) {
+  if (p->broken != AGMM_OK) return set_err(p->broken, "plan is unusable: %s", p->broken_msg.c_str());
+  hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+  unsigned long long id = 0;
+  hipError_t err = hipStreamGetCaptureInfo(s, &st, &id);
+  if (err != hipSuccess) return hip_err(err, "hipStreamGetCaptureInfo");
+  if (st == hipStreamCaptureStatusInvalidated)
+    return set_err(AGMM_ERR_HIP, "the stream's graph capture has been invalidated");
+  c.s = s;
+  c.capturing = st == hipStreamCaptureStatusActive;
+  c.capture_id = c.capturing ? id : 0;
+  if (c.capturing) p->captured = true;
+  const bool linked = p->done_state == kDoneEager
+                          ? !c.capturing
+                          : (p->done_state == kDoneCaptured && c.capturing && p->done_capture_id == id);
+  if (linked && p->done_stream != s) {
+    err = hipStreamWaitEvent(s, p->ev_done, 0);
+    if (err != hipSuccess) return hip_err(err, "hipStreamWaitEvent(done)");
+  }
+  return AGMM_OK;
+}
+
+// End a call that enqueued work: every internal stream has joined `c.s`.
+int leave(agmm_plan* p, const Call& c) {
+  const hipError_t err = hipEventRecord(p->ev_done, c.s);
+  if (err != hipSuccess) return hip_err(err, "hipEventRecord(done)");
+  p->done_state = c.capturing ? kDoneCaptured : kDoneEager;
+  p->done_capture_id = c.capture_id;
+  p->done_stream = c.s;
+  return AGMM_OK;
+}
+
 agmm::RowMap shard_rows(const agmm_plan* p, const void* const* shards) {
   agmm::RowMap r{};
   for (int g = 0; g < p->N; ++g) r.a_group[g] = shards[g];
@@ -443,6 +574,17 @@ agmm::RowMap shard_rows(const agmm_plan* p, const void* const* shards) {
   r.rows_per_group = (int32_t)p->m_s;
   r.num_groups = p->N;
   r.c_group_rows = p->m_s;
+  r.c_row_off = 0;
+  return r;
+}
+
+agmm::RowMap dense_rows(const void* a, int64_t rows, int64_t ld) {
+  agmm::RowMap r{};
+  r.a_group[0] = a;
+  r.a_ld = ld;
+  r.rows_per_group = (int32_t)rows;
+  r.num_groups = 1;
+  r.c_group_rows = 0;
   r.c_row_off = 0;
   return r;
 }
@@ -458,10 +600,10 @@ agmm::GemmProblem base_problem(agmm_plan* p, const agmm::RowMap& rows, int64_t m
   g.ldb = ldb_of(p);
   g.c = C;
   g.ldc = ldc_of(p);
-  g.order.num_rb = (int32_t)cdiv(m_launch, p->bm);
-  g.order.num_cb = (int32_t)cdiv(p->n, p->bn);
-  if (p->group_m > 0) {
-    g.order.group_m = p->group_m;
+  g.order.num_rb = (int32_t)cdiv(m_launch, p->L.bm);
+  g.order.num_cb = (int32_t)cdiv(p->n, p->L.bn);
+  if (p->s.group_m > 0) {
+    g.order.group_m = p->s.group_m;
   } else {
     if (p->group_key_rb != g.order.num_rb || p->group_key_cb != g.order.num_cb) {
       p->group_auto = pick_group_m(g.order.num_rb, g.order.num_cb);
@@ -470,33 +612,38 @@ agmm::GemmProblem base_problem(agmm_plan* p, const agmm::RowMap& rows, int64_t m
     }
     g.order.group_m = p->group_auto;
   }
-  g.order.xcd_remap = p->xcd_remap;
+  g.order.xcd_remap = p->s.xcd_remap;
   g.order.rb_order = nullptr;
-  if (chunk >= 0 && p->d_order && chunk < (int)p->order_off.size() &&
-      p->order_len[chunk] == g.order.num_rb)
-    g.order.rb_order = p->d_order + p->order_off[chunk];
+  if (chunk >= 0 && p->d_order && chunk < (int)p->L.order_off.size() &&
+      p->L.order_len[chunk] == g.order.num_rb)
+    g.order.rb_order = p->d_order + p->L.order_off[chunk];
   g.splits = 1;
   g.k_per_split = (int32_t)p->k;
   return g;
 }
 
-// Whole-problem launches (not the staged chunks) use the plan's split-K.
+// Split-K for a launch: the plan's k ranges, when its partials buffer holds
+// this launch's [splits][m][n] sums (a launch larger than the ones the plan
+// sized it for, e.g. agmm_run_gathered on a staged plan, runs unsplit).
 void with_splits(const agmm_plan* p, agmm::GemmProblem& g) {
-  if (p->splits_used > 1) {
-    g.splits = p->splits_used;
-    g.k_per_split = (int32_t)p->k_per_split;
+  if (p->L.splits_used > 1 && p->partials &&
+      (size_t)p->L.splits_used * (size_t)g.m * (size_t)p->n * sizeof(float) <= p->L.part_bytes) {
+    g.splits = p->L.splits_used;
+    g.k_per_split = (int32_t)p->L.k_per_split;
     g.partials = p->partials;
   }
 }
 
-int launch_gemm(agmm_plan* p, agmm::GemmProblem& g, hipStream_t s) {
-  const bool timed = p->timing && p->tev_used + 2 <= (int)p->tev.size();
+int launch_gemm(agmm_plan* p, const Call& c, agmm::GemmProblem& g, hipStream_t s) {
+  // timing events are recorded eagerly only (inside a capture they would
+  // time nothing)
+  const bool timed = p->timing && !c.capturing && p->tev_used + 2 <= (int)p->tev.size();
   if (timed) hipEventRecord(p->tev[p->tev_used], s);
   hipError_t err;
   if (is_f32(p)) err = agmm::launch_gemm_f32(g, p->rt != 0, s);
-  else if (p->tile_used == agmm::kTileSkinny)
-    err = agmm::launch_skinny_fullk(g, p->dtype, p->skinny_shape_used, s);
-  else err = agmm::launch_gemm_mfma(g, p->tile_used, p->dtype, p->rt != 0, s);
+  else if (p->L.tile_used == agmm::kTileSkinny)
+    err = agmm::launch_skinny_fullk(g, p->dtype, p->L.skinny_shape_used, s);
+  else err = agmm::launch_gemm_mfma(g, p->L.tile_used, p->dtype, p->rt != 0, s);
   if (err != hipSuccess) return hip_err(err, "GEMM launch");
   if (timed) {
     hipEventRecord(p->tev[p->tev_used + 1], s);
@@ -560,44 +707,34 @@ int gather_chunk_sdma(agmm_plan* p, const void* const* shards, int64_t row0, int
 // in the staged pipeline beside the chunk GEMMs the chunks arrive too late
 // (workload 5: 5.26 ms against 3.47 ms with the kernel copy), so the kernel
 // copy stays the default.
-bool copy_on_sdma(const agmm_plan* p, hipStream_t caller, bool overlaps) {
-  if (p->copy_engine != 1 || !overlaps || lda_of(p) != p->k) return false;
-  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-  if (hipStreamIsCapturing(caller, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) {
-    (void)hipGetLastError();
-    return false;
-  }
-  return true;
+bool copy_on_sdma(const agmm_plan* p, const Call& c, bool overlaps) {
+  return p->s.copy_engine == 1 && overlaps && lda_of(p) == p->k && !c.capturing;
 }
 
-// Staged pipeline.  With `gathered` == nullptr the chunks go through the
-// plan's ring of slots; otherwise each chunk is copied to its final place in
-// the caller's [m, k] buffer (no slot is reused, so no copy waits for a GEMM).
-int run_staged(agmm_plan* p, const void* const* shards, const void* B, void* C, hipStream_t s,
-               void* gathered = nullptr) {
-  hipError_t err = hipEventRecord(p->ev_entry, s);
-  if (err != hipSuccess) return hip_err(err, "hipEventRecord");
-  err = hipStreamWaitEvent(p->copy_stream, p->ev_entry, 0);
-  if (err != hipSuccess) return hip_err(err, "hipStreamWaitEvent");
-  // Odd chunks' GEMMs run on a second stream, so the workgroups of chunk c+1
-  // take the CUs chunk c's workgroups leave (each chunk's launch is usually
-  // a partial round); only the ring-slot events order them.  With split-K the
-  // chunks share one partials buffer and stay on the caller's stream.
-  // The local shard's rows need no copy (tpu-inference `all_gather_matmul`:
-  // a device multiplies its own x block while the ring brings the others):
-  // with local_first their GEMM runs first, from the shard buffer, on the
-  // caller's stream beside chunk 0's copy, and the chunk GEMMs cover the
-  // other shards' rows only.
-  // Off by default: measured neutral on 8x1024x8192 -> 3584 (435 us), 1%
-  // faster on 8x4096x8192 -> 7168, slower where the launches are small
-  // (4x512x4096 -> 1024: 62 -> 75 us; with one chunk, 28 -> 43 us on
-  // 8x16x4096 -> 1792, so it is never used with a single chunk).
-  const bool local_first = p->local_first && p->N > 1 && p->num_chunks > 1;
-  const bool alt = p->gemm_streams == 2 && p->splits_used == 1 && (p->num_chunks > 1 || local_first);
-  if (alt && (err = hipStreamWaitEvent(p->compute2, p->ev_entry, 0)) != hipSuccess)
-    return hip_err(err, "hipStreamWaitEvent");
+// Fork: `other` waits for everything enqueued so far on the caller's stream.
+int fork_to(agmm_plan* p, const Call& c, hipStream_t other) {
+  hipError_t err = hipEventRecord(p->ev_entry, c.s);
+  if (err == hipSuccess) err = hipStreamWaitEvent(other, p->ev_entry, 0);
+  if (err != hipSuccess) return hip_err(err, "stream fork");
+  return AGMM_OK;
+}
+
+// Join: the caller's stream waits for everything enqueued so far on `other`.
+int join_from(const Call& c, hipStream_t other, hipEvent_t ev) {
+  hipError_t err = hipEventRecord(ev, other);
+  if (err == hipSuccess) err = hipStreamWaitEvent(c.s, ev, 0);
+  if (err != hipSuccess) return hip_err(err, "stream join");
+  return AGMM_OK;
+}
+
+// The chunk loop of the staged pipeline (the streams are forked and joined
+// by run_staged).
+int staged_chunks(agmm_plan* p, const Call& c, const void* const* shards, const void* B, void* C,
+                  void* gathered, bool alt, bool local_first) {
+  hipStream_t s = c.s;
+  hipError_t err;
   const int64_t e = elem_bytes(p->dtype);
-  const int r0 = p->local_shard;
+  const int r0 = p->s.local_shard;
   if (local_first) {
     agmm::RowMap rm{};
     rm.a_group[0] = shards[r0];
@@ -608,18 +745,18 @@ int run_staged(agmm_plan* p, const void* const* shards, const void* B, void* C, 
     rm.c_row_off = (int64_t)r0 * p->m_s;
     agmm::GemmProblem g = base_problem(p, rm, p->m_s, B, C, -1);
     with_splits(p, g);
-    const int rc = launch_gemm(p, g, s);
+    const int rc = launch_gemm(p, c, g, s);
     if (rc != AGMM_OK) return rc;
   }
-  for (int c = 0; c < p->num_chunks; ++c) {
-    const int slot = c % p->nslots;
-    const int64_t row0 = (int64_t)c * p->rows_per_chunk;
-    const int64_t rows_c = std::min<int64_t>(p->rows_per_chunk, p->m_s - row0);
+  for (int ch = 0; ch < p->L.num_chunks; ++ch) {
+    const int slot = ch % p->L.nslots;
+    const int64_t row0 = (int64_t)ch * p->L.rows_per_chunk;
+    const int64_t rows_c = std::min<int64_t>(p->L.rows_per_chunk, p->m_s - row0);
     // destination of shard g's rows of this chunk: dst + g * dst_group_rows rows
     char* dst = gathered ? static_cast<char*>(gathered) + (size_t)row0 * p->k * e
-                         : p->ring + (size_t)slot * p->slot_bytes;
+                         : p->ring + (size_t)slot * p->L.slot_bytes;
     const int64_t dst_group_rows = gathered ? p->m_s : rows_c;
-    if (!gathered && c >= p->nslots) {
+    if (!gathered && ch >= p->L.nslots) {
       err = hipStreamWaitEvent(p->copy_stream, p->ev_free[slot], 0);
       if (err != hipSuccess) return hip_err(err, "hipStreamWaitEvent(free)");
     }
@@ -630,17 +767,17 @@ int run_staged(agmm_plan* p, const void* const* shards, const void* B, void* C, 
     // -> ~3180 us on 8x4096x8192 -> 7168, pvalue 2, two slots).  With
     // copy_engine 1 the copies after the first go to the SDMA engines.
     int rc;
-    if (copy_on_sdma(p, s, c > 0)) {
+    if (copy_on_sdma(p, c, ch > 0)) {
       rc = gather_chunk_sdma(p, shards, row0, rows_c, dst, dst_group_rows, p->copy_stream);
     } else {
-      rc = gather_chunk(p, shards, row0, rows_c, dst, dst_group_rows, p->copy_wgs, p->copy_stream);
+      rc = gather_chunk(p, shards, row0, rows_c, dst, dst_group_rows, p->s.copy_wgs, p->copy_stream);
     }
     if (rc != AGMM_OK) return rc;
     if ((err = hipEventRecord(p->ev_ready[slot], p->copy_stream)) != hipSuccess)
       return hip_err(err, "hipEventRecord(ready)");
     // chunks alternate streams; with local_first chunk 0 takes the second
     // stream, beside the local GEMM on the caller's
-    hipStream_t cs = (alt && ((c & 1) == (local_first ? 0 : 1))) ? p->compute2 : s;
+    hipStream_t cs = (alt && ((ch & 1) == (local_first ? 0 : 1))) ? p->compute2 : s;
     if ((err = hipStreamWaitEvent(cs, p->ev_ready[slot], 0)) != hipSuccess)
       return hip_err(err, "hipStreamWaitEvent(ready)");
     if (!local_first) {
@@ -651,9 +788,9 @@ int run_staged(agmm_plan* p, const void* const* shards, const void* B, void* C, 
       rm.num_groups = p->N;
       rm.c_group_rows = p->m_s;
       rm.c_row_off = row0;
-      agmm::GemmProblem g = base_problem(p, rm, rows_c * p->N, B, C, c);
+      agmm::GemmProblem g = base_problem(p, rm, rows_c * p->N, B, C, ch);
       with_splits(p, g);
-      rc = launch_gemm(p, g, cs);
+      rc = launch_gemm(p, c, g, cs);
       if (rc != AGMM_OK) return rc;
     } else {
       // the other shards, as the runs [0, r0) and (r0, N) of consecutive
@@ -671,18 +808,86 @@ int run_staged(agmm_plan* p, const void* const* shards, const void* B, void* C, 
         rm.c_row_off = (int64_t)lo * p->m_s + row0;
         agmm::GemmProblem g = base_problem(p, rm, rows_c * cnt, B, C, -1);
         with_splits(p, g);
-        rc = launch_gemm(p, g, cs);
+        rc = launch_gemm(p, c, g, cs);
         if (rc != AGMM_OK) return rc;
       }
     }
     if (!gathered && (err = hipEventRecord(p->ev_free[slot], cs)) != hipSuccess)
       return hip_err(err, "hipEventRecord(free)");
   }
+  return AGMM_OK;
+}
+
+// Staged pipeline.  With `gathered` == nullptr the chunks go through the
+// plan's ring of slots; otherwise each chunk is copied to its final place in
+// the caller's [m, k] buffer (no slot is reused, so no copy waits for a GEMM).
+// The copy stream (and the second GEMM stream) fork from the caller's stream
+// at entry and always join it again before the call returns.
+int run_staged(agmm_plan* p, const Call& c, const void* const* shards, const void* B, void* C,
+               void* gathered = nullptr) {
+  // Odd chunks' GEMMs run on a second stream, so the workgroups of chunk c+1
+  // take the CUs chunk c's workgroups leave (each chunk's launch is usually
+  // a partial round); only the ring-slot events order them.  With split-K the
+  // chunks share one partials buffer and stay on the caller's stream.
+  // The local shard's rows need no copy (tpu-inference `all_gather_matmul`:
+  // a device multiplies its own x block while the ring brings the others):
+  // with local_first their GEMM runs first, from the shard buffer, on the
+  // caller's stream beside chunk 0's copy, and the chunk GEMMs cover the
+  // other shards' rows only.
+  // Off by default: measured neutral on 8x1024x8192 -> 3584 (435 us), 1%
+  // faster on 8x4096x8192 -> 7168, slower where the launches are small
+  // (4x512x4096 -> 1024: 62 -> 75 us; with one chunk, 28 -> 43 us on
+  // 8x16x4096 -> 1792, so it is never used with a single chunk).
+  const bool local_first = p->s.local_first && p->N > 1 && p->L.num_chunks > 1;
+  const bool alt = p->s.gemm_streams == 2 && p->L.splits_used == 1 && (p->L.num_chunks > 1 || local_first);
+  int rc = fork_to(p, c, p->copy_stream);
+  if (rc != AGMM_OK) return rc;
   if (alt) {
-    if ((err = hipEventRecord(p->ev_c2, p->compute2)) != hipSuccess) return hip_err(err, "hipEventRecord");
-    if ((err = hipStreamWaitEvent(s, p->ev_c2, 0)) != hipSuccess) return hip_err(err, "stream join");
+    const hipError_t err = hipStreamWaitEvent(p->compute2, p->ev_entry, 0);
+    if (err != hipSuccess) rc = hip_err(err, "hipStreamWaitEvent");
   }
-  return ok();
+  if (rc == AGMM_OK) rc = staged_chunks(p, c, shards, B, C, gathered, alt, local_first);
+  // join whatever was enqueued, also after an error
+  const int rj = join_from(c, p->copy_stream, p->ev_side);
+  const int rj2 = alt ? join_from(c, p->compute2, p->ev_c2) : AGMM_OK;
+  if (rc != AGMM_OK) return rc;
+  return rj != AGMM_OK ? rj : rj2;
+}
+
+// agmm_run's work, after enter().
+int run_plan(agmm_plan* p, const Call& c, const void* const* shard_ptrs, const void* B, void* C) {
+  int rc;
+  switch (p->L.variant_used) {
+    case AGMM_VARIANT_FUSED:
+    case AGMM_VARIANT_SKINNY: {
+      agmm::GemmProblem g = base_problem(p, shard_rows(p, shard_ptrs), p->m, B, C, 0);
+      with_splits(p, g);
+      return launch_gemm(p, c, g, c.s);
+    }
+    case AGMM_VARIANT_UNFUSED: {
+      rc = gather_chunk(p, shard_ptrs, 0, p->m_s, p->ring, p->m_s, 0, c.s);
+      if (rc != AGMM_OK) return rc;
+      agmm::GemmProblem g = base_problem(p, dense_rows(p->ring, p->m, p->k), p->m, B, C, -1);
+      with_splits(p, g);
+      return launch_gemm(p, c, g, c.s);
+    }
+    case AGMM_VARIANT_STAGED:
+      return run_staged(p, c, shard_ptrs, B, C);
+    default:
+      return set_err(AGMM_ERR_INVALID_ARG, "plan has no valid variant");
+  }
+}
+
+// A call that enqueues work: enter, body, leave.
+template <class F>
+int guarded(agmm_plan* p, hipStream_t s, F&& body) {
+  Call c;
+  int rc = enter(p, s, c);
+  if (rc != AGMM_OK) return rc;
+  rc = body(c);
+  const int rl = leave(p, c);
+  if (rc != AGMM_OK) return rc;
+  return rl != AGMM_OK ? rl : ok();
 }
 
 }  // namespace
@@ -721,26 +926,20 @@ agmm_plan_t agmm_plan_create(int num_shards, int64_t m_per_shard, int64_t k, int
       cus > 0)
     p->cu_count = cus;
   err = hipStreamCreateWithFlags(&p->copy_stream, hipStreamNonBlocking);
-  if (err != hipSuccess) {
-    hip_err(err, "hipStreamCreate");
-    delete p;
-    return nullptr;
-  }
-  err = hipEventCreateWithFlags(&p->ev_entry, hipEventDisableTiming);
+  if (err == hipSuccess) err = hipStreamCreateWithFlags(&p->compute2, hipStreamNonBlocking);
+  if (err == hipSuccess) err = hipEventCreateWithFlags(&p->ev_entry, hipEventDisableTiming);
   if (err == hipSuccess) err = hipEventCreateWithFlags(&p->ev_side, hipEventDisableTiming);
   if (err == hipSuccess) err = hipEventCreateWithFlags(&p->ev_c2, hipEventDisableTiming);
-  if (err == hipSuccess) err = hipStreamCreateWithFlags(&p->compute2, hipStreamNonBlocking);
+  if (err == hipSuccess) err = hipEventCreateWithFlags(&p->ev_done, hipEventDisableTiming);
   if (err != hipSuccess) {
-    if (p->ev_entry) hipEventDestroy(p->ev_entry);
-    if (p->ev_side) hipEventDestroy(p->ev_side);
-    if (p->ev_c2) hipEventDestroy(p->ev_c2);
-    if (p->compute2) hipStreamDestroy(p->compute2);
-    hip_err(err, "hipEventCreate");
-    hipStreamDestroy(p->copy_stream);
-    delete p;
+    hip_err(err, "creating the plan's streams and events");
+    const int st = g_status;
+    const std::string msg = g_msg;
+    agmm_plan_destroy(p);
+    set_err(st, "%s", msg.c_str());
     return nullptr;
   }
-  if (configure(p) != AGMM_OK) {
+  if (apply(p, Settings{}) != AGMM_OK) {
     const int st = g_status;
     const std::string msg = g_msg;
     agmm_plan_destroy(p);
@@ -755,177 +954,147 @@ int agmm_plan_set_int(agmm_plan_t p, const char* key, int64_t v) {
   if (!p) return set_err(AGMM_ERR_INVALID_ARG, "plan is NULL");
   if (!key) return set_err(AGMM_ERR_INVALID_ARG, "key is NULL");
   std::lock_guard<std::mutex> lk(p->mu);
+  if (p->broken != AGMM_OK) return set_err(p->broken, "plan is unusable: %s", p->broken_msg.c_str());
+  // A graph that captured a call holds the workspace addresses and tile
+  // tables of the plan's current layout; changing it would leave that graph
+  // reading freed or rewritten memory.
+  if (p->captured)
+    return set_err(AGMM_ERR_UNSUPPORTED,
+                   "the plan has been captured into a graph; its settings are fixed (create a new plan)");
   const std::string k(key);
+  Settings s = p->s;
   auto bad = [&]() {
     return set_err(AGMM_ERR_INVALID_ARG, "value %lld out of range for key '%s'", (long long)v, key);
   };
   if (k == "variant") {
     if (v < AGMM_VARIANT_AUTO || v > AGMM_VARIANT_SKINNY) return bad();
-    p->variant = (int)v;
+    s.variant = (int)v;
   } else if (k == "pvalue") {
     if (v < 1 || v > (1 << 20)) return bad();
-    p->pvalue = (int)v;
+    s.pvalue = (int)v;
   } else if (k == "nbuf") {
     if (v < 1 || v > 64) return bad();
-    p->nbuf = (int)v;
+    s.nbuf = (int)v;
   } else if (k == "tile") {
     if (v < -1 || v >= agmm::kTileCount) return bad();
-    p->tile = (int)v;
+    s.tile = (int)v;
   } else if (k == "splits") {
     if (v < 0 || v > 4096) return bad();
-    p->splits = (int)v;
+    s.splits = (int)v;
   } else if (k == "local_shard") {
     if (v < 0 || v >= p->N) return bad();
-    p->local_shard = (int)v;
+    s.local_shard = (int)v;
   } else if (k == "order") {
     if (v != 0 && v != 1) return bad();
-    p->order = (int)v;
+    s.order = (int)v;
   } else if (k == "group_m") {
     if (v < 0 || v > 1 << 20) return bad();
-    p->group_m = (int)v;
+    s.group_m = (int)v;
   } else if (k == "xcd_remap") {
     if (v != 0 && v != 1) return bad();
-    p->xcd_remap = (int)v;
+    s.xcd_remap = (int)v;
   } else if (k == "local_first") {
     if (v != 0 && v != 1) return bad();
-    p->local_first = (int)v;
+    s.local_first = (int)v;
   } else if (k == "gemm_streams") {
     if (v < 1 || v > 2) return bad();
-    p->gemm_streams = (int)v;
+    s.gemm_streams = (int)v;
   } else if (k == "lda" || k == "ldb" || k == "ldc") {
     // 0 restores the dense default; otherwise at least the row length, and
     // A / B rows 16-byte aligned for the vector and direct-to-LDS loads
     const int64_t e = elem_bytes(p->dtype);
     const int64_t row = k == "lda" ? p->k : k == "ldc" ? p->n : (p->rt ? p->k : p->n);
     if (v != 0 && (v < row || v >= kDimLimit || (k != "ldc" && (v * e) % 16 != 0))) return bad();
-    (k == "lda" ? p->lda : k == "ldb" ? p->ldb : p->ldc) = v;
+    (k == "lda" ? s.lda : k == "ldb" ? s.ldb : s.ldc) = v;
   } else if (k == "copy_wgs") {
     if (v < 0 || v > 1 << 20) return bad();
-    p->copy_wgs = (int)v;
+    s.copy_wgs = (int)v;
   } else if (k == "skinny_shape") {
     if (v < -1 || v > 6) return bad();
-    p->skinny_shape = (int)v;
+    s.skinny_shape = (int)v;
   } else if (k == "copy_engine") {
     if (v < 0 || v > 1) return bad();
-    p->copy_engine = (int)v;
+    s.copy_engine = (int)v;
   } else if (k == "debug_keep_slots") {
     if (v != 0 && v != 1) return bad();
-    p->debug_keep_slots = (int)v;
+    s.debug_keep_slots = (int)v;
   } else {
     return set_err(AGMM_ERR_INVALID_ARG, "unknown key '%s'", key);
   }
-  // Wait for in-flight work that may use the current workspace.
-  hipError_t err = hipDeviceSynchronize();
-  if (err != hipSuccess) return hip_err(err, "hipDeviceSynchronize");
-  return configure(p);
+  return apply(p, s);
 }
 
 int agmm_plan_get_int(agmm_plan_t p, const char* key, int64_t* value) {
   if (!p || !key || !value) return set_err(AGMM_ERR_INVALID_ARG, "NULL argument");
+  std::lock_guard<std::mutex> lk(p->mu);
   const std::string k(key);
+  const Settings& s = p->s;
+  const Layout& L = p->L;
   int64_t v;
-  if (k == "variant") v = p->variant;
-  else if (k == "variant_used") v = p->variant_used;
-  else if (k == "pvalue") v = p->pvalue;
-  else if (k == "nbuf") v = p->nbuf;
-  else if (k == "tile") v = p->tile_used;
-  else if (k == "splits") v = p->splits_used;
-  else if (k == "local_shard") v = p->local_shard;
-  else if (k == "order") v = p->order;
-  else if (k == "group_m") v = p->group_m;
+  if (k == "variant") v = s.variant;
+  else if (k == "variant_used") v = L.variant_used;
+  else if (k == "pvalue") v = s.pvalue;
+  else if (k == "nbuf") v = s.nbuf;
+  else if (k == "tile") v = L.tile_used;
+  else if (k == "splits") v = L.splits_used;
+  else if (k == "local_shard") v = s.local_shard;
+  else if (k == "order") v = s.order;
+  else if (k == "group_m") v = s.group_m;
   else if (k == "group_m_used")   // for a launch over the whole problem
-    v = p->group_m > 0 ? p->group_m : pick_group_m(cdiv(p->m, p->bm), cdiv(p->n, p->bn));
-  else if (k == "xcd_remap") v = p->xcd_remap;
-  else if (k == "copy_wgs") v = p->copy_wgs;
-  else if (k == "copy_engine") v = p->copy_engine;
-  else if (k == "skinny_shape") v = p->skinny_shape_used;
+    v = s.group_m > 0 ? s.group_m : pick_group_m(cdiv(p->m, L.bm), cdiv(p->n, L.bn));
+  else if (k == "xcd_remap") v = s.xcd_remap;
+  else if (k == "copy_wgs") v = s.copy_wgs;
+  else if (k == "copy_engine") v = s.copy_engine;
+  else if (k == "skinny_shape") v = L.skinny_shape_used;
   else if (k == "lda") v = lda_of(p);
   else if (k == "ldb") v = ldb_of(p);
   else if (k == "ldc") v = ldc_of(p);
-  else if (k == "gemm_streams") v = p->gemm_streams;
-  else if (k == "local_first") v = p->local_first;
-  else if (k == "debug_keep_slots") v = p->debug_keep_slots;
-  else if (k == "num_chunks") v = p->num_chunks;
-  else if (k == "rows_per_chunk") v = p->rows_per_chunk;
-  else if (k == "num_slots") v = p->nslots;
-  else if (k == "tile_bm") v = p->bm;
-  else if (k == "tile_bn") v = p->bn;
-  else if (k == "k_per_split") v = p->k_per_split;
-  else if (k == "num_row_blocks") v = p->order_len.empty() ? 0 : p->order_len[0];
+  else if (k == "gemm_streams") v = s.gemm_streams;
+  else if (k == "local_first") v = s.local_first;
+  else if (k == "debug_keep_slots") v = s.debug_keep_slots;
+  else if (k == "num_chunks") v = L.num_chunks;
+  else if (k == "rows_per_chunk") v = L.rows_per_chunk;
+  else if (k == "num_slots") v = L.nslots;
+  else if (k == "tile_bm") v = L.bm;
+  else if (k == "tile_bn") v = L.bn;
+  else if (k == "k_per_split") v = L.k_per_split;
+  else if (k == "num_row_blocks") v = L.order_len.empty() ? 0 : L.order_len[0];
   else if (k == "cu_count") v = p->cu_count;
+  else if (k == "captured") v = p->captured ? 1 : 0;
+  else if (k == "usable") v = p->broken == AGMM_OK ? 1 : 0;
   else return set_err(AGMM_ERR_INVALID_ARG, "unknown key '%s'", key);
   *value = v;
   return ok();
 }
 
-size_t agmm_plan_workspace_bytes(agmm_plan_t p) { return p ? p->ws_bytes : 0; }
+size_t agmm_plan_workspace_bytes(agmm_plan_t p) { return p ? p->ws_cap : 0; }
 
 const void* agmm_plan_slot_ptr(agmm_plan_t p, int slot) {
-  if (!p || !p->ring || slot < 0 || slot >= p->nslots) return nullptr;
-  return p->ring + (size_t)slot * p->slot_bytes;
+  if (!p || !p->ring || slot < 0 || slot >= p->L.nslots) return nullptr;
+  return p->ring + (size_t)slot * p->L.slot_bytes;
 }
 
 int agmm_plan_tile_order(agmm_plan_t p, int chunk, int32_t* out, int capacity) {
-  if (!p || !out || chunk < 0 || chunk >= (int)p->order_len.size()) {
+  if (!p || !out || chunk < 0 || chunk >= (int)p->L.order_len.size()) {
     set_err(AGMM_ERR_INVALID_ARG, "bad arguments to agmm_plan_tile_order");
     return -1;
   }
-  const int len = p->order_len[chunk];
+  const int len = p->L.order_len[chunk];
   if (capacity < len) {
     set_err(AGMM_ERR_INVALID_ARG, "capacity %d < %d row blocks", capacity, len);
     return -1;
   }
-  std::memcpy(out, p->h_order.data() + p->order_off[chunk], sizeof(int32_t) * len);
+  std::memcpy(out, p->L.h_order.data() + p->L.order_off[chunk], sizeof(int32_t) * len);
   ok();
   return len;
 }
-
-}  // extern "C"
-
-namespace {
-
-// agmm_run's work, with the plan already locked.
-int run_plan(agmm_plan* p, const void* const* shard_ptrs, const void* B, void* C, hipStream_t s) {
-  int rc;
-  switch (p->variant_used) {
-    case AGMM_VARIANT_FUSED:
-    case AGMM_VARIANT_SKINNY: {
-      agmm::GemmProblem g = base_problem(p, shard_rows(p, shard_ptrs), p->m, B, C, 0);
-      with_splits(p, g);
-      rc = launch_gemm(p, g, s);
-      return rc == AGMM_OK ? ok() : rc;
-    }
-    case AGMM_VARIANT_UNFUSED: {
-      rc = gather_chunk(p, shard_ptrs, 0, p->m_s, p->ring, p->m_s, 0, s);
-      if (rc != AGMM_OK) return rc;
-      agmm::RowMap rm{};
-      rm.a_group[0] = p->ring;
-      rm.a_ld = p->k;
-      rm.rows_per_group = (int32_t)p->m;
-      rm.num_groups = 1;
-      rm.c_group_rows = 0;
-      rm.c_row_off = 0;
-      agmm::GemmProblem g = base_problem(p, rm, p->m, B, C, -1);
-      with_splits(p, g);
-      rc = launch_gemm(p, g, s);
-      return rc == AGMM_OK ? ok() : rc;
-    }
-    case AGMM_VARIANT_STAGED:
-      return run_staged(p, shard_ptrs, B, C, s);
-    default:
-      return set_err(AGMM_ERR_INVALID_ARG, "plan has no valid variant");
-  }
-}
-
-}  // namespace
-
-extern "C" {
 
 int agmm_run(agmm_plan_t p, const void* const* shard_ptrs, const void* B, void* C, void* stream) {
   int rc = check_ptrs(p, shard_ptrs, B, C);
   if (rc != AGMM_OK) return rc;
   std::lock_guard<std::mutex> lk(p->mu);
-  return run_plan(p, shard_ptrs, B, C, static_cast<hipStream_t>(stream));
+  return guarded(p, static_cast<hipStream_t>(stream),
+                 [&](const Call& c) { return run_plan(p, c, shard_ptrs, B, C); });
 }
 
 int agmm_plan_autotune(agmm_plan_t p, const void* const* shard_ptrs, const void* B, void* C,
@@ -935,6 +1104,15 @@ int agmm_plan_autotune(agmm_plan_t p, const void* const* shard_ptrs, const void*
   if (iters < 1 || iters > 1000) return set_err(AGMM_ERR_INVALID_ARG, "iters must be in [1, 1000]");
   std::lock_guard<std::mutex> lk(p->mu);
   hipStream_t s = static_cast<hipStream_t>(stream);
+  hipStreamCaptureStatus cst = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &cst) != hipSuccess) return hip_err(hipGetLastError(), "hipStreamIsCapturing");
+  if (cst != hipStreamCaptureStatusNone || p->captured)
+    return set_err(AGMM_ERR_UNSUPPORTED,
+                   "autotuning times real runs and reconfigures the plan: not under graph capture, "
+                   "nor on a plan a graph has captured");
+  Call c;
+  rc = enter(p, s, c);
+  if (rc != AGMM_OK) return rc;
   hipEvent_t e0 = nullptr, e1 = nullptr;
   hipError_t err = hipEventCreate(&e0);
   if (err == hipSuccess) err = hipEventCreate(&e1);
@@ -944,10 +1122,10 @@ int agmm_plan_autotune(agmm_plan_t p, const void* const* shard_ptrs, const void*
   }
   // time the current configuration: warm-up run, then `iters` runs
   auto time_current = [&](double& ms) -> int {
-    int r = run_plan(p, shard_ptrs, B, C, s);
+    int r = run_plan(p, c, shard_ptrs, B, C);
     if (r != AGMM_OK) return r;
     if (hipEventRecord(e0, s) != hipSuccess) return hip_err(hipGetLastError(), "hipEventRecord");
-    for (int i = 0; i < iters && r == AGMM_OK; ++i) r = run_plan(p, shard_ptrs, B, C, s);
+    for (int i = 0; i < iters && r == AGMM_OK; ++i) r = run_plan(p, c, shard_ptrs, B, C);
     if (r != AGMM_OK) return r;
     if (hipEventRecord(e1, s) != hipSuccess || hipEventSynchronize(e1) != hipSuccess)
       return hip_err(hipGetLastError(), "hipEventSynchronize");
@@ -956,28 +1134,26 @@ int agmm_plan_autotune(agmm_plan_t p, const void* const* shard_ptrs, const void*
     ms = (double)f / iters;
     return AGMM_OK;
   };
+  // the runs above are all on `s`; apply() waits for the plan's last call,
+  // so mark `s` as where it happened
+  auto mark_done = [&]() { return leave(p, c); };
   // let the clocks settle before the first candidate is timed (they take
   // more than ~10 ms of load to ramp; the first timing would otherwise lose)
   {
     const auto t0 = std::chrono::steady_clock::now();
     do {
-      rc = run_plan(p, shard_ptrs, B, C, s);
+      rc = run_plan(p, c, shard_ptrs, B, C);
       if (rc == AGMM_OK && hipStreamSynchronize(s) != hipSuccess)
         rc = hip_err(hipGetLastError(), "hipStreamSynchronize");
     } while (rc == AGMM_OK &&
              std::chrono::steady_clock::now() - t0 < std::chrono::milliseconds(100));
-    if (rc != AGMM_OK) {
-      hipEventDestroy(e0);
-      hipEventDestroy(e1);
-      return rc;
-    }
   }
-  const int tile0 = p->tile, splits0 = p->splits, group0 = p->group_m;
   double best = 1e300;
-  int best_tile = tile0, best_splits = splits0, best_group = group0;
-  if (is_f32(p)) {
+  if (rc == AGMM_OK && is_f32(p)) {
     rc = time_current(best);
-  } else {
+  } else if (rc == AGMM_OK) {
+    const Settings base = p->s;
+    Settings best_s = base;
     // candidate settings of the plan's variant; configurations that resolve
     // to the same (tile, splits, group) are timed once
     std::vector<int> tiles = {agmm::kTile256x256m16, agmm::kTile256x256r5, agmm::kTile256x256,
@@ -995,11 +1171,15 @@ int agmm_plan_autotune(agmm_plan_t p, const void* const* shard_ptrs, const void*
     for (int t : tiles)
       for (int sp : splits_c)
         for (int gm : groups_c) {
-          p->tile = t;
-          p->splits = sp;
-          p->group_m = gm;
-          if (configure(p) != AGMM_OK) continue;
-          const std::array<int, 3> key = {p->tile_used, p->splits_used, p->group_m};
+          Settings s2 = base;
+          s2.tile = t;
+          s2.splits = sp;
+          s2.group_m = gm;
+          if (mark_done() != AGMM_OK || apply(p, s2) != AGMM_OK) {
+            if (p->broken != AGMM_OK) break;
+            continue;
+          }
+          const std::array<int, 3> key = {p->L.tile_used, p->L.splits_used, p->s.group_m};
           if (std::find(seen.begin(), seen.end(), key) != seen.end()) continue;
           seen.push_back(key);
           double ms = 0;
@@ -1009,20 +1189,19 @@ int agmm_plan_autotune(agmm_plan_t p, const void* const* shard_ptrs, const void*
           }
           if (ms < best) {
             best = ms;
-            best_tile = t;
-            best_splits = sp;
-            best_group = gm;
+            best_s = s2;
           }
         }
-    p->tile = best_tile;
-    p->splits = best_splits;
-    p->group_m = best_group;
-    rc = configure(p);
+    rc = mark_done();
+    if (rc == AGMM_OK && p->broken == AGMM_OK) rc = apply(p, best_s);
+    else if (p->broken != AGMM_OK) rc = set_err(p->broken, "plan is unusable: %s", p->broken_msg.c_str());
     if (rc == AGMM_OK && best >= 1e300) rc = set_err(AGMM_ERR_HIP, "no candidate configuration ran");
   }
+  const int rl = leave(p, c);
   hipEventDestroy(e0);
   hipEventDestroy(e1);
   if (rc != AGMM_OK) return rc;
+  if (rl != AGMM_OK) return rl;
   if (best_ms) *best_ms = best;
   return ok();
 }
@@ -1040,6 +1219,7 @@ int agmm_gather(agmm_plan_t p, const void* const* shard_ptrs, void* gathered, vo
   if ((p->k * (int64_t)elem_bytes(p->dtype)) % 16 != 0)
     return set_err(AGMM_ERR_UNSUPPORTED, "the gather copy needs 16-byte rows");
   std::lock_guard<std::mutex> lk(p->mu);
+  // no workspace is used: nothing to order against the plan's other calls
   const int rc = gather_chunk(p, shard_ptrs, 0, p->m_s, gathered, p->m_s, 0,
                               static_cast<hipStream_t>(stream));
   return rc == AGMM_OK ? ok() : rc;
@@ -1051,17 +1231,11 @@ int agmm_run_gathered(agmm_plan_t p, const void* gathered, const void* B, void* 
   if (!aligned16(gathered) || !aligned16(B) || !aligned16(C))
     return set_err(AGMM_ERR_UNSUPPORTED, "pointers must be 16-byte aligned");
   std::lock_guard<std::mutex> lk(p->mu);
-  agmm::RowMap rm{};
-  rm.a_group[0] = gathered;
-  rm.a_ld = p->k;
-  rm.rows_per_group = (int32_t)p->m;
-  rm.num_groups = 1;
-  rm.c_group_rows = 0;
-  rm.c_row_off = 0;
-  agmm::GemmProblem g = base_problem(p, rm, p->m, B, C, -1);
-  with_splits(p, g);
-  const int rc = launch_gemm(p, g, static_cast<hipStream_t>(stream));
-  return rc == AGMM_OK ? ok() : rc;
+  return guarded(p, static_cast<hipStream_t>(stream), [&](const Call& c) {
+    agmm::GemmProblem g = base_problem(p, dense_rows(gathered, p->m, p->k), p->m, B, C, -1);
+    with_splits(p, g);
+    return launch_gemm(p, c, g, c.s);
+  });
 }
 
 int agmm_run_gather_out(agmm_plan_t p, const void* const* shard_ptrs, const void* B, void* C,
@@ -1073,49 +1247,38 @@ int agmm_run_gather_out(agmm_plan_t p, const void* const* shard_ptrs, const void
   if ((p->k * (int64_t)elem_bytes(p->dtype)) % 16 != 0)
     return set_err(AGMM_ERR_UNSUPPORTED, "the gather copy needs 16-byte rows (k * elem_bytes %% 16 == 0)");
   std::lock_guard<std::mutex> lk(p->mu);
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const int copy_wgs = p->copy_wgs > 0 ? p->copy_wgs : p->cu_count;
-  switch (p->variant_used) {
-    case AGMM_VARIANT_STAGED:
-      return run_staged(p, shard_ptrs, B, C, s, gathered);
-    case AGMM_VARIANT_UNFUSED: {
-      // the gather is the first half of this variant anyway
-      rc = gather_chunk(p, shard_ptrs, 0, p->m_s, gathered, p->m_s, 0, s);
-      if (rc != AGMM_OK) return rc;
-      agmm::RowMap rm{};
-      rm.a_group[0] = gathered;
-      rm.a_ld = p->k;
-      rm.rows_per_group = (int32_t)p->m;
-      rm.num_groups = 1;
-      rm.c_group_rows = 0;
-      rm.c_row_off = 0;
-      agmm::GemmProblem g = base_problem(p, rm, p->m, B, C, -1);
-      with_splits(p, g);
-      rc = launch_gemm(p, g, s);
-      return rc == AGMM_OK ? ok() : rc;
+  return guarded(p, static_cast<hipStream_t>(stream), [&](const Call& c) -> int {
+    const int copy_wgs = p->s.copy_wgs > 0 ? p->s.copy_wgs : p->cu_count;
+    switch (p->L.variant_used) {
+      case AGMM_VARIANT_STAGED:
+        return run_staged(p, c, shard_ptrs, B, C, gathered);
+      case AGMM_VARIANT_UNFUSED: {
+        // the gather is the first half of this variant anyway
+        int r = gather_chunk(p, shard_ptrs, 0, p->m_s, gathered, p->m_s, 0, c.s);
+        if (r != AGMM_OK) return r;
+        agmm::GemmProblem g = base_problem(p, dense_rows(gathered, p->m, p->k), p->m, B, C, -1);
+        with_splits(p, g);
+        return launch_gemm(p, c, g, c.s);
+      }
+      default: {
+        // fused / skinny / fp32: the GEMM reads the shards on the caller's
+        // stream while the copy stream writes the gathered operand; the
+        // caller's stream then waits for the copy
+        int r = fork_to(p, c, p->copy_stream);
+        if (r != AGMM_OK) return r;
+        r = copy_on_sdma(p, c, true)
+                ? gather_chunk_sdma(p, shard_ptrs, 0, p->m_s, gathered, p->m_s, p->copy_stream)
+                : gather_chunk(p, shard_ptrs, 0, p->m_s, gathered, p->m_s, copy_wgs, p->copy_stream);
+        if (r == AGMM_OK) {
+          agmm::GemmProblem g = base_problem(p, shard_rows(p, shard_ptrs), p->m, B, C, 0);
+          with_splits(p, g);
+          r = launch_gemm(p, c, g, c.s);
+        }
+        const int rj = join_from(c, p->copy_stream, p->ev_side);
+        return r != AGMM_OK ? r : rj;
+      }
     }
-    default: {
-      // fused / skinny / fp32: the GEMM reads the shards on the caller's
-      // stream while the copy stream writes the gathered operand; the
-      // caller's stream then waits for the copy
-      hipError_t err = hipEventRecord(p->ev_entry, s);
-      if (err == hipSuccess) err = hipStreamWaitEvent(p->copy_stream, p->ev_entry, 0);
-      if (err != hipSuccess) return hip_err(err, "stream fork");
-      rc = copy_on_sdma(p, s, true)
-               ? gather_chunk_sdma(p, shard_ptrs, 0, p->m_s, gathered, p->m_s, p->copy_stream)
-               : gather_chunk(p, shard_ptrs, 0, p->m_s, gathered, p->m_s, copy_wgs, p->copy_stream);
-      if (rc != AGMM_OK) return rc;
-      if ((err = hipEventRecord(p->ev_side, p->copy_stream)) != hipSuccess)
-        return hip_err(err, "hipEventRecord(side)");
-      agmm::GemmProblem g = base_problem(p, shard_rows(p, shard_ptrs), p->m, B, C, 0);
-      with_splits(p, g);
-      rc = launch_gemm(p, g, s);
-      if (rc != AGMM_OK) return rc;
-      if ((err = hipStreamWaitEvent(s, p->ev_side, 0)) != hipSuccess)
-        return hip_err(err, "stream join");
-      return ok();
-    }
-  }
+  });
 }
 
 int agmm_plan_timing_begin(agmm_plan_t p) {
@@ -1158,16 +1321,21 @@ int agmm_plan_timing_end(agmm_plan_t p) {
 
 void agmm_plan_destroy(agmm_plan_t p) {
   if (!p) return;
-  if (p->copy_stream) hipStreamSynchronize(p->copy_stream);
-  if (p->compute2) hipStreamSynchronize(p->compute2);
-  hipDeviceSynchronize();
-  free_resources(p);
+  {
+    std::lock_guard<std::mutex> lk(p->mu);
+    // the plan's own work: its last call (which the internal streams joined)
+    // and anything still queued on the internal streams
+    if (p->done_state == kDoneEager && p->ev_done) hipEventSynchronize(p->ev_done);
+    if (p->copy_stream) hipStreamSynchronize(p->copy_stream);
+    if (p->compute2) hipStreamSynchronize(p->compute2);
+    (void)hipGetLastError();
+  }
+  if (p->ws) hipFree(p->ws);
   for (hipEvent_t e : p->ev_ready) hipEventDestroy(e);
   for (hipEvent_t e : p->ev_free) hipEventDestroy(e);
   for (hipEvent_t e : p->tev) hipEventDestroy(e);
-  if (p->ev_entry) hipEventDestroy(p->ev_entry);
-  if (p->ev_side) hipEventDestroy(p->ev_side);
-  if (p->ev_c2) hipEventDestroy(p->ev_c2);
+  for (hipEvent_t e : {p->ev_entry, p->ev_side, p->ev_c2, p->ev_done})
+    if (e) hipEventDestroy(e);
   if (p->compute2) hipStreamDestroy(p->compute2);
   if (p->copy_stream) hipStreamDestroy(p->copy_stream);
   delete p;
@@ -1177,6 +1345,6 @@ int agmm_last_status(void) { return g_status; }
 
 const char* agmm_last_error(void) { return g_msg.c_str(); }
 
-const char* agmm_version(void) { return "agmm 0.1.0 (gfx950)"; }
+const char* agmm_version(void) { return "agmm 0.2.0 (gfx950)"; }
 
 }  // extern "C"

@@ -55,29 +55,26 @@ struct GemmProblem {
   float* partials;         // [splits][m][n] fp32 scratch
 };
 
-// Tile shapes compiled for the MFMA kernels.
+// Tile shapes compiled for the MFMA kernels.  Each one is reached by the
+// plan's automatic choice or by the autotuner's candidate list.
 enum TileCfg : int {
-  kTile256x256 = 0,      // 4 waves, 128x128 per wave, 32-deep k-tiles
-  kTile128x128 = 1,      // 64x64 per wave
-  kTile256x128 = 2,      // 128x64 per wave
-  kTile256x256k64 = 3,   // as kTile256x256 with 64-deep k-tiles
-  kTile256x128k64 = 4,
-  kTile128x128k64 = 5,
-  kTile256x256w8 = 6,    // 8 waves (two per SIMD), 128x64 per wave
-  kTile256x128w8 = 7,    // 8 waves, 128x32 per wave
-  kTile128x64 = 8,       // 4 waves, 64x32 per wave; B stored n x k only
-  kTile256x256pp = 9,    // 8 waves, 128x64 per wave, ping-pong compute/memory groups
-  kTile128x128s8 = 10,   // 8-stage LDS ring (whole short k ranges in flight)
-  kTile128x64s8 = 11,    // same for the 128x64 tile; B stored n x k only
-  kTile256x256s5 = 12,   // 5-stage ring: 4 k-tiles in flight (latency of L2 misses)
-  kTile256x256r5 = 13,   // 64-deep k-tiles in a ring of 5 operand slots (whole L2 lines per load)
-  kTile128x128r5 = 14,   // same ring, 128x128, two workgroups per CU
-  kTile128x64r5 = 15,    // same ring, 128x64; B stored n x k only
-  kTile256x256m16 = 16,  // part ring, 256x256, on 16x16x32 MFMAs
-  kTile128x128m16 = 17,  // part ring, 128x128, on 16x16x32 MFMAs
-  kTileSkinny = 18,      // 64x16 over the whole k, wave-private LDS rings (launch_skinny_fullk); B n x k only
-  kTileCount = 19,
+  kTile256x256 = 0,      // 4 waves, 128x128 per wave, 32-deep k-tiles in a 4-stage ring (k < 256)
+  kTile128x128 = 1,      // 64x64 per wave, two workgroups per CU
+  kTile256x128 = 2,      // 128x64 per wave, two workgroups per CU
+  kTile128x64 = 3,       // 4 waves, 64x32 per wave; B stored n x k only
+  kTile128x64s8 = 4,     // 8-stage LDS ring (whole short k ranges in flight); B stored n x k only
+  kTile256x256r5 = 5,    // 64-deep k-tiles in a ring of 5 operand slots (whole L2 lines per load)
+  kTile128x128r5 = 6,    // same ring, 128x128, two workgroups per CU
+  kTile128x64r5 = 7,     // same ring, 128x64; B stored n x k only
+  kTile256x256m16 = 8,   // part ring, 256x256, on 16x16x32 MFMAs (automatic for k >= 256)
+  kTile128x128m16 = 9,   // part ring, 128x128, on 16x16x32 MFMAs
+  kTileSkinny = 10,      // whole k per workgroup, wave-private LDS rings (launch_skinny_fullk); B n x k only
+  kTileCount = 11,
 };
+// Tiles that read B only as stored n x k (rhs_transpose).
+constexpr bool tile_needs_bt(int cfg) {
+  return cfg == kTile128x64 || cfg == kTile128x64s8 || cfg == kTile128x64r5 || cfg == kTileSkinny;
+}
 int tile_bm(int cfg);
 int tile_bn(int cfg);
 int tile_bk(int cfg);

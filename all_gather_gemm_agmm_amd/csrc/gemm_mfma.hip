@@ -204,7 +204,6 @@ __device__ __forceinline__ void tile_coords(const TileOrder& o, int wg, int nwg,
 
 // Main-loop forms.
 //   kLoopStages:   ring of NST stages, each one k-tile of A and B.
-//   kLoopPingPong: 8 waves in two groups alternating compute and memory work.
 //   kLoopParts:    ring of NST slots, each holding one operand of one k-tile
 //                  ("part"); the parts alternate A, B, A, B, ...  With an odd
 //                  slot count this keeps 2.5 k-tiles of 64-deep operands in
@@ -216,7 +215,6 @@ struct BoolTag {
 };
 
 constexpr int kLoopStages = 0;
-constexpr int kLoopPingPong = 1;
 constexpr int kLoopParts = 2;
 
 template <int BM, int BN, int BK, int DT, bool BT, int NST, int WAVES, int LOOP = kLoopStages>
@@ -441,22 +439,6 @@ void gemm_mfma_kernel(GemmProblem p) {
   constexpr int kMfmaPerSub = T::FM * T::FN;
   constexpr int kReadsPerSub = T::FM + (BT ? T::FN : 2 * T::FN);
 
-  // ---- main loop, ping-pong form (8 waves, two per SIMD) -------------------------
-  // Waves 0-3 (group 0) own output rows [0, BM/2) of the tile, waves 4-7
-  // (group 1) rows [BM/2, BM); the two waves on one SIMD belong to different
-  // groups.  Each k-tile has two phases separated by barriers; in every
-  // phase one group only issues MFMAs from fragments already in registers
-  // while the other group issues its share of the global->LDS loads and
-  // reads the fragments for its next compute phase:
-  //   phase A of tile it: group 0 multiplies tile it;
-  //                       group 1 loads tile it+3, reads tile it
-  //   phase B of tile it: group 1 multiplies tile it;
-  //                       group 0 loads tile it+3, reads tile it+1
-  // A wave that stalls on a load issue therefore never holds up the MFMA
-  // stream of its SIMD.  Tile t is complete in LDS before the barrier that
-  // opens phase B of tile t-1 (every wave waits for its own loads of t
-  // there); tile t+3 goes into the stage of tile t-1, whose last readers
-  // finished before the barrier that closes phase B of tile t-1.
   // ---- main loop, part ring ----------------------------------------------------
   // Slot q % 5 receives part q: A of k-tile q/2 for even q, B for odd q.
   // Parts 0-3 are issued up front.  During k-tile t:
@@ -570,48 +552,6 @@ void gemm_mfma_kernel(GemmProblem p) {
     };
     if (interior) ring(BoolTag<true>{});
     else ring(BoolTag<false>{});
-  } else if constexpr (LOOP == kLoopPingPong) {
-    static_assert(WAVES == 8 && T::MID_SYNC && kStages == 4, "ping-pong layout");
-    const int grp = wave >> 2;
-    u32x4_t pa[T::SUB][T::FM], pb[T::SUB][T::FN];
-    auto read_tile = [&](int stage) {
-#pragma unroll
-      for (int s2 = 0; s2 < T::SUB; ++s2)
-        read_frags(smem + stage * T::STAGE_BYTES, s2, pa[s2], pb[s2]);
-    };
-    auto mul_tile = [&]() {
-#pragma unroll
-      for (int s2 = 0; s2 < T::SUB; ++s2) mfma_block(pa[s2], pb[s2]);
-    };
-#pragma unroll
-    for (int t = 0; t < 3; ++t) issue(t, k_begin + t * kBK);
-    wait_vmcnt<2 * T::LOADS>();
-    block_barrier();
-    if (grp == 0) read_tile(0);
-    int st_cur = 0;   // stage of tile it
-    int st_new = 3;   // stage of tile it+3
-    for (int it = 0; it < nk; ++it) {
-      const int st_next = (st_cur + 1) & 3;
-      const int k_new = k_begin + (it + 3) * kBK;
-      if (grp == 0) {
-        mul_tile();
-        wait_vmcnt<T::LOADS>();          // own loads of tile it+1 done
-      } else {
-        issue(st_new, k_new);
-        read_tile(st_cur);
-        wait_vmcnt<2 * T::LOADS>();      // own loads of tile it+1 done
-      }
-      block_barrier();
-      if (grp == 1) {
-        mul_tile();
-      } else {
-        issue(st_new, k_new);
-        read_tile(st_next);
-      }
-      block_barrier();
-      st_cur = st_next;
-      st_new = (st_new + 1) & 3;
-    }
   } else {
   // ---- main loop ---------------------------------------------------------------
   // Fragment registers alternate between two sets: the LDS reads of substep
@@ -1400,22 +1340,14 @@ constexpr TileInfo kTiles[kTileCount] = {
     {256, 256, 32, 4, 4, 1},   // kTile256x256:      128 KiB LDS, 3 k-tiles in flight
     {128, 128, 32, 4, 4, 2},   // kTile128x128:      64 KiB, two workgroups per CU
     {256, 128, 32, 3, 4, 2},   // kTile256x128:      72 KiB, two workgroups per CU
-    {256, 256, 64, 2, 4, 1},   // kTile256x256k64:   128 KiB, 128-byte rows per load
-    {256, 128, 64, 3, 4, 1},   // kTile256x128k64:   144 KiB
-    {128, 128, 64, 2, 4, 2},   // kTile128x128k64:   64 KiB, two workgroups per CU
-    {256, 256, 32, 4, 8, 2},   // kTile256x256w8:    8 waves (2 per SIMD), 128x64 per wave
-    {256, 128, 32, 4, 8, 2},   // kTile256x128w8:    8 waves, 128x32 per wave
     {128, 64, 32, 4, 4, 1},    // kTile128x64:       48 KiB; B stored n x k only (skinny m)
-    {256, 256, 32, 4, 8, 2},   // kTile256x256pp:    8 waves in ping-pong groups
-    {128, 128, 32, 8, 4, 1},   // kTile128x128s8:    128 KiB, 7 k-tiles in flight (short k ranges)
     {128, 64, 32, 8, 4, 1},    // kTile128x64s8:     96 KiB, 7 k-tiles in flight; B n x k only
-    {256, 256, 32, 5, 4, 1},   // kTile256x256s5:    160 KiB (all of LDS), 4 k-tiles in flight
     {256, 256, 64, 5, 4, 1},   // kTile256x256r5:    160 KiB part ring, 64-deep k-tiles
     {128, 128, 64, 5, 4, 2},   // kTile128x128r5:    80 KiB part ring, two workgroups per CU
     {128, 64, 64, 5, 4, 2},    // kTile128x64r5:     80 KiB part ring; B stored n x k only
     {256, 256, 64, 5, 4, 1},   // kTile256x256m16:   part ring on 16x16x32 MFMAs
     {128, 128, 64, 5, 4, 2},   // kTile128x128m16:   same, two workgroups per CU
-    {64, 16, 64, 4, 4, 1},     // kTileSkinny:       skinny kernel, whole k (launch_skinny_fullk)
+    {32, 32, 64, 4, 8, 1},     // kTileSkinny:       skinny kernel, whole k (launch_skinny_fullk)
 };
 
 int tile_bm(int cfg) { return kTiles[cfg].bm; }
@@ -1426,34 +1358,23 @@ int tile_occ(int cfg) { return kTiles[cfg].occ; }
 hipError_t launch_gemm_mfma(const GemmProblem& p, int tile_cfg, int dtype, bool rhs_transpose,
                             hipStream_t stream) {
   if (dtype != kDtypeBf16 && dtype != kDtypeFp16) return hipErrorInvalidValue;
+  // an n-contiguous B tile of 64 columns is too narrow for its LDS swizzle
+  if (tile_needs_bt(tile_cfg) && !rhs_transpose) return hipErrorInvalidValue;
   switch (tile_cfg) {
     case kTile256x256: return launch_tile<256, 256, 32, 4, 4, 1>(p, dtype, rhs_transpose, stream);
     case kTile128x128: return launch_tile<128, 128, 32, 4, 4, 2>(p, dtype, rhs_transpose, stream);
     case kTile256x128: return launch_tile<256, 128, 32, 3, 4, 2>(p, dtype, rhs_transpose, stream);
-    case kTile256x256k64: return launch_tile<256, 256, 64, 2, 4, 1>(p, dtype, rhs_transpose, stream);
-    case kTile256x128k64: return launch_tile<256, 128, 64, 3, 4, 1>(p, dtype, rhs_transpose, stream);
-    case kTile128x128k64: return launch_tile<128, 128, 64, 2, 4, 2>(p, dtype, rhs_transpose, stream);
-    case kTile256x256w8: return launch_tile<256, 256, 32, 4, 8, 2>(p, dtype, rhs_transpose, stream);
-    case kTile256x128w8: return launch_tile<256, 128, 32, 4, 8, 2>(p, dtype, rhs_transpose, stream);
     case kTile128x64:
-      // an n-contiguous B tile of 64 columns is too narrow for its LDS swizzle
-      if (!rhs_transpose) return hipErrorInvalidValue;
       return dtype == kDtypeBf16 ? launch_one<128, 64, 32, kDtypeBf16, true, 4, 4, 1>(p, stream)
                                  : launch_one<128, 64, 32, kDtypeFp16, true, 4, 4, 1>(p, stream);
-    case kTile256x256pp:
-      return launch_tile<256, 256, 32, 4, 8, 2, kLoopPingPong>(p, dtype, rhs_transpose, stream);
-    case kTile128x128s8: return launch_tile<128, 128, 32, 8, 4, 1>(p, dtype, rhs_transpose, stream);
     case kTile128x64s8:
-      if (!rhs_transpose) return hipErrorInvalidValue;
       return dtype == kDtypeBf16 ? launch_one<128, 64, 32, kDtypeBf16, true, 8, 4, 1>(p, stream)
                                  : launch_one<128, 64, 32, kDtypeFp16, true, 8, 4, 1>(p, stream);
-    case kTile256x256s5: return launch_tile<256, 256, 32, 5, 4, 1>(p, dtype, rhs_transpose, stream);
     case kTile256x256r5:
       return launch_tile<256, 256, 64, 5, 4, 1, kLoopParts>(p, dtype, rhs_transpose, stream);
     case kTile128x128r5:
       return launch_tile<128, 128, 64, 5, 4, 2, kLoopParts>(p, dtype, rhs_transpose, stream);
     case kTile128x64r5:
-      if (!rhs_transpose) return hipErrorInvalidValue;
       return dtype == kDtypeBf16 ? launch_one<128, 64, 64, kDtypeBf16, true, 5, 4, 2, kLoopParts>(p, stream)
                                  : launch_one<128, 64, 64, kDtypeFp16, true, 5, 4, 2, kLoopParts>(p, stream);
     case kTile256x256m16: return launch_m16<256, 256, 64, 4, 1>(p, dtype, rhs_transpose, stream);

@@ -128,11 +128,21 @@ agmm_plan_t agmm_plan_create(int num_shards, int64_t m_per_shard, int64_t k, int
  * Row strides are the plan's "lda", "ldb", "ldc" settings (default: dense,
  * i.e. k, n_local or k, n_local); every buffer must hold its last row in full.
  * All device pointers must be 16-byte aligned.
- * Not safe to call concurrently on one plan from two host threads or on two
- * streams at once (the ring and split-K scratch are shared); serial calls on
- * different streams are safe (the plan orders them with its events).
+ * Ordering between calls on one plan: every call that enqueues work on the
+ * plan (agmm_run, agmm_run_gathered, agmm_run_gather_out, agmm_plan_autotune)
+ * records the plan's completion event on its stream after the plan's internal
+ * streams have joined that stream, and the next such call's stream waits on
+ * it before any of its own work.  So calls on different streams, or from
+ * different host threads (a mutex serialises the host side), run one after
+ * the other on the GPU and never overwrite ring slots or split-K partial sums
+ * a previous call still reads (the Ascend tutorial's "Double Buffering": a
+ * slot is not refilled before the chunk reading it has been consumed).
+ * Within one graph capture calls are ordered the same way.  Across a capture
+ * boundary (a graph replay against eager calls) no event links them: the
+ * caller orders replays with its streams, as for any graph.
  * Returns AGMM_OK, AGMM_ERR_INVALID_ARG (NULL plan/pointer),
- * AGMM_ERR_UNSUPPORTED (misaligned pointer) or AGMM_ERR_HIP (launch failed).
+ * AGMM_ERR_UNSUPPORTED (misaligned pointer), AGMM_ERR_HIP (launch failed), or
+ * the status that left the plan unusable (see agmm_plan_set_int).
  */
 int agmm_run(agmm_plan_t plan, const void *const *shard_ptrs, const void *B, void *C,
              void *stream);
@@ -199,26 +209,24 @@ int agmm_plan_autotune(agmm_plan_t plan, const void *const *shard_ptrs, const vo
  *   "pvalue"        >= 1: tile-rows of each shard per staged chunk
  *   "nbuf"          >= 1: ring slots for the staged variant
  *   "tile"          -1: automatic, else a compiled bf16/fp16 tile shape:
- *                   0 256x256 (32-deep k-tiles, 4 stages), 1 128x128,
- *                   2 256x128, 3 256x256 (64-deep, 2 stages), 4 256x128
- *                   (64-deep), 5 128x128 (64-deep), 6 256x256 (8 waves),
- *                   7 256x128 (8 waves), 8 128x64 (rhs_transpose only),
- *                   9 256x256 (8 waves, ping-pong), 10 128x128 (8 stages),
- *                   11 128x64 (8 stages, rhs_transpose only), 12 256x256
- *                   (5 stages), 13 256x256 (64-deep k-tiles in a 5-slot
- *                   operand ring), 14 128x128 and 15 128x64
- *                   (rhs_transpose only) in the same ring, 16 256x256 and
- *                   17 128x128 in the same ring on 16x16x32 MFMAs (the
- *                   automatic choices for k >= 256), 18 the whole-k skinny
- *                   kernel (rhs_transpose only; tile from "skinny_shape"; no
- *                   k split; the automatic skinny choice for m <= 128; 15
- *                   for 128 < m <= 256)
+ *                   0 256x256 (32-deep k-tiles, 4 LDS stages; automatic for
+ *                   k < 256), 1 128x128 and 2 256x128 (same loop, two
+ *                   workgroups per CU), 3 128x64 and 4 128x64 with 8 stages
+ *                   (rhs_transpose only), 5 256x256, 6 128x128 and 7 128x64
+ *                   (rhs_transpose only) with 64-deep k-tiles in a 5-slot
+ *                   operand ring, 8 256x256 and 9 128x128 in the same ring on
+ *                   16x16x32 MFMAs (the automatic choices for k >= 256),
+ *                   10 the whole-k skinny kernel (rhs_transpose only; tile
+ *                   from "skinny_shape"; no k split; the automatic skinny
+ *                   choice for m <= 128; 7 for 128 < m <= 256).  A tile that
+ *                   needs rhs_transpose on a plan without it is rejected
+ *                   with AGMM_ERR_UNSUPPORTED.
  *   "splits"        0: automatic, else k-splits (fp32 partial sums, then a
  *                   fixed-order reduction) of every bf16/fp16 launch (for the
  *                   staged variant: of each chunk's launch); automatic splits
  *                   are used by the split-K skinny tiles and by launches
  *                   whose output tiles fill at most half of the workgroup
- *                   slots; tile 18 ignores it
+ *                   slots; tile 10 ignores it
  *   "local_shard"   0 .. num_shards-1: where the ring order starts
  *   "order"         0: ring order from local_shard, 1: natural order
  *   "group_m"       row blocks walked together (L2 reuse); 0 (default):
@@ -230,7 +238,7 @@ int agmm_plan_autotune(agmm_plan_t plan, const void *const *shard_ptrs, const vo
  *                   agmm_run_gather_out (0 = one per CU)
  *   "skinny_shape"  -1 (automatic: 5, or 0 when 64 x 16 gives more
  *                   workgroups than 32 x 32) or 0..6: output tile of the
- *                   whole-k skinny kernel (tile 18), rows x columns: 0 64 x 16,
+ *                   whole-k skinny kernel (tile 10), rows x columns: 0 64 x 16,
  *                   1 32 x 32, 2 32 x 16, 3 16 x 32, 4 64 x 32 (4 waves);
  *                   5 32 x 32, 6 64 x 16 (8 waves).  Reads back the shape in
  *                   use.
@@ -259,19 +267,32 @@ int agmm_plan_autotune(agmm_plan_t plan, const void *const *shard_ptrs, const vo
  *                   rows.  The ring slots still hold every shard's rows.
  *   "debug_keep_slots" 0/1: staged variant uses one slot per chunk (nothing
  *                   is overwritten; for inspection by agmm_plan_slot_ptr)
- * Changing a key that affects the workspace reallocates it (synchronously).
- * Returns AGMM_OK, AGMM_ERR_INVALID_ARG (unknown key / out of range) or
- * AGMM_ERR_OOM.
+ * A change waits for the plan's previous call to finish, then keeps the
+ * workspace allocation if the new layout fits in it and reallocates it
+ * otherwise.  It is all or nothing: when the new value is rejected (range,
+ * a tile the layout cannot use, AGMM_ERR_OOM) the plan keeps its previous
+ * settings and a workspace for them.  Only if even that workspace cannot be
+ * allocated again is the plan left unusable: every later call on it then
+ * fails with the status of that failure (get "usable" reads 0).  A plan that
+ * a graph has captured keeps its settings for good (the graph holds its
+ * workspace addresses and tile tables): set_int then returns
+ * AGMM_ERR_UNSUPPORTED (get "captured" reads 1).
+ * Returns AGMM_OK, AGMM_ERR_INVALID_ARG (unknown key / out of range),
+ * AGMM_ERR_UNSUPPORTED (captured plan, tile not usable) or AGMM_ERR_OOM.
  */
 int agmm_plan_set_int(agmm_plan_t plan, const char *key, int64_t value);
 
 /* Read a plan setting (keys above, plus "num_chunks", "rows_per_chunk",
- * "tile_bm", "tile_bn", "num_row_blocks", the resolved "variant_used", and
- * "group_m_used": the row-block group a launch over the whole problem uses).
- * value: host pointer.  Returns AGMM_OK or AGMM_ERR_INVALID_ARG. */
+ * "num_slots", "tile_bm", "tile_bn", "k_per_split", "num_row_blocks",
+ * "cu_count", the resolved "variant_used", "group_m_used": the row-block
+ * group a launch over the whole problem uses, "captured": 1 once a call was
+ * captured into a graph, and "usable": 0 after a failed reconfiguration left
+ * the plan without a workspace).  value: host pointer.  Returns AGMM_OK or
+ * AGMM_ERR_INVALID_ARG. */
 int agmm_plan_get_int(agmm_plan_t plan, const char *key, int64_t *value);
 
-/* Bytes of device workspace the plan holds (ring, partials, tables). */
+/* Bytes of device workspace the plan holds (ring, partials, tables; the
+ * allocation is kept when a new layout needs less). */
 size_t agmm_plan_workspace_bytes(agmm_plan_t plan);
 
 /* Device address of ring slot `slot` ([num_shards][rows_per_chunk][k]) or
@@ -301,7 +322,10 @@ int agmm_plan_timing_begin(agmm_plan_t plan);
 int agmm_plan_timing_read(agmm_plan_t plan, double *total_ms, int64_t *launches);
 int agmm_plan_timing_end(agmm_plan_t plan);
 
-/* Wait for the plan's internal streams, free its workspace. NULL is a no-op. */
+/* Wait for the plan's last call and its internal streams (nothing else on
+ * the device), then free its workspace, streams and events.  NULL is a
+ * no-op.  Destroy a plan only after every graph that captured it has been
+ * destroyed or has finished its last replay: the graph uses its workspace. */
 void agmm_plan_destroy(agmm_plan_t plan);
 
 /* Thread-local status / message of the last failing call (AGMM_OK / "" if none). */

@@ -55,3 +55,18 @@ def sample_rows(num_shards: int, m_s: int, extra=(), per_shard=4, seed=0):
         if 0 <= x < num_shards * m_s:
             rows.add(int(x))
     return sorted(rows)
+
+
+def block_rows(m: int, block=256, seed=0):
+    """Two rows of every `block`-row block of C, one in each half (the two
+    128-row wave halves of a 256-row tile), at offsets that vary from block
+    to block (so different rows of the 16-row MFMA blocks are hit)."""
+    rng = np.random.default_rng(seed)
+    rows = []
+    for b0 in range(0, m, block):
+        half = block // 2
+        for lo in (b0, b0 + half):
+            hi = min(lo + half, m)
+            if lo < hi:
+                rows.append(int(rng.integers(lo, hi)))
+    return rows

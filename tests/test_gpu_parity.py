@@ -5,6 +5,8 @@ Tolerance (stated for the all-gather matmul workloads): per element
 for fp32 inputs, C_ref being the oracle's float64 result.  Gathered operands
 and schedule-invariance checks are bit-exact.
 """
+import time
+
 import numpy as np
 import pytest
 import torch
@@ -12,7 +14,7 @@ import torch
 import oracle
 import all_gather_gemm_agmm_amd as agmm
 from all_gather_gemm_agmm_amd import inputs as I
-from gpu_util import BOUND, rel_err, sample_rows, to_bits, to_device, torch_dtype
+from gpu_util import BOUND, block_rows, rel_err, sample_rows, to_bits, to_device, torch_dtype
 
 pytestmark = pytest.mark.gpu
 
@@ -81,14 +83,14 @@ def test_small_ragged(case, variant):
     check_against_oracle(w, shards, B, C)
 
 
-@pytest.mark.parametrize("tile", list(range(19)))
+@pytest.mark.parametrize("tile", list(range(agmm.NUM_TILES)))
 @pytest.mark.parametrize("dtype,rt", [(BF16, False), (BF16, True), (FP16, False), (FP16, True)])
 @pytest.mark.parametrize("k", [328, 384])
 def test_tiles_ragged(tile, dtype, rt, k):
     """Every tile shape against the oracle on ragged m and n; k = 328 leaves a
     ragged last k-tile, k = 384 is whole 64-deep k-tiles, so interior tiles
     take the unmasked load path."""
-    if tile in (8, 11, 15, 18) and not rt:
+    if tile in agmm.TILES_NEED_BT and not rt:
         pytest.skip("the 128x64 and skinny whole-k tiles take B stored n x k only")
     w, shards, B = make_case(3, 200, k, 392, dtype, rt, seed=900 + tile + k)
     shards_d = [to_device(s, dtype) for s in shards]
@@ -113,7 +115,7 @@ SKINNY_FULLK = [
 @pytest.mark.parametrize("shape", [0, 1, 2, 3, 4, 5, 6])
 @pytest.mark.parametrize("case", SKINNY_FULLK, ids=lambda c: f"{c[0]}x{c[1]}x{c[2]}x{c[3]}-d{c[4]}-{len(c[5])}")
 def test_skinny_fullk_tile(case, shape):
-    """Tile 18 (tiles over the whole of k, wave-private LDS rings), every
+    """The whole-k skinny tile (tiles over the whole of k, wave-private LDS rings), every
     tile shape (64x16, 32x32, 32x16, 16x32, 64x32), against the oracle on
     ragged m, n and k, strided operands; C's row padding untouched; a second
     run bit-identical."""
@@ -129,9 +131,9 @@ def test_skinny_fullk_tile(case, shape):
     bfull = torch.full((n, ldb), float("nan"), dtype=dt, device="cuda")
     bfull[:, :k] = to_device(B, dtype)
     C = torch.full((N * m_s, ldc), float("nan"), dtype=dt, device="cuda")
-    plan = agmm.Plan(N, m_s, k, n, dtype, True, variant="skinny", tile=18, skinny_shape=shape, **extra)
+    plan = agmm.Plan(N, m_s, k, n, dtype, True, variant="skinny", tile=agmm.TILE_SKINNY, skinny_shape=shape, **extra)
     try:
-        assert plan.get("tile") == 18 and plan.get("splits") == 1 and plan.get("skinny_shape") == shape
+        assert plan.get("tile") == agmm.TILE_SKINNY and plan.get("splits") == 1 and plan.get("skinny_shape") == shape
         plan.run(sd, bfull[:, :k], C[:, :n])
         torch.cuda.synchronize()
         first = to_bits(C[:, :n])
@@ -146,7 +148,7 @@ def test_skinny_fullk_tile(case, shape):
 
 
 @pytest.mark.parametrize("shape,tile,skinny_shape", [
-    ((8, 16, 4096, 1792), 18, 5), ((2, 16, 4096, 1024), 18, 0), ((16, 16, 4096, 1792), 15, None)])
+    ((8, 16, 4096, 1792), 10, 5), ((2, 16, 4096, 1024), 10, 0), ((16, 16, 4096, 1792), 7, None)])
 def test_skinny_automatic_choice(shape, tile, skinny_shape):
     """The skinny variant's automatic tile: the whole-k kernel for m <= 128
     (64 x 16 when that gives more workgroups than 32 x 32), the split-K
@@ -164,17 +166,17 @@ def test_skinny_fullk_needs_transposed_b():
     plan = agmm.Plan(2, 16, 64, 64, BF16, False, variant="skinny")
     try:
         with pytest.raises(agmm.AgmmError):
-            plan.set("tile", 18)
+            plan.set("tile", agmm.TILE_SKINNY)
     finally:
         plan.close()
 
 
 def test_skinny_fullk_in_staged_chunks():
-    """Tile 18 under the staged variant: chunk launches map their rows to C
+    """The whole-k skinny tile under the staged variant: chunk launches map their rows to C
     through the chunk's row offset."""
     w, shards, B = make_case(3, 200, 384, 130, BF16, True, seed=2300)
     C, _ = run_variant(w, [to_device(x, BF16) for x in shards], to_device(B, BF16), "staged",
-                       pvalue=1, tile=18)
+                       pvalue=1, tile=agmm.TILE_SKINNY)
     check_against_oracle(w, shards, B, C)
 
 
@@ -217,13 +219,64 @@ def test_workload4_sampled(variant):
     check_against_oracle(w, shards, B, C, rows=rows)
 
 
-def test_workload5_fused_sampled():
+def test_workload4_every_tile():
+    """Workload 4 (fp16, B n x k): two rows of every 256-row block, one in
+    each 128-row wave half, all columns, so every 256 x 256 output tile and
+    every wave's sub-tile is compared with the oracle; fused and unfused
+    (same tile, same k order per element) are bit-identical."""
+    w, shards, B, sd, bd = workload_inputs(4)
+    outs = {}
+    for variant in ("fused", "unfused"):
+        plan = agmm.Plan(w.num_shards, w.m_per_shard, w.k, w.n_local, w.dtype, w.rhs_transpose,
+                         variant=variant)
+        try:
+            C = torch.full((w.m, w.n_local), float("nan"), dtype=torch_dtype(w.dtype), device="cuda")
+            plan.run(sd, bd, C)
+            torch.cuda.synchronize()
+            outs[variant] = (C, plan.get("tile"), plan.get("splits"))
+        finally:
+            plan.close()
+    C = outs["fused"][0]
+    assert not torch.isnan(C.float()).any().item(), "some outputs were never written"
+    check_against_oracle(w, shards, B, C, rows=block_rows(w.m, seed=4))
+    assert outs["fused"][1:] == outs["unfused"][1:]
+    assert torch.equal(C.view(torch.int16), outs["unfused"][0].view(torch.int16))
+
+
+def test_workload5_every_tile_every_variant():
+    """Workload 5, the benchmarked configuration (8 x 4096 x 8192 -> 7168
+    bf16), through the fused, staged (pvalue 2, 2 slots: 8 chunks, each slot
+    reused four times) and unfused paths.  C starts as NaN and no NaN may
+    remain.  The oracle checks two rows of every 256-row block (one in each
+    128-row wave half, at offsets that vary from block to block) over all
+    7168 columns: every one of the 3584 output tiles and every wave's
+    sub-tile.  The three paths use the same tile and the same k order per
+    element, so their outputs must also be bit-identical, which covers every
+    element of the staged and unfused outputs."""
     w, shards, B, sd, bd = workload_inputs(5)
-    C, used = run_variant(w, sd, bd, "fused")
-    rows = sample_rows(w.num_shards, w.m_per_shard, per_shard=2, seed=5)
-    check_against_oracle(w, shards, B, C, rows=rows)
-    # a property that holds at any size: every output finite and C not all zero
-    assert torch.isfinite(C.float()).all().item()
+    rows = block_rows(w.m, seed=5)
+    outs = {}
+    for variant in ("fused", "staged", "unfused"):
+        settings = {"pvalue": 2, "nbuf": 2} if variant == "staged" else {}
+        plan = agmm.Plan(w.num_shards, w.m_per_shard, w.k, w.n_local, w.dtype, w.rhs_transpose,
+                         variant=variant, **settings)
+        try:
+            if variant == "staged":
+                assert plan.get("num_chunks") == 8 and plan.get("num_slots") == 2
+            C = torch.full((w.m, w.n_local), float("nan"), dtype=torch_dtype(w.dtype), device="cuda")
+            plan.run(sd, bd, C)
+            torch.cuda.synchronize()
+            outs[variant] = (plan.get("tile"), plan.get("splits"))
+        finally:
+            plan.close()
+        assert not torch.isnan(C.float()).any().item(), f"{variant}: some outputs were never written"
+        check_against_oracle(w, shards, B, C, rows=rows)
+        if variant == "fused":
+            C_fused = C
+        else:
+            assert outs[variant] == outs["fused"], (variant, outs)
+            assert torch.equal(C.view(torch.int16), C_fused.view(torch.int16)), variant
+            del C
 
 
 # ---------------------------------------------------------------- gather, exact
@@ -355,10 +408,10 @@ def test_fp16_subnormal_outputs():
     assert rel_err(got, ref) <= BOUND[FP16]
 
 
-@pytest.mark.parametrize("tile,splits", [(8, 4), (8, 7), (1, 3), (2, 2), (10, 11), (11, 9), (14, 3), (15, 5)])
+@pytest.mark.parametrize("tile,splits", [(3, 4), (3, 7), (1, 3), (2, 2), (0, 11), (4, 9), (6, 3), (7, 5)])
 def test_split_k_ragged(tile, splits):
     """Split-K partials + fixed-order reduction, with a ragged last k range."""
-    rt = tile in (8, 11, 15)
+    rt = tile in agmm.TILES_NEED_BT
     w, shards, B = make_case(2, 50, 968, 200 if rt else 208, FP16, rt, seed=400 + tile + splits)
     C, used = run_variant(w, [to_device(s, FP16) for s in shards], to_device(B, FP16), "skinny",
                           tile=tile, splits=splits)
@@ -366,7 +419,7 @@ def test_split_k_ragged(tile, splits):
     check_against_oracle(w, shards, B, C)
 
 
-@pytest.mark.parametrize("tile", [16, 17])
+@pytest.mark.parametrize("tile", [8, 9])
 @pytest.mark.parametrize("dtype,rt", [(BF16, False), (BF16, True), (FP16, False), (FP16, True)])
 @pytest.mark.parametrize("splits,k", [(1, 1024), (3, 1024), (1, 1000)])
 def test_mfma16_tiles(tile, dtype, rt, splits, k):
@@ -380,9 +433,9 @@ def test_mfma16_tiles(tile, dtype, rt, splits, k):
 
 
 @pytest.mark.parametrize("variant,tile,splits,rt,pvalue", [
-    ("fused", 13, 3, False, None), ("fused", 1, 0, False, None), ("unfused", 5, 2, True, None),
-    ("fused", 0, 2, True, None), ("fused", 13, 0, True, None),
-    ("staged", 14, 2, False, 1), ("staged", 15, 0, True, 1)])
+    ("fused", 5, 3, False, None), ("fused", 1, 0, False, None), ("unfused", 6, 2, True, None),
+    ("fused", 0, 2, True, None), ("fused", 5, 0, True, None),
+    ("staged", 6, 2, False, 1), ("staged", 7, 0, True, 1)])
 def test_split_k_variants(variant, tile, splits, rt, pvalue):
     """Split-K on the fused, unfused and staged variants (explicit and
     automatic k ranges; staged: per chunk, two chunks with a ragged second
@@ -409,7 +462,7 @@ def test_staged_slot_reuse_alternating_streams(dtype, rt):
     bd = to_device(B, dtype)
     out = {}
     for variant, extra in (("staged", {"pvalue": 1, "nbuf": 2}), ("fused", {})):
-        plan = agmm.Plan(3, 400, 256, 264, dtype, rt, variant=variant, tile=14, splits=1, **extra)
+        plan = agmm.Plan(3, 400, 256, 264, dtype, rt, variant=variant, tile=6, splits=1, **extra)
         try:
             if variant == "staged":
                 assert plan.get("num_chunks") == 4
@@ -441,7 +494,7 @@ def test_strided_inputs(variant, dtype, rt, lds):
     m_s = 40 if variant == "skinny" else 200
     w, shards, B = make_case(3, m_s, 240, 128, dtype, rt, seed=510 + lda)
     plan = agmm.Plan(3, m_s, 240, 128, dtype, rt, variant=variant,
-                     **({"pvalue": 1, "tile": 14} if variant == "staged" else {}))
+                     **({"pvalue": 1, "tile": 6} if variant == "staged" else {}))
     try:
         plan.set("lda", lda)
         plan.set("ldb", ldb)
@@ -518,7 +571,7 @@ def _random_cases(count, seed):
             variant = "fused"
         settings = {"variant": variant}
         if dtype != FP32 and rng.random() < 0.6:
-            tiles = [0, 1, 2, 3, 4, 5, 6, 7, 9, 10, 12, 13, 14, 16, 17] + ([8, 11, 15, 18] if rt else [])
+            tiles = [0, 1, 2, 5, 6, 8, 9] + (list(agmm.TILES_NEED_BT) if rt else [])
             settings["tile"] = int(rng.choice(tiles))
             if variant in ("fused", "unfused", "skinny", "staged") and rng.random() < 0.5:
                 settings["splits"] = int(rng.integers(1, 6))
@@ -564,7 +617,7 @@ def test_repeated_runs_fresh_inputs():
 @pytest.mark.parametrize("variant,settings", [
     ("fused", {}), ("skinny", {}), ("unfused", {}), ("fused", {"splits": 3}),
     ("staged", {"pvalue": 1, "tile": 1, "nbuf": 2}),
-    ("staged", {"pvalue": 1, "tile": 14, "nbuf": 2, "splits": 2})])
+    ("staged", {"pvalue": 1, "tile": 6, "nbuf": 2, "splits": 2})])
 def test_graph_capture_replays(variant, settings):
     """agmm_run captured into a HIP graph (launches, and for the staged plan
     the copy stream and second GEMM stream joined through events) and
@@ -584,6 +637,10 @@ def test_graph_capture_replays(variant, settings):
         with torch.cuda.graph(g):
             plan.run(sd, bd, C)
         torch.cuda.synchronize()
+        assert plan.get("captured") == 1
+        with pytest.raises(agmm.AgmmError) as ei:
+            plan.set("group_m", 8)          # the graph holds the current layout
+        assert ei.value.status == agmm.AGMM_ERR_UNSUPPORTED
         for rep in range(3):
             w2, sh2, B2 = make_case(N, m_s, k, n, dtype, rt, seed=901 + rep)
             for d, h in zip(sd, sh2):
@@ -619,7 +676,7 @@ def test_run_gathered_matches_fused():
 
 
 @pytest.mark.parametrize("variant,dtype,rt,settings", [
-    ("fused", BF16, False, {"tile": 14}), ("staged", FP16, True, {"pvalue": 1, "tile": 14}),
+    ("fused", BF16, False, {"tile": 6}), ("staged", FP16, True, {"pvalue": 1, "tile": 6}),
     ("unfused", BF16, True, {}), ("skinny", BF16, True, {}), ("fused", FP32, False, {}),
     ("fused", BF16, True, {"copy_engine": 1}), ("staged", BF16, False, {"pvalue": 1, "copy_engine": 1}),
     ("unfused", BF16, False, {"copy_engine": 1})])
@@ -658,7 +715,7 @@ def test_staged_copy_engines(copy_engine, nbuf):
     bd = to_device(B, BF16)
     outs = []
     for ce in (0, copy_engine):
-        plan = agmm.Plan(3, 520, 256, 200, BF16, True, variant="staged", pvalue=1, tile=14,
+        plan = agmm.Plan(3, 520, 256, 200, BF16, True, variant="staged", pvalue=1, tile=6,
                          nbuf=nbuf, copy_engine=ce)
         try:
             assert plan.get("num_chunks") == 5 and plan.get("copy_engine") == ce
@@ -689,10 +746,10 @@ def test_group_m_automatic(shape, want):
 
 
 @pytest.mark.parametrize("local_shard", [0, 1, 3])
-@pytest.mark.parametrize("settings", [{"pvalue": 1, "nbuf": 2, "tile": 14},
+@pytest.mark.parametrize("settings", [{"pvalue": 1, "nbuf": 2, "tile": 6},
                                       {"pvalue": 2, "nbuf": 1, "tile": 1},
-                                      {"pvalue": 1, "nbuf": 2, "tile": 14, "splits": 2},
-                                      {"pvalue": 1, "nbuf": 3, "tile": 14, "gemm_streams": 1}])
+                                      {"pvalue": 1, "nbuf": 2, "tile": 6, "splits": 2},
+                                      {"pvalue": 1, "nbuf": 3, "tile": 6, "gemm_streams": 1}])
 def test_staged_local_first(local_shard, settings):
     """The staged variant with the local shard's rows computed first from
     its own buffer (local_first 1) against the same plan without (0): the
@@ -748,6 +805,133 @@ def test_run_rejects_misaligned_pointer():
         assert ei.value.status == agmm.AGMM_ERR_INVALID_ARG
     finally:
         plan.close()
+
+
+def test_set_int_rejection_keeps_the_plan():
+    """A rejected setting (the whole-k skinny tile on a plan whose B is
+    stored k x n) leaves every setting as it was: the plan still runs with
+    its previous tile and computes the oracle's values."""
+    w, shards, B = make_case(2, 16, 64, 64, BF16, False, seed=84)
+    plan = agmm.Plan(2, 16, 64, 64, BF16, False, variant="skinny")
+    try:
+        tile0, ws0 = plan.get("tile"), plan.workspace_bytes()
+        with pytest.raises(agmm.AgmmError) as ei:
+            plan.set("tile", agmm.TILE_SKINNY)
+        assert ei.value.status == agmm.AGMM_ERR_UNSUPPORTED
+        assert plan.get("tile") == tile0 and plan.get("usable") == 1
+        assert plan.workspace_bytes() == ws0
+        C = plan.run([to_device(x, BF16) for x in shards], to_device(B, BF16))
+        torch.cuda.synchronize()
+    finally:
+        plan.close()
+    check_against_oracle(w, shards, B, C)
+
+
+def test_set_int_oom_restores_previous_layout(monkeypatch):
+    """A reconfiguration whose workspace cannot be allocated (test hook: no
+    allocation larger than the current workspace) fails with AGMM_ERR_OOM
+    and leaves the plan with its previous settings and a workspace for them:
+    runs stay correct."""
+    w, shards, B = make_case(3, 200, 256, 136, BF16, True, seed=85)
+    sd = [to_device(x, BF16) for x in shards]
+    bd = to_device(B, BF16)
+    plan = agmm.Plan(3, 200, 256, 136, BF16, True, variant="unfused")
+    try:
+        assert plan.get("splits") == 1
+        # split-K adds [2][600][136] fp32 partial sums to the [600, 256] operand
+        monkeypatch.setenv("AGMM_TEST_FAIL_ALLOC", str(plan.workspace_bytes()))
+        with pytest.raises(agmm.AgmmError) as ei:
+            plan.set("splits", 2)
+        assert ei.value.status == agmm.AGMM_ERR_OOM
+        monkeypatch.delenv("AGMM_TEST_FAIL_ALLOC")
+        assert plan.get("usable") == 1
+        assert plan.get("variant_used") == agmm.VARIANTS["unfused"] and plan.get("splits") == 1
+        C = torch.full((w.m, w.n_local), float("nan"), dtype=torch.bfloat16, device="cuda")
+        plan.run(sd, bd, C)
+        torch.cuda.synchronize()
+    finally:
+        plan.close()
+    check_against_oracle(w, shards, B, C)
+
+
+def test_set_int_oom_unrecoverable_plan_refuses_runs(monkeypatch):
+    """When neither the new nor the previous workspace can be allocated the
+    plan is marked unusable: every later call fails with the allocation's
+    status and launches nothing (C keeps its NaN fill)."""
+    w, shards, B = make_case(2, 300, 256, 128, BF16, False, seed=86)
+    sd = [to_device(x, BF16) for x in shards]
+    bd = to_device(B, BF16)
+    plan = agmm.Plan(2, 300, 256, 128, BF16, False, variant="unfused")
+    try:
+        monkeypatch.setenv("AGMM_TEST_FAIL_ALLOC", "1")
+        with pytest.raises(agmm.AgmmError) as ei:
+            plan.set("splits", 2)          # a larger workspace: ring plus partials
+        assert ei.value.status == agmm.AGMM_ERR_OOM
+        monkeypatch.delenv("AGMM_TEST_FAIL_ALLOC")
+        assert plan.get("usable") == 0
+        C = torch.full((w.m, w.n_local), float("nan"), dtype=torch.bfloat16, device="cuda")
+        for call in (lambda: plan.run(sd, bd, C), lambda: plan.run_gathered(torch.cat(sd), bd, C),
+                     lambda: plan.run_gather_out(sd, bd, C), lambda: plan.set("splits", 1)):
+            with pytest.raises(agmm.AgmmError) as ei:
+                call()
+            assert ei.value.status == agmm.AGMM_ERR_OOM
+        torch.cuda.synchronize()
+        assert torch.isnan(C.float()).all().item()
+    finally:
+        plan.close()
+
+
+def _spin_cycles_per_ms():
+    """Rate of torch's bounded spin kernel (torch.cuda._sleep) on this GPU.
+    The kernel runs once untimed first: the first launch in a process also
+    loads its code, and that host-side delay would land between the events."""
+    torch.cuda._sleep(1000)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    torch.cuda._sleep(4_000_000)
+    e.record()
+    torch.cuda.synchronize()
+    return 4_000_000 / max(s.elapsed_time(e), 1e-3)
+
+
+@pytest.mark.parametrize("variant,settings", [
+    ("staged", {"pvalue": 1, "nbuf": 2, "tile": 6}),            # 4 chunks through 2 slots
+    ("fused", {"tile": 1, "splits": 3}),                         # split-K partials
+    ("skinny", {"tile": 7, "splits": 4})])
+def test_serial_calls_on_two_streams_are_ordered(variant, settings):
+    """Call 1 on stream s1 (queued behind a ~150 ms spin kernel), then at once
+    call 2 with other inputs on stream s2, no host synchronisation between
+    them.  The plan orders call 2 after call 1 (it shares the ring slots or
+    the split-K partials), so call 2 cannot have finished while s1 is still
+    spinning, and both outputs match their own oracle."""
+    m_s = 24 if variant == "skinny" else 400
+    cases = [make_case(3, m_s, 512, 264, BF16, True, seed=2500 + i) for i in range(2)]
+    dev = [([to_device(x, BF16) for x in sh], to_device(B, BF16)) for _, sh, B in cases]
+    plan = agmm.Plan(3, m_s, 512, 264, BF16, True, variant=variant, **settings)
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    Cs = [torch.full((3 * m_s, 264), float("nan"), dtype=torch.bfloat16, device="cuda") for _ in range(2)]
+    try:
+        if variant == "staged":
+            assert plan.get("num_chunks") == 4 and plan.get("num_slots") == 2
+        else:
+            assert plan.get("splits") > 1
+        cycles = int(150 * _spin_cycles_per_ms())
+        torch.cuda.synchronize()
+        done2 = torch.cuda.Event()
+        with torch.cuda.stream(s1):
+            torch.cuda._sleep(cycles)
+            plan.run(dev[0][0], dev[0][1], Cs[0], stream=s1)
+        with torch.cuda.stream(s2):
+            plan.run(dev[1][0], dev[1][1], Cs[1], stream=s2)
+            done2.record(s2)
+        time.sleep(0.03)
+        assert not done2.query(), "call 2 finished while call 1 was still queued behind the spin"
+        torch.cuda.synchronize()
+    finally:
+        plan.close()
+    for (w, sh, B), C in zip(cases, Cs):
+        check_against_oracle(w, sh, B, C)
 
 
 def test_oom_hook_reports_status(monkeypatch):
