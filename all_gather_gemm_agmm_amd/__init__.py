@@ -53,6 +53,7 @@ EXPORTS = [
     ("agmm_plan_timing_read", _ci, [_vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_i64)]),
     ("agmm_plan_timing_end", _ci, [_vp]),
     ("agmm_plan_destroy", None, [_vp]),
+    ("agmm_run_noalloc", _ci, [_ci, _i64, _i64, _i64, _ci, _ci, ctypes.POINTER(_vp), _vp, _vp, _vp]),
     ("agmm_last_status", _ci, []),
     ("agmm_last_error", _cc, []),
     ("agmm_version", _cc, []),
@@ -182,6 +183,33 @@ def agmm_plan_timing_end(plan) -> int:
 def agmm_plan_destroy(plan) -> None:
     if plan:
         load_library().agmm_plan_destroy(plan)
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def agmm_run_noalloc(num_shards, m_per_shard, k, n_local, dtype, rhs_transpose,
+                     shard_ptrs: Sequence[int], B: int, C: int, stream: int) -> int:
+    return _check(load_library().agmm_run_noalloc(num_shards, m_per_shard, k, n_local, dtype,
+                                                  int(bool(rhs_transpose)), _ptr_table(shard_ptrs),
+                                                  B, C, stream))
+
+
+def run_noalloc(shards, B, C, rhs_transpose: bool, stream=None):
+    """agmm_run_noalloc on torch tensors: dense row-major shards [m_s, k], B
+    [k, n] (or [n, k] with rhs_transpose) and a caller-provided C [m, n]."""
+    m_s, k = shards[0].shape
+    n = B.shape[0] if rhs_transpose else B.shape[1]
+    dtype = {"torch.bfloat16": AGMM_BF16, "torch.float16": AGMM_FP16,
+             "torch.float32": AGMM_FP32}[str(B.dtype)]
+    for t in list(shards) + [B, C]:
+        if not t.is_contiguous():
+            raise ValueError("agmm_run_noalloc takes dense row-major tensors")
+    if tuple(C.shape) != (len(shards) * m_s, n):
+        raise ValueError(f"C has shape {tuple(C.shape)}, expected {(len(shards) * m_s, n)}")
+    agmm_run_noalloc(len(shards), m_s, k, n, dtype, rhs_transpose, [s.data_ptr() for s in shards],
+                     B.data_ptr(), C.data_ptr(), _stream_handle(stream))
+    return C
 
 
 def agmm_last_status() -> int:

@@ -35,6 +35,7 @@ SOURCES = {
     "gather_f32.hip": [],
     "gemm_mfma.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
     "skinny.hip": [],
+    "noalloc.hip": [],
 }
 
 

@@ -237,23 +237,20 @@ int pick_group_m(int64_t nrb, int64_t ncb) {
   const int64_t per = std::min<int64_t>(tiles, cdiv(tiles, 8));
   int best = 4;
   int64_t best_cost = INT64_MAX;
-  std::vector<char> rows, cols;
   for (int g : {4, 8, 2, 16, 1}) {
-    rows.assign((size_t)nrb, 0);
-    cols.assign((size_t)ncb, 0);
-    const int64_t gsz = (int64_t)g * ncb;
-    for (int64_t t = 0; t < per; ++t) {
-      const int64_t grp = t / gsz, first = grp * g;
-      const int64_t rows_here = std::min<int64_t>(nrb - first, g);
-      const int64_t in = t - grp * gsz;
-      rows[(size_t)(first + in % rows_here)] = 1;
-      cols[(size_t)(in / rows_here)] = 1;
+    // tiles [0, per) walk groups of g row blocks (the last one shorter),
+    // column by column: a group's first `take` tiles touch min(take, rows)
+    // of its row blocks and its first ceil(take / rows) column blocks
+    int64_t t = 0, rows = 0, cols = 0;
+    for (int64_t grp = 0; t < per; ++grp) {
+      const int64_t rh = std::min<int64_t>(nrb - grp * g, g);
+      const int64_t take = std::min<int64_t>(rh * ncb, per - t);
+      rows += std::min(take, rh);
+      cols = std::max(cols, cdiv(take, rh));
+      t += take;
     }
-    int64_t cost = 0;
-    for (char c : rows) cost += c;
-    for (char c : cols) cost += c;
-    if (cost < best_cost) {
-      best_cost = cost;
+    if (rows + cols < best_cost) {
+      best_cost = rows + cols;
       best = g;
     }
   }
@@ -287,10 +284,10 @@ void ring_order(const agmm_plan* p, const Settings& s, int64_t rpg, int64_t row_
   std::stable_sort(out.begin(), out.end(), [&](int32_t a, int32_t b) { return key[a] < key[b]; });
 }
 
-// Derive the layout of a plan from its problem and the settings: variant,
-// tiles, chunks, split-K, sizes and tile orders.  Host only; touches
-// nothing of the plan.
-int derive(const agmm_plan* p, const Settings& s, Layout& L) {
+// Derive the launch layout of a plan from its problem and the settings:
+// variant, tiles, chunks, split-K and sizes (not the tile-order tables).
+// Host only; touches nothing of the plan and allocates nothing.
+int derive_launch(const agmm_plan* p, const Settings& s, Layout& L) {
   const int64_t e = elem_bytes(p->dtype);
   // variant
   int v = s.variant;
@@ -398,8 +395,13 @@ int derive(const agmm_plan* p, const Settings& s, Layout& L) {
     const int64_t part_m = v == AGMM_VARIANT_STAGED ? std::max<int64_t>(launch_m, p->m_s) : launch_m;
     if (L.splits_used > 1) L.part_bytes = (size_t)L.splits_used * part_m * p->n * sizeof(float);
   }
+  return AGMM_OK;
+}
 
-  // tile orders (one table per chunk)
+// derive_launch plus the tile-order tables (one per chunk).
+int derive(const agmm_plan* p, const Settings& s, Layout& L) {
+  const int rc = derive_launch(p, s, L);
+  if (rc != AGMM_OK) return rc;
   L.h_order.clear();
   L.order_off.clear();
   L.order_len.clear();
@@ -1339,6 +1341,54 @@ void agmm_plan_destroy(agmm_plan_t p) {
   if (p->compute2) hipStreamDestroy(p->compute2);
   if (p->copy_stream) hipStreamDestroy(p->copy_stream);
   delete p;
+}
+
+int agmm_run_noalloc(int num_shards, int64_t m_per_shard, int64_t k, int64_t n_local, int dtype,
+                     int rhs_transpose, const void* const* shard_ptrs, const void* B, void* C,
+                     void* stream) {
+  static_assert(AGMM_NOALLOC_SCRATCH_BYTES == agmm::kNoallocScratchBytes, "scratch size");
+  int rc = validate(num_shards, m_per_shard, k, n_local, dtype, rhs_transpose);
+  if (rc != AGMM_OK) return rc;
+  // a plan on the stack: the problem and a default launch layout, no
+  // workspace, no streams, no events, no tile-order table
+  agmm_plan p;
+  p.N = num_shards;
+  p.m_s = m_per_shard;
+  p.k = k;
+  p.n = n_local;
+  p.m = (int64_t)num_shards * m_per_shard;
+  p.dtype = dtype;
+  p.rt = rhs_transpose;
+  rc = check_ptrs(&p, shard_ptrs, B, C);
+  if (rc != AGMM_OK) return rc;
+  hipError_t err = hipGetDevice(&p.device);
+  if (err != hipSuccess) return hip_err(err, "hipGetDevice");
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, p.device) == hipSuccess && cus > 0)
+    p.cu_count = cus;
+  rc = derive_launch(&p, p.s, p.L);
+  if (rc != AGMM_OK) return rc;
+  if (p.L.variant_used != AGMM_VARIANT_FUSED && p.L.variant_used != AGMM_VARIANT_SKINNY)
+    return set_err(AGMM_ERR_UNSUPPORTED, "agmm_run_noalloc runs the fused and skinny paths only");
+  if (p.L.part_bytes > AGMM_NOALLOC_SCRATCH_BYTES)
+    return set_err(AGMM_ERR_UNSUPPORTED,
+                   "this problem's split-K partial sums need %zu bytes of scratch; the "
+                   "no-allocation entry point has %zu (use a plan)",
+                   p.L.part_bytes, (size_t)AGMM_NOALLOC_SCRATCH_BYTES);
+  if (p.L.part_bytes > 0) {
+    void* scratch = nullptr;
+    err = agmm::noalloc_scratch(&scratch);
+    if (err != hipSuccess) return hip_err(err, "locating the no-allocation scratch");
+    p.partials = static_cast<float*>(scratch);
+  }
+  // every partial sum a launch reads was written by that launch's own split
+  // workgroups first, so the scratch needs no clearing between calls
+  Call c;
+  c.s = static_cast<hipStream_t>(stream);
+  agmm::GemmProblem g = base_problem(&p, shard_rows(&p, shard_ptrs), p.m, B, C, -1);
+  with_splits(&p, g);
+  rc = launch_gemm(&p, c, g, c.s);
+  return rc == AGMM_OK ? ok() : rc;
 }
 
 int agmm_last_status(void) { return g_status; }

@@ -115,4 +115,11 @@ struct GatherProblem {
 };
 hipError_t launch_gather(const GatherProblem& p, int max_workgroups, hipStream_t stream);
 
+// Size of the device scratch of the no-allocation entry point (one per GPU,
+// held for the life of the process; equal to AGMM_NOALLOC_SCRATCH_BYTES).
+constexpr size_t kNoallocScratchBytes = size_t(32) << 20;
+// Device address of the current GPU's scratch (looked up on the first call
+// on each device, then cached).
+hipError_t noalloc_scratch(void** ptr);
+
 }  // namespace agmm

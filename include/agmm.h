@@ -328,6 +328,33 @@ int agmm_plan_timing_end(agmm_plan_t plan);
  * destroyed or has finished its last replay: the graph uses its workspace. */
 void agmm_plan_destroy(agmm_plan_t plan);
 
+/*
+ * For callers that cannot allocate device memory (code being captured into a
+ * graph, tight serving loops, harnesses that forbid hipMalloc): the work of
+ * agmm_run on a newly created plan for this problem (automatic variant, tile
+ * and k split; the fused and skinny paths only), with no plan and nothing
+ * allocated.  The split-K partial sums go into a scratch array of
+ * AGMM_NOALLOC_SCRATCH_BYTES that the library keeps in the memory of every
+ * GPU it runs on until the process ends; its device address is looked up on
+ * the first call on each device (make that first call outside graph
+ * capture).  Arguments, layouts (dense rows), alignment and stream rules are
+ * agmm_run's.  Tile visit order is the natural one (the values do not depend
+ * on it), so C is bit-identical to agmm_run's on a default plan.
+ * Every call on one GPU shares that GPU's scratch and leaves its partial sums
+ * there: calls whose work overlaps on one GPU (different streams without an
+ * ordering between them, or host threads) race and may return wrong values;
+ * order them on one stream.  Nothing needs clearing between calls: every
+ * partial sum a call reads was written by that call.
+ * Returns AGMM_OK, agmm_plan_validate's statuses, agmm_run's pointer
+ * statuses, AGMM_ERR_UNSUPPORTED when the problem resolves to the staged or
+ * unfused path or its partial sums need more than
+ * AGMM_NOALLOC_SCRATCH_BYTES (nothing is launched then), or AGMM_ERR_HIP.
+ */
+#define AGMM_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+int agmm_run_noalloc(int num_shards, int64_t m_per_shard, int64_t k, int64_t n_local, int dtype,
+                     int rhs_transpose, const void *const *shard_ptrs, const void *B, void *C,
+                     void *stream);
+
 /* Thread-local status / message of the last failing call (AGMM_OK / "" if none). */
 int agmm_last_status(void);
 const char *agmm_last_error(void);
