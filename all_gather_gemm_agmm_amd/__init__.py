@@ -28,10 +28,11 @@ VARIANT_NAMES = {v: k for k, v in VARIANTS.items()}
 # Values of the plan key "tile" (include/agmm.h lists what each one is).
 TILES = {"256x256": 0, "128x128": 1, "256x128": 2, "128x64": 3, "128x64_s8": 4,
          "256x256_ring": 5, "128x128_ring": 6, "128x64_ring": 7, "256x256_m16": 8,
-         "128x128_m16": 9, "skinny": 10}
+         "128x128_m16": 9, "skinny": 10, "256x224_m16": 11}
 NUM_TILES = len(TILES)
 TILE_SKINNY = TILES["skinny"]
-TILES_NEED_BT = (TILES["128x64"], TILES["128x64_s8"], TILES["128x64_ring"], TILE_SKINNY)
+TILES_NEED_BT = (TILES["128x64"], TILES["128x64_s8"], TILES["128x64_ring"], TILE_SKINNY,
+                 TILES["256x224_m16"])
 
 # (name, restype, argtypes) of every symbol include/agmm.h declares.
 _vp, _i64, _ci, _cc = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_char_p

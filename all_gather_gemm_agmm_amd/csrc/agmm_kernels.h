@@ -69,11 +69,13 @@ enum TileCfg : int {
   kTile256x256m16 = 8,   // part ring, 256x256, on 16x16x32 MFMAs (automatic for k >= 256)
   kTile128x128m16 = 9,   // part ring, 128x128, on 16x16x32 MFMAs
   kTileSkinny = 10,      // whole k per workgroup, wave-private LDS rings (launch_skinny_fullk); B n x k only
-  kTileCount = 11,
+  kTile256x224m16 = 11,  // part ring, 256x224 on 16x16x32 MFMAs (7 column blocks per wave); B n x k only
+  kTileCount = 12,
 };
 // Tiles that read B only as stored n x k (rhs_transpose).
 constexpr bool tile_needs_bt(int cfg) {
-  return cfg == kTile128x64 || cfg == kTile128x64s8 || cfg == kTile128x64r5 || cfg == kTileSkinny;
+  return cfg == kTile128x64 || cfg == kTile128x64s8 || cfg == kTile128x64r5 || cfg == kTileSkinny ||
+         cfg == kTile256x224m16;
 }
 int tile_bm(int cfg);
 int tile_bn(int cfg);

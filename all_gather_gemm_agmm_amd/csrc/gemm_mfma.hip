@@ -909,19 +909,21 @@ void gemm_m16_kernel(GemmProblem p) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) acc[i][j][e] = 0.0f;
 
-  // A fragments of k32 step `st`, and B fragments of column blocks
-  // 4h .. 4h+3 (one half of the wave's columns) of step `st`
+  // A fragments of k32 step `st`, and B fragments of one half of the wave's
+  // column blocks of step `st`: half 0 is blocks [0, FH0), half 1 [FH0, FN)
+  // (FH0 = FH1 when FN is even; 4 and 3 for the 7 blocks of a 112-column
+  // sub-tile)
   auto read_a = [&](const char* sa, int st, u32x4_t* af) {
 #pragma unroll
     for (int f = 0; f < FM; ++f)
       af[f] = *reinterpret_cast<const u32x4_t*>(sa + a_off[f] + (((4 * st) ^ a_x[f]) << 4));
   };
-  constexpr int FH = FN / 2;   // column blocks per half
-  static_assert(FN % 2 == 0, "two halves of column blocks");
+  constexpr int FH0 = (FN + 1) / 2, FH1 = FN - FH0;   // column blocks of each half
+  static_assert(FH1 >= 1, "two halves of column blocks");
   auto read_b = [&](const char* sb, int st, int h, u32x4_t* bfr) {
 #pragma unroll
-    for (int q = 0; q < FH; ++q) {
-      const int f = h * FH + q;
+    for (int q = 0; q < (h ? FH1 : FH0); ++q) {
+      const int f = (h ? FH0 : 0) + q;
       if constexpr (BT) {
         bfr[q] = *reinterpret_cast<const u32x4_t*>(sb + b_off[f] + (((4 * st) ^ b_x[f]) << 4));
       } else {
@@ -955,15 +957,16 @@ void gemm_m16_kernel(GemmProblem p) {
   // tracks itself.
   constexpr bool kTied = OCC == 1;
   auto mfma_half = [&](auto tied, const u32x4_t* af, const u32x4_t* bfr, int h) {
+    const int c0 = h ? FH0 : 0;
 #pragma unroll
-    for (int q = 0; q < FH; ++q)
+    for (int q = 0; q < (h ? FH1 : FH0); ++q)
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
-        if constexpr (kTied && decltype(tied)::value) mfma16<DT>(acc[i][h * FH + q], bfr[q], af[i]);
-        else acc[i][h * FH + q] = mfma16_builtin<DT>(bfr[q], af[i], acc[i][h * FH + q]);
+        if constexpr (kTied && decltype(tied)::value) mfma16<DT>(acc[i][c0 + q], bfr[q], af[i]);
+        else acc[i][c0 + q] = mfma16_builtin<DT>(bfr[q], af[i], acc[i][c0 + q]);
       }
   };
-  constexpr int kMfmaPerHalf = FM * FH;
+  constexpr int kMfmaHalf0 = FM * FH0, kMfmaHalf1 = FM * FH1;   // MFMAs of each half
 
   // ---- main loop: the part ring (see gemm_mfma_kernel) -----------------------
   constexpr int L = T::A_IPW;
@@ -1013,7 +1016,7 @@ void gemm_m16_kernel(GemmProblem p) {
     // Every read of this k-tile's slots is issued before the sync, which also
     // waits for them (lgkmcnt), so the loads after it may overwrite them.
     // A part loads ride on half-steps 0-2, the B part on half-step 3.
-    u32x4_t A0[FM], A1[FM], Ba[FH], Bb[FH];
+    u32x4_t A0[FM], A1[FM], Ba[FH0], Bb[FH0];
     if constexpr (kTied && FAST) mfma16_drain(acc);
     put_a(0, 0, 0, L);
     put_b(1, 0);
@@ -1024,11 +1027,11 @@ void gemm_m16_kernel(GemmProblem p) {
     read_b(smem + PB, 0, 0, Ba);
     read_a(smem, 0, A0);
     int sa_slot = 0, sb_slot = 1;
-    auto interleave = [&](int nread, int nload) {
+    auto interleave = [&](int nmfma, int nread, int nload) {
       // MFMA / LDS read pairs first (the next half-step waits on the reads),
       // then the global->LDS loads spread over the remaining MFMAs
-      const int nr = nread < kMfmaPerHalf ? nread : kMfmaPerHalf;
-      const int left = kMfmaPerHalf - nr;
+      const int nr = nread < nmfma ? nread : nmfma;
+      const int left = nmfma - nr;
 #pragma unroll
       for (int q = 0; q < nr; ++q) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -1042,7 +1045,7 @@ void gemm_m16_kernel(GemmProblem p) {
           __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
       }
     };
-    constexpr int kReadsB = BT ? FH : 2 * FH;   // LDS read instructions per B half
+    constexpr int kReadsB0 = BT ? FH0 : 2 * FH0, kReadsB1 = BT ? FH1 : 2 * FH1;   // LDS reads per B half
     if constexpr (kTied && FAST) {
       // The compiler cannot see the tied MFMAs as MFMAs, so the interleaving
       // is written out and pinned: after MFMA number x of a half-step comes
@@ -1050,16 +1053,17 @@ void gemm_m16_kernel(GemmProblem p) {
       // the next half-step needs them; then the global->LDS loads spread
       // over the remaining MFMAs), each group fenced from the next.
       auto half = [&](const u32x4_t* af, const u32x4_t* bfr, int h, int nread, int nload, auto&& op) {
+        const int c0 = h ? FH0 : 0, nm = h ? kMfmaHalf1 : kMfmaHalf0;
 #pragma unroll
-        for (int q = 0; q < FH; ++q)
+        for (int q = 0; q < (h ? FH1 : FH0); ++q)
 #pragma unroll
           for (int i = 0; i < FM; ++i) {
             const int x = q * FM + i;
-            mfma16<DT>(acc[i][h * FH + q], bfr[q], af[i]);
+            mfma16<DT>(acc[i][c0 + q], bfr[q], af[i]);
             if (x < nread) {
               op(x);
             } else {
-              const int left = kMfmaPerHalf - nread, y = x - nread;
+              const int left = nm - nread, y = x - nread;
 #pragma unroll
               for (int r = y * nload / left; r < (y + 1) * nload / left; ++r) op(nread + r);
             }
@@ -1067,7 +1071,8 @@ void gemm_m16_kernel(GemmProblem p) {
           }
       };
       constexpr int L0 = L / 3, L1 = (2 * L) / 3 - L / 3, L2 = L - (2 * L) / 3;
-      static_assert(FM + FH <= kMfmaPerHalf, "one read per MFMA");
+      // one LDS read per MFMA, and MFMAs left over for the loads
+      static_assert(FH1 + (L0 > 0 ? 1 : 0) <= kMfmaHalf0 && FM + FH0 < kMfmaHalf1, "reads per MFMA");
       for (int it = 0; it < nk; ++it) {
         const char* sa = smem + sa_slot * PB;
         const char* sb = smem + sb_slot * PB;
@@ -1075,20 +1080,20 @@ void gemm_m16_kernel(GemmProblem p) {
         const int na = sa_slot + 2 >= 5 ? sa_slot - 3 : sa_slot + 2;
         const int nb = sb_slot + 2 >= 5 ? sb_slot - 3 : sb_slot + 2;
         // (0,0): MFMAs A0 x Ba; reads Bb (step 0, half 1); A loads 0 .. L0-1
-        half(A0, Ba, 0, FH, L0, [&](int k) {
-          if (k < FH) Bb[k] = read_b_one(sb, 0, FH + k);
-          else put_a(a_new, it + 2, k - FH, k - FH + 1);
+        half(A0, Ba, 0, FH1, L0, [&](int k) {
+          if (k < FH1) Bb[k] = read_b_one(sb, 0, FH0 + k);
+          else put_a(a_new, it + 2, k - FH1, k - FH1 + 1);
         });
         // (0,1): MFMAs A0 x Bb; reads A1 (step 1), Ba (step 1, half 0); A loads L0 ..
-        half(A0, Bb, 1, FM + FH, L1, [&](int k) {
+        half(A0, Bb, 1, FM + FH0, L1, [&](int k) {
           if (k < FM) A1[k] = read_a_one(sa, 1, k);
-          else if (k < FM + FH) Ba[k - FM] = read_b_one(sb, 1, k - FM);
-          else put_a(a_new, it + 2, L0 + k - FM - FH, L0 + k - FM - FH + 1);
+          else if (k < FM + FH0) Ba[k - FM] = read_b_one(sb, 1, k - FM);
+          else put_a(a_new, it + 2, L0 + k - FM - FH0, L0 + k - FM - FH0 + 1);
         });
         // (1,0): MFMAs A1 x Ba; reads Bb (step 1, half 1); the last A loads
-        half(A1, Ba, 0, FH, L2, [&](int k) {
-          if (k < FH) Bb[k] = read_b_one(sb, 1, FH + k);
-          else put_a(a_new, it + 2, L0 + L1 + k - FH, L0 + L1 + k - FH + 1);
+        half(A1, Ba, 0, FH1, L2, [&](int k) {
+          if (k < FH1) Bb[k] = read_b_one(sb, 1, FH0 + k);
+          else put_a(a_new, it + 2, L0 + L1 + k - FH1, L0 + L1 + k - FH1 + 1);
         });
         // (1,1): sync; MFMAs A1 x Bb; reads Ba, A0 of the next k-tile; B loads
         wait_vmcnt<L>();
@@ -1096,10 +1101,10 @@ void gemm_m16_kernel(GemmProblem p) {
         block_barrier();
         const char* sa2 = smem + na * PB;
         const char* sb2 = smem + nb * PB;
-        half(A1, Bb, 1, FH + FM, LB, [&](int k) {
-          if (k < FH) Ba[k] = read_b_one(sb2, 0, k);
-          else if (k < FH + FM) A0[k - FH] = read_a_one(sa2, 0, k - FH);
-          else put_b_one(sa_slot, it + 2, k - FH - FM);
+        half(A1, Bb, 1, FH0 + FM, LB, [&](int k) {
+          if (k < FH0) Ba[k] = read_b_one(sb2, 0, k);
+          else if (k < FH0 + FM) A0[k - FH0] = read_a_one(sa2, 0, k - FH0);
+          else put_b_one(sa_slot, it + 2, k - FH0 - FM);
         });
         sa_slot = na;
         sb_slot = nb;
@@ -1116,18 +1121,18 @@ void gemm_m16_kernel(GemmProblem p) {
       read_b(sb, 0, 1, Bb);
       put_a(a_new, it + 2, 0, L0);
       mfma_half(tag, A0, Ba, 0);
-      interleave(kReadsB, L0);
+      interleave(kMfmaHalf0, kReadsB1, L0);
       // (0,1)
       read_a(sa, 1, A1);
       read_b(sb, 1, 0, Ba);
       put_a(a_new, it + 2, L0, L0 + L1);
       mfma_half(tag, A0, Bb, 1);
-      interleave(FM + kReadsB, L1);
+      interleave(kMfmaHalf1, FM + kReadsB0, L1);
       // (1,0)
       read_b(sb, 1, 1, Bb);
       put_a(a_new, it + 2, L0 + L1, L);
       mfma_half(tag, A1, Ba, 0);
-      interleave(kReadsB, L2);
+      interleave(kMfmaHalf0, kReadsB1, L2);
       // (1,1)
       wait_vmcnt<L>();
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -1136,7 +1141,7 @@ void gemm_m16_kernel(GemmProblem p) {
       read_a(smem + na * PB, 0, A0);
       put_b(sa_slot, it + 2);
       mfma_half(tag, A1, Bb, 1);
-      interleave(kReadsB + FM, LB);
+      interleave(kMfmaHalf1, kReadsB0 + FM, LB);
       sa_slot = na;
       sb_slot = nb;
     }
@@ -1150,6 +1155,9 @@ void gemm_m16_kernel(GemmProblem p) {
   const int hi = g4 & 1;   // which half of a 16-byte (8-column) chunk
   constexpr int kRowB = BN * 2;
   constexpr int kChunks = kRowB / 16;
+  // staged C rows: chunk c of row r at c ^ (r mod kSwz), kSwz the largest
+  // power of two dividing the chunks per row (so positions stay in the row)
+  constexpr int kSwz = kChunks & -kChunks;
   static_assert(T::LDS_BYTES >= BM * kRowB, "LDS too small to stage the C tile");
   bool staged = false;
   if constexpr (!SPLIT) {
@@ -1165,7 +1173,7 @@ void gemm_m16_kernel(GemmProblem p) {
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
         const int c = wn * T::TN + j * 16 + 4 * g4;
-        const int pos = (c >> 3) ^ (r & (kChunks - 1));
+        const int pos = (c >> 3) ^ (r & (kSwz - 1));
         u32x2_t v;
         v[0] = pack2<DT>(acc[i][j][0], acc[i][j][1]);
         v[1] = pack2<DT>(acc[i][j][2], acc[i][j][3]);
@@ -1173,16 +1181,16 @@ void gemm_m16_kernel(GemmProblem p) {
       }
     }
     block_barrier();
-    constexpr int kRowsPerPass = T::THREADS / kChunks;
+    constexpr int kRowsPerPass = T::THREADS / kChunks;   // threads past whole rows stay idle
     const int ch = tid % kChunks;
-    int r = tid / kChunks;
+    int r = tid < kRowsPerPass * kChunks ? tid / kChunks : BM;
     int gi = m0 + r;
     int g = gi / p.rows.rows_per_group;
     int t = gi - g * p.rows.rows_per_group;
     uint16_t* cbase = static_cast<uint16_t*>(p.c) + n0 + ch * 8;
 #pragma unroll 4
     for (; r < BM; r += kRowsPerPass) {
-      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(smem + r * kRowB + ((ch ^ (r & (kChunks - 1))) << 4));
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(smem + r * kRowB + ((ch ^ (r & (kSwz - 1))) << 4));
       const int64_t crow = (int64_t)g * p.rows.c_group_rows + p.rows.c_row_off + t;
       __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(cbase + crow * p.ldc));
       t += kRowsPerPass;
@@ -1322,6 +1330,13 @@ hipError_t launch_m16_one(const GemmProblem& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// B stored n x k only (tiles whose B rows are not a power-of-two of chunks)
+template <int BM, int BN, int BK, int WAVES, int OCC>
+hipError_t launch_m16_bt(const GemmProblem& p, int dtype, hipStream_t s) {
+  return dtype == kDtypeBf16 ? launch_m16_one<BM, BN, BK, kDtypeBf16, true, WAVES, OCC>(p, s)
+                             : launch_m16_one<BM, BN, BK, kDtypeFp16, true, WAVES, OCC>(p, s);
+}
+
 template <int BM, int BN, int BK, int WAVES, int OCC>
 hipError_t launch_m16(const GemmProblem& p, int dtype, bool bt, hipStream_t s) {
   if (dtype == kDtypeBf16)
@@ -1348,6 +1363,7 @@ constexpr TileInfo kTiles[kTileCount] = {
     {256, 256, 64, 5, 4, 1},   // kTile256x256m16:   part ring on 16x16x32 MFMAs
     {128, 128, 64, 5, 4, 2},   // kTile128x128m16:   same, two workgroups per CU
     {32, 32, 64, 4, 8, 1},     // kTileSkinny:       skinny kernel, whole k (launch_skinny_fullk)
+    {256, 224, 64, 5, 4, 1},   // kTile256x224m16:   16x16x32 part ring, 7 column blocks per wave; B n x k only
 };
 
 int tile_bm(int cfg) { return kTiles[cfg].bm; }
@@ -1379,6 +1395,7 @@ hipError_t launch_gemm_mfma(const GemmProblem& p, int tile_cfg, int dtype, bool 
                                  : launch_one<128, 64, 64, kDtypeFp16, true, 5, 4, 2, kLoopParts>(p, stream);
     case kTile256x256m16: return launch_m16<256, 256, 64, 4, 1>(p, dtype, rhs_transpose, stream);
     case kTile128x128m16: return launch_m16<128, 128, 64, 4, 2>(p, dtype, rhs_transpose, stream);
+    case kTile256x224m16: return launch_m16_bt<256, 224, 64, 4, 1>(p, dtype, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -218,7 +218,10 @@ int agmm_plan_autotune(agmm_plan_t plan, const void *const *shard_ptrs, const vo
  *                   16x16x32 MFMAs (the automatic choices for k >= 256),
  *                   10 the whole-k skinny kernel (rhs_transpose only; tile
  *                   from "skinny_shape"; no k split; the automatic skinny
- *                   choice for m <= 128; 7 for 128 < m <= 256).  A tile that
+ *                   choice for m <= 128; 7 for 128 < m <= 256), 11 256x224
+ *                   in the 16x16x32 ring (rhs_transpose only; automatic where
+ *                   its 224-column tiles fill whole rounds of workgroups that
+ *                   256x256 tiles would leave partly idle).  A tile that
  *                   needs rhs_transpose on a plan without it is rejected
  *                   with AGMM_ERR_UNSUPPORTED.
  *   "splits"        0: automatic, else k-splits (fp32 partial sums, then a

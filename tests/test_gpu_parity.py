@@ -162,6 +162,22 @@ def test_skinny_automatic_choice(shape, tile, skinny_shape):
         plan.close()
 
 
+@pytest.mark.parametrize("shape,variant,want", [
+    ((8, 1024, 8192, 3584, FP16, True), "fused", 11), ((8, 1024, 8192, 3584, FP16, True), "staged", 11),
+    ((8, 4096, 8192, 7168, BF16, False), "fused", 8), ((8, 4096, 8192, 7168, BF16, True), "fused", 8)])
+def test_tile_choice_fills_rounds(shape, variant, want):
+    """The automatic tile: 256x224 (B stored n x k) where 256x256 tiles would
+    leave a partial last round of workgroups (8192 x 3584: 448 tiles, 1.75
+    rounds, against 512 tiles, 2 rounds; a staged chunk of 4096 rows: 224
+    against 256 tiles, one round each), 256x256 otherwise."""
+    settings = {"pvalue": 2, "nbuf": 2} if variant == "staged" else {}
+    plan = agmm.Plan(*shape, variant=variant, **settings)
+    try:
+        assert plan.get("tile") == want
+    finally:
+        plan.close()
+
+
 def test_skinny_fullk_needs_transposed_b():
     plan = agmm.Plan(2, 16, 64, 64, BF16, False, variant="skinny")
     try:
@@ -419,14 +435,19 @@ def test_split_k_ragged(tile, splits):
     check_against_oracle(w, shards, B, C)
 
 
-@pytest.mark.parametrize("tile", [8, 9])
+@pytest.mark.parametrize("tile", [8, 9, 11])
 @pytest.mark.parametrize("dtype,rt", [(BF16, False), (BF16, True), (FP16, False), (FP16, True)])
 @pytest.mark.parametrize("splits,k", [(1, 1024), (3, 1024), (1, 1000)])
 def test_mfma16_tiles(tile, dtype, rt, splits, k):
     """The 16x16x32-MFMA tiles on whole interior tiles (m, n multiples of the
     tile, whole k-tiles in every k range: the unmasked loop with its pinned
-    interleave), with split-K, and with a ragged k (masked loop)."""
-    w, shards, B = make_case(2, 512, k, 512, dtype, rt, seed=1600 + tile + splits + k)
+    interleave), with split-K, and with a ragged k (masked loop).  Tile 11
+    (256x224, B stored n x k) has 7 column blocks per wave: halves of 4 and
+    3 blocks, and C rows of 28 16-byte chunks in the staged epilogue."""
+    if tile in agmm.TILES_NEED_BT and not rt:
+        pytest.skip("B stored n x k only")
+    n = 448 if tile == 11 else 512
+    w, shards, B = make_case(2, 512, k, n, dtype, rt, seed=1600 + tile + splits + k)
     C, _ = run_variant(w, [to_device(s, dtype) for s in shards], to_device(B, dtype), "fused",
                        tile=tile, splits=splits)
     check_against_oracle(w, shards, B, C)
