@@ -1366,6 +1366,13 @@ constexpr TileInfo kTiles[kTileCount] = {
     {256, 224, 64, 5, 4, 1},   // kTile256x224m16:   16x16x32 part ring, 7 column blocks per wave; B n x k only
 };
 
+constexpr bool all_tiles_described() {
+  for (const TileInfo& t : kTiles)
+    if (t.bm <= 0 || t.bn <= 0 || t.bk <= 0 || t.waves <= 0 || t.occ <= 0) return false;
+  return true;
+}
+static_assert(all_tiles_described(), "every tile configuration needs its row of kTiles");
+
 int tile_bm(int cfg) { return kTiles[cfg].bm; }
 int tile_bn(int cfg) { return kTiles[cfg].bn; }
 int tile_bk(int cfg) { return kTiles[cfg].bk; }
