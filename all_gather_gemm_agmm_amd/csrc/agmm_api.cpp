@@ -89,17 +89,17 @@ int validate(int N, int64_t m_s, int64_t k, int64_t n, int dtype, int rt) {
       k * n >= (int64_t(1) << 40) || m * n >= (int64_t(1) << 40))
     return set_err(AGMM_ERR_UNSUPPORTED, "problem too large (m=%lld, k=%lld, n=%lld)",
                    (long long)m, (long long)k, (long long)n);
-  if (dtype != AGMM_FP32) {
-    if (k % 8 != 0)
-      return set_err(AGMM_ERR_UNSUPPORTED,
-                     "bf16/fp16 need k %% 8 == 0 (16-byte rows); got k=%lld", (long long)k);
-    if (!rt && n % 8 != 0)
-      return set_err(AGMM_ERR_UNSUPPORTED,
-                     "bf16/fp16 with B stored k x n need n_local %% 8 == 0; got %lld",
-                     (long long)n);
-  }
   return ok();
 }
+
+// bf16/fp16 rows that are not whole 16-byte vectors (k, or n for B stored
+// k x n, not a multiple of 8) cannot be fed to the vector and direct-to-LDS
+// loads: such problems run on zero-padded copies of A and B.
+bool needs_pad(int dtype, int64_t k, int64_t n, int rt) {
+  return dtype != AGMM_FP32 && (k % 8 != 0 || (!rt && n % 8 != 0));
+}
+
+int64_t round8(int64_t x) { return (x + 7) / 8 * 8; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -129,6 +129,11 @@ struct Layout {
   int tile_used = agmm::kTile256x256;
   int bm = 256, bn = 256;
   int skinny_shape_used = 5;
+  // zero-padded operands (needs_pad): the GEMM runs on A [m][kp] in the ring
+  // and on B [n][kp] (rhs_transpose) or [kp][np] in its own buffer
+  bool padded = false;
+  int64_t kp = 0, np = 0;
+  size_t padb_bytes = 0;
   int64_t rows_per_chunk = 0;
   int num_chunks = 1;
   int nslots = 0;
@@ -141,7 +146,9 @@ struct Layout {
 
   static size_t up(size_t x) { return (x + 255) & ~size_t(255); }
   size_t order_bytes() const { return h_order.size() * sizeof(int32_t); }
-  size_t total_bytes() const { return up(ring_bytes) + up(part_bytes) + up(order_bytes()); }
+  size_t total_bytes() const {
+    return up(ring_bytes) + up(part_bytes) + up(padb_bytes) + up(order_bytes());
+  }
 };
 
 // Where the plan's previous call recorded its `done` event.
@@ -164,6 +171,7 @@ struct agmm_plan {
   size_t ws_cap = 0;
   char* ring = nullptr;
   float* partials = nullptr;
+  char* padb = nullptr;             // zero-padded B (padded layouts)
   int32_t* d_order = nullptr;
   // last automatic group_m choice, keyed by the launch's block counts
   int64_t group_key_rb = -1, group_key_cb = -1;
@@ -303,7 +311,13 @@ int derive_launch(const agmm_plan* p, const Settings& s, Layout& L) {
     else v = AGMM_VARIANT_FUSED;
   }
   if (is_f32(p) && v == AGMM_VARIANT_SKINNY) v = AGMM_VARIANT_FUSED;
-  if ((v == AGMM_VARIANT_STAGED || v == AGMM_VARIANT_UNFUSED) && (p->k * e) % 16 != 0)
+  L.padded = needs_pad(p->dtype, p->k, p->n, p->rt);
+  L.kp = L.padded ? round8(p->k) : p->k;
+  L.np = L.padded && !p->rt ? round8(p->n) : p->n;
+  // padded operands are gathered (with the zero fill) into the ring first:
+  // every requested variant runs as gather-then-GEMM
+  if (L.padded) v = AGMM_VARIANT_UNFUSED;
+  if ((v == AGMM_VARIANT_STAGED || v == AGMM_VARIANT_UNFUSED) && !L.padded && (p->k * e) % 16 != 0)
     return set_err(AGMM_ERR_UNSUPPORTED,
                    "the gather copy needs 16-byte rows (k * elem_bytes %% 16 == 0)");
   L.variant_used = v;
@@ -353,8 +367,8 @@ int derive_launch(const agmm_plan* p, const Settings& s, Layout& L) {
   L.num_chunks = 1;
   L.nslots = 0;
   L.splits_used = 1;
-  L.k_per_split = p->k;
-  L.ring_bytes = L.part_bytes = L.slot_bytes = 0;
+  L.k_per_split = L.kp;
+  L.ring_bytes = L.part_bytes = L.slot_bytes = L.padb_bytes = 0;
   if (v == AGMM_VARIANT_STAGED) {
     L.rows_per_chunk = std::min<int64_t>(p->m_s, (int64_t)s.pvalue * L.bm);
     L.num_chunks = (int)cdiv(p->m_s, L.rows_per_chunk);
@@ -363,8 +377,9 @@ int derive_launch(const agmm_plan* p, const Settings& s, Layout& L) {
     L.ring_bytes = L.slot_bytes * L.nslots;
   } else if (v == AGMM_VARIANT_UNFUSED) {
     L.nslots = 1;
-    L.slot_bytes = (size_t)p->m * p->k * e;
+    L.slot_bytes = (size_t)p->m * L.kp * e;
     L.ring_bytes = L.slot_bytes;
+    if (L.padded) L.padb_bytes = (size_t)(p->rt ? p->n * L.kp : L.kp * L.np) * e;
   }
   // split-K: skinny problems always, the other variants when one launch has
   // too few output tiles to give every CU a workgroup.  A power of two of k
@@ -391,12 +406,12 @@ int derive_launch(const agmm_plan* p, const Settings& s, Layout& L) {
         // long enough k ranges that the partial sums stay small next to the
         // operand traffic (skinny problems have no other way to fill the GPU)
         const int64_t min_k = v == AGMM_VARIANT_SKINNY ? agmm::kTileBK : 1024;
-        while (want * 2 * tiles <= slots && p->k / (want * 2) >= min_k) want *= 2;
+        while (want * 2 * tiles <= slots && L.kp / (want * 2) >= min_k) want *= 2;
       }
     }
-    want = std::max<int64_t>(1, std::min<int64_t>(want, cdiv(p->k, agmm::kTileBK)));
-    L.k_per_split = cdiv(cdiv(p->k, want), agmm::kTileBK) * agmm::kTileBK;
-    L.splits_used = (int)cdiv(p->k, L.k_per_split);
+    want = std::max<int64_t>(1, std::min<int64_t>(want, cdiv(L.kp, agmm::kTileBK)));
+    L.k_per_split = cdiv(cdiv(L.kp, want), agmm::kTileBK) * agmm::kTileBK;
+    L.splits_used = (int)cdiv(L.kp, L.k_per_split);
     // a staged plan's launches: its chunks and (local_first) the local shard's rows
     const int64_t part_m = v == AGMM_VARIANT_STAGED ? std::max<int64_t>(launch_m, p->m_s) : launch_m;
     if (L.splits_used > 1) L.part_bytes = (size_t)L.splits_used * part_m * p->n * sizeof(float);
@@ -472,6 +487,7 @@ int apply(agmm_plan* p, const Settings& s) {
     p->ws_cap = 0;
     p->ring = nullptr;
     p->partials = nullptr;
+    p->padb = nullptr;
     p->d_order = nullptr;
     rc = alloc_ws(p, total);
     if (rc != AGMM_OK) {
@@ -485,6 +501,7 @@ int apply(agmm_plan* p, const Settings& s) {
         char* q = p->ws;
         if (p->L.ring_bytes) { p->ring = q; q += Layout::up(p->L.ring_bytes); }
         if (p->L.part_bytes) { p->partials = reinterpret_cast<float*>(q); q += Layout::up(p->L.part_bytes); }
+        if (p->L.padb_bytes) { p->padb = q; q += Layout::up(p->L.padb_bytes); }
         if (p->L.order_bytes()) {
           p->d_order = reinterpret_cast<int32_t*>(q);
           if (hipMemcpy(p->d_order, p->L.h_order.data(), p->L.order_bytes(), hipMemcpyHostToDevice) != hipSuccess) {
@@ -502,10 +519,12 @@ int apply(agmm_plan* p, const Settings& s) {
   p->L = std::move(L);
   p->ring = nullptr;
   p->partials = nullptr;
+  p->padb = nullptr;
   p->d_order = nullptr;
   char* q = p->ws;
   if (p->L.ring_bytes) { p->ring = q; q += Layout::up(p->L.ring_bytes); }
   if (p->L.part_bytes) { p->partials = reinterpret_cast<float*>(q); q += Layout::up(p->L.part_bytes); }
+  if (p->L.padb_bytes) { p->padb = q; q += Layout::up(p->L.padb_bytes); }
   if (p->L.order_bytes()) {
     p->d_order = reinterpret_cast<int32_t*>(q);
     const hipError_t err = hipMemcpy(p->d_order, p->L.h_order.data(), p->L.order_bytes(), hipMemcpyHostToDevice);
@@ -707,6 +726,44 @@ int gather_chunk_sdma(agmm_plan* p, const void* const* shards, int64_t row0, int
   return AGMM_OK;
 }
 
+// Element-granular copy of rows with zero fill (launch_pad_copy), for rows
+// that are not whole 16-byte vectors.
+int pad_copy(const agmm_plan* p, const void* const* groups, int ngroups, int64_t src_rows,
+             int64_t src_ld, int64_t cols, int64_t rows, void* dst, int64_t dst_group_rows,
+             int64_t dst_ld, int64_t dst_cols, hipStream_t s) {
+  agmm::PadCopyProblem c{};
+  for (int g = 0; g < ngroups; ++g) c.src_group[g] = groups[g];
+  c.num_groups = ngroups;
+  c.elem_bytes = (int32_t)elem_bytes(p->dtype);
+  c.src_row0 = 0;
+  c.src_rows = src_rows;
+  c.src_ld = src_ld;
+  c.cols = cols;
+  c.rows = rows;
+  c.dst = dst;
+  c.dst_group_rows = dst_group_rows;
+  c.dst_ld = dst_ld;
+  c.dst_cols = dst_cols;
+  const hipError_t err = agmm::launch_pad_copy(c, s);
+  if (err != hipSuccess) return hip_err(err, "pad copy launch");
+  return AGMM_OK;
+}
+
+// The gathered operand [m][k] (dense rows) from the shards: the vector
+// gather copy when rows are whole 16-byte vectors, else element by element.
+int gather_rows(agmm_plan* p, const void* const* shards, void* dst, int max_wgs, hipStream_t s) {
+  const int64_t e = elem_bytes(p->dtype);
+  if ((p->k * e) % 16 == 0 && (lda_of(p) * e) % 16 == 0)
+    return gather_chunk(p, shards, 0, p->m_s, dst, p->m_s, max_wgs, s);
+  return pad_copy(p, shards, p->N, p->m_s, lda_of(p), p->k, p->m_s, dst, p->m_s, p->k, p->k, s);
+}
+
+// A padded layout's run: A (from the shards, or from a gathered [m][k]
+// buffer) into the ring as [m][kp] and B into its buffer, both zero-filled,
+// then the GEMM over kp (the zeros add nothing to any sum).
+int run_padded(agmm_plan* p, const Call& c, const void* const* shards, const void* gathered,
+               const void* B, void* C);
+
 // Whether a copy goes to the SDMA engines: only when the plan asks for them
 // (copy_engine 1), the copy runs beside a GEMM (`overlaps`), the shard rows
 // are dense and the caller's stream is not being captured into a graph (the
@@ -716,7 +773,8 @@ int gather_chunk_sdma(agmm_plan* p, const void* const* shards, int64_t row0, int
 // (workload 5: 5.26 ms against 3.47 ms with the kernel copy), so the kernel
 // copy stays the default.
 bool copy_on_sdma(const agmm_plan* p, const Call& c, bool overlaps) {
-  return p->s.copy_engine == 1 && overlaps && lda_of(p) == p->k && !c.capturing;
+  return p->s.copy_engine == 1 && overlaps && lda_of(p) == p->k && !c.capturing &&
+         (p->k * (int64_t)elem_bytes(p->dtype)) % 16 == 0;
 }
 
 // Fork: `other` waits for everything enqueued so far on the caller's stream.
@@ -862,9 +920,27 @@ int run_staged(agmm_plan* p, const Call& c, const void* const* shards, const voi
   return rj != AGMM_OK ? rj : rj2;
 }
 
+int run_padded(agmm_plan* p, const Call& c, const void* const* shards, const void* gathered,
+               const void* B, void* C) {
+  const Layout& L = p->L;
+  int rc = gathered
+               ? pad_copy(p, &gathered, 1, p->m, p->k, p->k, p->m, p->ring, p->m, L.kp, L.kp, c.s)
+               : pad_copy(p, shards, p->N, p->m_s, lda_of(p), p->k, p->m_s, p->ring, p->m_s, L.kp, L.kp, c.s);
+  if (rc != AGMM_OK) return rc;
+  rc = p->rt ? pad_copy(p, &B, 1, p->n, ldb_of(p), p->k, p->n, p->padb, p->n, L.kp, L.kp, c.s)
+             : pad_copy(p, &B, 1, p->k, ldb_of(p), p->n, L.kp, p->padb, L.kp, L.np, L.np, c.s);
+  if (rc != AGMM_OK) return rc;
+  agmm::GemmProblem g = base_problem(p, dense_rows(p->ring, p->m, L.kp), p->m, p->padb, C, -1);
+  g.k = (int32_t)L.kp;
+  g.ldb = p->rt ? L.kp : L.np;
+  with_splits(p, g);
+  return launch_gemm(p, c, g, c.s);
+}
+
 // agmm_run's work, after enter().
 int run_plan(agmm_plan* p, const Call& c, const void* const* shard_ptrs, const void* B, void* C) {
   int rc;
+  if (p->L.padded) return run_padded(p, c, shard_ptrs, nullptr, B, C);
   switch (p->L.variant_used) {
     case AGMM_VARIANT_FUSED:
     case AGMM_VARIANT_SKINNY: {
@@ -1010,9 +1086,11 @@ int agmm_plan_set_int(agmm_plan_t p, const char* key, int64_t v) {
   } else if (k == "lda" || k == "ldb" || k == "ldc") {
     // 0 restores the dense default; otherwise at least the row length, and
     // A / B rows 16-byte aligned for the vector and direct-to-LDS loads
+    // (not needed where the rows go through the element-granular padded copy)
     const int64_t e = elem_bytes(p->dtype);
     const int64_t row = k == "lda" ? p->k : k == "ldc" ? p->n : (p->rt ? p->k : p->n);
-    if (v != 0 && (v < row || v >= kDimLimit || (k != "ldc" && (v * e) % 16 != 0))) return bad();
+    const bool any_ld = k == "ldc" || needs_pad(p->dtype, p->k, p->n, p->rt);
+    if (v != 0 && (v < row || v >= kDimLimit || (!any_ld && (v * e) % 16 != 0))) return bad();
     (k == "lda" ? s.lda : k == "ldb" ? s.ldb : s.ldc) = v;
   } else if (k == "copy_wgs") {
     if (v < 0 || v > 1 << 20) return bad();
@@ -1225,12 +1303,9 @@ int agmm_gather(agmm_plan_t p, const void* const* shard_ptrs, void* gathered, vo
     if (!aligned16(shard_ptrs[r]))
       return set_err(AGMM_ERR_UNSUPPORTED, "shard_ptrs[%d] is not 16-byte aligned", r);
   }
-  if ((p->k * (int64_t)elem_bytes(p->dtype)) % 16 != 0)
-    return set_err(AGMM_ERR_UNSUPPORTED, "the gather copy needs 16-byte rows");
   std::lock_guard<std::mutex> lk(p->mu);
   // no workspace is used: nothing to order against the plan's other calls
-  const int rc = gather_chunk(p, shard_ptrs, 0, p->m_s, gathered, p->m_s, 0,
-                              static_cast<hipStream_t>(stream));
+  const int rc = gather_rows(p, shard_ptrs, gathered, 0, static_cast<hipStream_t>(stream));
   return rc == AGMM_OK ? ok() : rc;
 }
 
@@ -1241,6 +1316,7 @@ int agmm_run_gathered(agmm_plan_t p, const void* gathered, const void* B, void* 
     return set_err(AGMM_ERR_UNSUPPORTED, "pointers must be 16-byte aligned");
   std::lock_guard<std::mutex> lk(p->mu);
   return guarded(p, static_cast<hipStream_t>(stream), [&](const Call& c) {
+    if (p->L.padded) return run_padded(p, c, nullptr, gathered, B, C);
     agmm::GemmProblem g = base_problem(p, dense_rows(gathered, p->m, p->k), p->m, B, C, -1);
     with_splits(p, g);
     return launch_gemm(p, c, g, c.s);
@@ -1253,11 +1329,15 @@ int agmm_run_gather_out(agmm_plan_t p, const void* const* shard_ptrs, const void
   if (rc != AGMM_OK) return rc;
   if (!gathered) return set_err(AGMM_ERR_INVALID_ARG, "gathered is NULL");
   if (!aligned16(gathered)) return set_err(AGMM_ERR_UNSUPPORTED, "gathered is not 16-byte aligned");
-  if ((p->k * (int64_t)elem_bytes(p->dtype)) % 16 != 0)
-    return set_err(AGMM_ERR_UNSUPPORTED, "the gather copy needs 16-byte rows (k * elem_bytes %% 16 == 0)");
   std::lock_guard<std::mutex> lk(p->mu);
   return guarded(p, static_cast<hipStream_t>(stream), [&](const Call& c) -> int {
     const int copy_wgs = p->s.copy_wgs > 0 ? p->s.copy_wgs : p->cu_count;
+    if (p->L.padded) {
+      // the gathered output keeps rows of k elements; the GEMM runs on the
+      // padded copies
+      const int r = gather_rows(p, shard_ptrs, gathered, 0, c.s);
+      return r != AGMM_OK ? r : run_padded(p, c, shard_ptrs, nullptr, B, C);
+    }
     switch (p->L.variant_used) {
       case AGMM_VARIANT_STAGED:
         return run_staged(p, c, shard_ptrs, B, C, gathered);
@@ -1277,7 +1357,7 @@ int agmm_run_gather_out(agmm_plan_t p, const void* const* shard_ptrs, const void
         if (r != AGMM_OK) return r;
         r = copy_on_sdma(p, c, true)
                 ? gather_chunk_sdma(p, shard_ptrs, 0, p->m_s, gathered, p->m_s, p->copy_stream)
-                : gather_chunk(p, shard_ptrs, 0, p->m_s, gathered, p->m_s, copy_wgs, p->copy_stream);
+                : gather_rows(p, shard_ptrs, gathered, copy_wgs, p->copy_stream);
         if (r == AGMM_OK) {
           agmm::GemmProblem g = base_problem(p, shard_rows(p, shard_ptrs), p->m, B, C, 0);
           with_splits(p, g);
@@ -1375,6 +1455,10 @@ int agmm_run_noalloc(int num_shards, int64_t m_per_shard, int64_t k, int64_t n_l
     p.cu_count = cus;
   rc = derive_launch(&p, p.s, p.L);
   if (rc != AGMM_OK) return rc;
+  if (p.L.padded)
+    return set_err(AGMM_ERR_UNSUPPORTED,
+                   "rows that are not whole 16-byte vectors run on padded copies, which need a "
+                   "plan's workspace (use a plan)");
   if (p.L.variant_used != AGMM_VARIANT_FUSED && p.L.variant_used != AGMM_VARIANT_SKINNY)
     return set_err(AGMM_ERR_UNSUPPORTED, "agmm_run_noalloc runs the fused and skinny paths only");
   if (p.L.part_bytes > AGMM_NOALLOC_SCRATCH_BYTES)

@@ -117,6 +117,28 @@ struct GatherProblem {
 };
 hipError_t launch_gather(const GatherProblem& p, int max_workgroups, hipStream_t stream);
 
+// Element-granular copy of rows for rows that are not whole 16-byte vectors
+// (any row length and strides), with zero fill:
+//   dst[(g * dst_group_rows + t) * dst_ld + c] =
+//       (t < src_rows && c < cols) ? src_group[g][(src_row0 + t) * src_ld + c] : 0
+// for g < num_groups, t < rows, c < dst_cols.  Strides and lengths in
+// elements of elem_bytes (2 or 4) bytes; pointers aligned to an element.
+struct PadCopyProblem {
+  const void* src_group[kMaxGroups];
+  int32_t num_groups;
+  int32_t elem_bytes;
+  int64_t src_row0;
+  int64_t src_rows;        // rows of each group that exist in the source (the rest are zeros)
+  int64_t src_ld;
+  int64_t cols;            // elements of a source row that are copied
+  int64_t rows;            // rows written per group
+  void* dst;
+  int64_t dst_group_rows;
+  int64_t dst_ld;
+  int64_t dst_cols;        // elements written per row (zeros past cols)
+};
+hipError_t launch_pad_copy(const PadCopyProblem& p, hipStream_t stream);
+
 // Size of the device scratch of the no-allocation entry point (one per GPU,
 // held for the life of the process; equal to AGMM_NOALLOC_SCRATCH_BYTES).
 constexpr size_t kNoallocScratchBytes = size_t(32) << 20;

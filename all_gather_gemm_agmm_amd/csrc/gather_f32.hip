@@ -15,6 +15,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+#include <type_traits>
+
 #include "agmm_kernels.h"
 
 namespace agmm {
@@ -64,6 +67,44 @@ __global__ __launch_bounds__(kCopyThreads) void gather_kernel(GatherProblem p) {
         if constexpr (NT) __builtin_nontemporal_store(v[q], d);
         else *d = v[q];
       }
+  }
+}
+
+// Element-granular row copy with zero fill (rows that are not whole 16-byte
+// vectors: a k or n that is not a multiple of 8 16-bit elements).  Each
+// thread assembles one 16-byte chunk of a destination row from element
+// loads (consecutive threads take consecutive chunks, so a wave reads and
+// writes contiguous runs) and stores it whole when the destination row is
+// 16-byte aligned, element by element otherwise.
+template <int E>
+__global__ __launch_bounds__(256) void pad_copy_kernel(PadCopyProblem p) {
+  typedef typename std::conditional<E == 2, uint16_t, uint32_t>::type elem_t;
+  constexpr int V = 16 / E;                  // elements per 16-byte chunk
+  const int64_t chunks = (p.dst_cols + V - 1) / V;
+  const int64_t per_group = chunks * p.rows;
+  const int64_t total = per_group * p.num_groups;
+  const bool vec_rows = ((p.dst_ld * E) % 16) == 0 && (reinterpret_cast<uintptr_t>(p.dst) & 15) == 0;
+  for (int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; u < total;
+       u += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t g = u / per_group;
+    const int64_t rem = u - g * per_group;
+    const int64_t t = rem / chunks;
+    const int64_t c0 = (rem - t * chunks) * V;
+    const elem_t* src = static_cast<const elem_t*>(p.src_group[g]) + (p.src_row0 + t) * p.src_ld;
+    const bool row_ok = t < p.src_rows;
+    elem_t v[V];
+#pragma unroll
+    for (int j = 0; j < V; ++j) v[j] = (row_ok && c0 + j < p.cols) ? src[c0 + j] : elem_t(0);
+    elem_t* dst = static_cast<elem_t*>(p.dst) + (g * p.dst_group_rows + t) * p.dst_ld + c0;
+    if (vec_rows && c0 + V <= p.dst_cols) {
+      u32x4_t w;
+      __builtin_memcpy(&w, v, 16);
+      *reinterpret_cast<u32x4_t*>(dst) = w;
+    } else {
+#pragma unroll
+      for (int j = 0; j < V; ++j)
+        if (c0 + j < p.dst_cols) dst[j] = v[j];
+    }
   }
 }
 
@@ -168,6 +209,21 @@ hipError_t launch_gather(const GatherProblem& p, int max_workgroups, hipStream_t
     hipLaunchKernelGGL(gather_kernel<true>, dim3((unsigned)wgs), dim3(kCopyThreads), 0, stream, p);
   else
     hipLaunchKernelGGL(gather_kernel<false>, dim3((unsigned)wgs), dim3(kCopyThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_pad_copy(const PadCopyProblem& p, hipStream_t stream) {
+  if ((p.elem_bytes != 2 && p.elem_bytes != 4) || p.num_groups < 1 || p.num_groups > kMaxGroups ||
+      p.rows < 0 || p.dst_cols < p.cols || p.dst_ld < p.dst_cols || p.cols < 0)
+    return hipErrorInvalidValue;
+  const int64_t chunks = (p.dst_cols + 16 / p.elem_bytes - 1) / (16 / p.elem_bytes);
+  const int64_t total = chunks * p.rows * p.num_groups;
+  if (total == 0) return hipSuccess;
+  const int64_t wgs = std::min<int64_t>((total + 255) / 256, 8192);
+  if (p.elem_bytes == 2)
+    hipLaunchKernelGGL(pad_copy_kernel<2>, dim3((unsigned)wgs), dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL(pad_copy_kernel<4>, dim3((unsigned)wgs), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -96,11 +96,15 @@ typedef enum {
  *   m_per_shard, k, n_local >= 1, with m*k, k*n_local, m*n_local < 2^31
  *   dtype         agmm_dtype
  *   rhs_transpose 0: B is [k, n_local]; 1: B is [n_local, k]
- * bf16/fp16 additionally need k % 8 == 0 (16-byte rows for vector loads) and,
- * without rhs_transpose, n_local % 8 == 0; fp32 needs k % 4 == 0 for the
- * gather copy used by the staged/unfused variants.  (The tpu-inference
- * page's own `validate_inputs` rules — 2-D inputs, equal dtypes, matching k —
- * are implied by this signature; its TPU tiling rules are not imposed.)
+ * Any k and n_local are accepted.  bf16/fp16 rows that are not whole
+ * 16-byte vectors (k % 8 != 0, or n_local % 8 != 0 with B stored k x n) are
+ * computed on zero-padded copies of A ([m][k rounded up to 8]) and B that the
+ * plan keeps in its workspace, the way the Ascend tutorial's kernel masks its
+ * K and N tails: every requested variant then runs as gather-then-GEMM.  The
+ * staged and unfused variants of fp32 plans need k % 4 == 0 (16-byte rows
+ * for the gather copy).  (The tpu-inference page's own `validate_inputs`
+ * rules - 2-D inputs, equal dtypes, matching k - are implied by this
+ * signature; its TPU tiling rules are not imposed.)
  */
 int agmm_plan_validate(int num_shards, int64_t m_per_shard, int64_t k, int64_t n_local,
                        int dtype, int rhs_transpose);
@@ -150,7 +154,8 @@ int agmm_run(agmm_plan_t plan, const void *const *shard_ptrs, const void *B, voi
 /*
  * Enqueue only the all-gather: gathered[r*m_per_shard + i, :] = shard r row i,
  * a bit-exact copy.  gathered is a device buffer [m, k] of the plan's dtype,
- * 16-byte aligned.  (The gathered operand the tpu-inference kernel returns as
+ * 16-byte aligned (rows of any length: a vector copy for whole 16-byte rows,
+ * an element copy otherwise).  (The gathered operand the tpu-inference kernel returns as
  * its second output, `x_hbm_scratch`.)  Same stream rules as agmm_run.
  */
 int agmm_gather(agmm_plan_t plan, const void *const *shard_ptrs, void *gathered, void *stream);
@@ -178,9 +183,9 @@ int agmm_run_gathered(agmm_plan_t plan, const void *gathered, const void *B, voi
  *   fused, skinny and fp32 plans: the GEMM reads the shards on `stream`
  *                  while the plan's second stream writes `gathered`.
  * `gathered` is a caller-owned device buffer of the plan's dtype, 16-byte
- * aligned, not aliasing the shards, B or C; requires k * elem_bytes % 16 == 0
- * (else AGMM_ERR_UNSUPPORTED).  Same stream rules and return codes as
- * agmm_run; work enqueued later on `stream` sees both outputs complete.
+ * aligned, not aliasing the shards, B or C.  Same stream rules and return
+ * codes as agmm_run; work enqueued later on `stream` sees both outputs
+ * complete.
  */
 int agmm_run_gather_out(agmm_plan_t plan, const void *const *shard_ptrs, const void *B, void *C,
                         void *gathered, void *stream);
@@ -254,7 +259,9 @@ int agmm_plan_autotune(agmm_plan_t plan, const void *const *shard_ptrs, const vo
  *                   kernel copies then).  Both are bit copies.
  *   "lda", "ldb", "ldc"  0 (dense, the default) or the element stride between
  *                   rows of the shards, of B as stored and of C: at least the
- *                   row length; lda and ldb also a multiple of 16 bytes.  The
+ *                   row length; lda and ldb also a multiple of 16 bytes
+ *                   (any value for plans on padded copies, see
+ *                   agmm_plan_validate).  The
  *                   gathered buffers of agmm_gather / agmm_run_gathered /
  *                   agmm_run_gather_out stay dense [m, k].  get returns the
  *                   stride in use.

@@ -48,8 +48,6 @@ def test_validate_accepts_the_workloads():
     ((2, 4, 8, -1, 0, 0), agmm.AGMM_ERR_INVALID_ARG, "sizes"),
     ((2, 4, 8, 8, 7, 0), agmm.AGMM_ERR_INVALID_ARG, "dtype"),
     ((2, 4, 8, 8, 0, 2), agmm.AGMM_ERR_INVALID_ARG, "rhs_transpose"),
-    ((2, 4, 12, 8, 0, 1), agmm.AGMM_ERR_UNSUPPORTED, "k % 8"),
-    ((2, 4, 16, 12, 1, 0), agmm.AGMM_ERR_UNSUPPORTED, "n_local % 8"),
     ((2, 1 << 29, 8, 8, 0, 0), agmm.AGMM_ERR_UNSUPPORTED, "too large"),
 ])
 def test_validate_rejects(args, status, fragment):
@@ -58,10 +56,14 @@ def test_validate_rejects(args, status, fragment):
     assert fragment in agmm.agmm_last_error()
 
 
-def test_validate_accepts_ragged_and_fp32_odd_shapes():
+def test_validate_accepts_ragged_and_odd_shapes():
     assert agmm.agmm_plan_validate(3, 100, 200, 136, 0, 0) == agmm.AGMM_OK
     assert agmm.agmm_plan_validate(3, 100, 200, 130, 1, 1) == agmm.AGMM_OK  # n free with B^T
     assert agmm.agmm_plan_validate(2, 5, 7, 3, 2, 0) == agmm.AGMM_OK        # fp32: any shape
+    # 16-bit rows that are not whole 16-byte vectors run on zero-padded copies
+    assert agmm.agmm_plan_validate(2, 4, 12, 8, 0, 1) == agmm.AGMM_OK
+    assert agmm.agmm_plan_validate(2, 4, 16, 12, 1, 0) == agmm.AGMM_OK
+    assert agmm.agmm_plan_validate(3, 7, 13, 5, 1, 0) == agmm.AGMM_OK
     assert agmm.agmm_last_status() == agmm.AGMM_OK and agmm.agmm_last_error() == ""
 
 

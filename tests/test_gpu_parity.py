@@ -536,6 +536,80 @@ def test_strided_inputs(variant, dtype, rt, lds):
     check_against_oracle(w, shards, B, C)
 
 
+PADDED = [
+    # N, m_s, k, n, dtype, rhs_transpose: rows that are not whole 16-byte vectors
+    (3, 50, 100, 130, BF16, False),    # k % 8 == 4, n % 8 == 2 with B stored k x n
+    (2, 33, 257, 65, FP16, True),      # odd k
+    (4, 64, 1000, 300, BF16, False),   # n % 8 == 4 only (k whole)
+    (1, 7, 13, 5, FP16, False),        # everything tiny and odd
+    (2, 40, 2051, 96, BF16, True),     # a long ragged k (split-K over the padded k)
+]
+
+
+@pytest.mark.parametrize("variant", ["auto", "fused", "staged", "skinny"])
+@pytest.mark.parametrize("case", PADDED, ids=lambda c: "x".join(map(str, c[:4])) + f"_{I.DTYPE_NAMES[c[4]]}_rt{int(c[5])}")
+def test_padded_shapes(case, variant):
+    """bf16/fp16 problems whose rows are not whole 16-byte vectors run on
+    zero-padded copies of A and B (every requested variant resolves to that
+    gather-then-GEMM form): the oracle's values; C's padding untouched."""
+    N, m_s, k, n, dtype, rt = case
+    w, shards, B = make_case(N, m_s, k, n, dtype, rt, seed=2800 + N + m_s + k + n)
+    sd = [to_device(x, dtype) for x in shards]
+    bd = to_device(B, dtype)
+    plan = agmm.Plan(N, m_s, k, n, dtype, rt, variant=variant)
+    try:
+        assert plan.get("variant_used") == agmm.VARIANTS["unfused"]
+        c_full = torch.full((w.m, n + 3), float("nan"), dtype=torch_dtype(dtype), device="cuda")
+        plan.set("ldc", n + 3)
+        C = plan.run(sd, bd, c_full[:, :n])
+        C2, G = plan.run_gather_out(sd, bd)
+        C3 = plan.run_gathered(G, bd)
+        torch.cuda.synchronize()
+    finally:
+        plan.close()
+    assert bool(torch.isnan(c_full[:, n:].float()).all())
+    assert np.array_equal(to_bits(G), np.concatenate(shards, axis=0))
+    assert np.array_equal(to_bits(C), to_bits(C2)) and np.array_equal(to_bits(C), to_bits(C3))
+    check_against_oracle(w, shards, B, C)
+
+
+def test_padded_strided_and_split():
+    """A padded problem with row strides that are not 16-byte multiples
+    (allowed where rows go through the element copy) and explicit split-K."""
+    N, m_s, k, n, dtype, rt = 3, 70, 1003, 77, FP16, True
+    lda, ldb = 1005, 1010
+    w, shards, B = make_case(N, m_s, k, n, dtype, rt, seed=2900)
+    plan = agmm.Plan(N, m_s, k, n, dtype, rt, splits=2)
+    try:
+        plan.set("lda", lda)
+        plan.set("ldb", ldb)
+        assert plan.get("splits") == 2
+        sd = [strided(to_device(x, dtype), lda) for x in shards]
+        bd = strided(to_device(B, dtype), ldb)
+        C = plan.run(sd, bd)
+        G = plan.gather(sd)
+        torch.cuda.synchronize()
+    finally:
+        plan.close()
+    assert np.array_equal(to_bits(G), np.concatenate(shards, axis=0))
+    check_against_oracle(w, shards, B, C)
+
+
+@pytest.mark.parametrize("dtype,k", [(BF16, 13), (FP16, 302), (FP32, 37)])
+def test_gather_any_row_length(dtype, k):
+    """agmm_gather with rows that are not whole 16-byte vectors (the element
+    copy): bit-exact."""
+    w, shards, _ = make_case(4, 29, k, 8, dtype, True, seed=3000 + k)
+    sd = [to_device(x, dtype) for x in shards]
+    plan = agmm.Plan(4, 29, k, 8, dtype, True)
+    try:
+        G = plan.gather(sd)
+        torch.cuda.synchronize()
+    finally:
+        plan.close()
+    assert np.array_equal(to_bits(G), oracle.gather(shards, dtype))
+
+
 def test_stride_keys_validated():
     plan = agmm.Plan(2, 16, 64, 40, BF16, True)
     try:

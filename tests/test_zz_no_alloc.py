@@ -80,3 +80,15 @@ def test_noalloc_refuses_problems_beyond_its_scratch():
     assert "scratch" in str(ei.value)
     torch.cuda.synchronize()
     assert torch.isnan(C.float()).all().item()
+
+
+def test_noalloc_refuses_padded_shapes():
+    """Rows that are not whole 16-byte vectors need a plan's padded copies."""
+    sd = [torch.zeros((8, 13), dtype=torch.bfloat16, device="cuda") for _ in range(2)]
+    bd = torch.zeros((24, 13), dtype=torch.bfloat16, device="cuda")
+    C = torch.full((16, 24), float("nan"), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(agmm.AgmmError) as ei:
+        agmm.run_noalloc(sd, bd, C, True)
+    assert ei.value.status == agmm.AGMM_ERR_UNSUPPORTED
+    torch.cuda.synchronize()
+    assert torch.isnan(C.float()).all().item()
