@@ -117,6 +117,7 @@ struct Settings {
   int copy_wgs = 0;
   int skinny_shape = -1;  // tile shape of the whole-k skinny kernel; -1 automatic
   int copy_engine = 0;    // copies beside a GEMM: 0 gather kernel (CUs), 1 SDMA engines
+  int gather_out = 0;     // agmm_run_gather_out on fused/skinny plans: 0 automatic, 1 side copy, 2 sequential
   int64_t lda = 0, ldb = 0, ldc = 0;   // element strides between rows (0: dense)
   int gemm_streams = 2;   // staged: chunk GEMMs alternate over this many streams (1 or 2)
   int local_first = 0;    // staged: the local shard's rows first, straight from its buffer
@@ -1101,6 +1102,9 @@ int agmm_plan_set_int(agmm_plan_t p, const char* key, int64_t v) {
   } else if (k == "copy_engine") {
     if (v < 0 || v > 1) return bad();
     s.copy_engine = (int)v;
+  } else if (k == "gather_out") {
+    if (v < 0 || v > 2) return bad();
+    s.gather_out = (int)v;
   } else if (k == "debug_keep_slots") {
     if (v != 0 && v != 1) return bad();
     s.debug_keep_slots = (int)v;
@@ -1131,6 +1135,7 @@ int agmm_plan_get_int(agmm_plan_t p, const char* key, int64_t* value) {
   else if (k == "xcd_remap") v = s.xcd_remap;
   else if (k == "copy_wgs") v = s.copy_wgs;
   else if (k == "copy_engine") v = s.copy_engine;
+  else if (k == "gather_out") v = s.gather_out;
   else if (k == "skinny_shape") v = L.skinny_shape_used;
   else if (k == "lda") v = lda_of(p);
   else if (k == "ldb") v = ldb_of(p);
@@ -1350,9 +1355,25 @@ int agmm_run_gather_out(agmm_plan_t p, const void* const* shard_ptrs, const void
         return launch_gemm(p, c, g, c.s);
       }
       default: {
-        // fused / skinny / fp32: the GEMM reads the shards on the caller's
-        // stream while the copy stream writes the gathered operand; the
-        // caller's stream then waits for the copy
+        // fused / skinny / fp32.  Sequential (the automatic choice): gather
+        // into `gathered` on the caller's stream, then the GEMM reads it (same
+        // tile and k order: the same C as from the shards).  Measured (ms per
+        // call, sequential against the copy beside the GEMM on the CUs / on
+        // the SDMA engines): 8x4096x8192 -> 7168 bf16 2.995 / 3.357 / 3.104
+        // (the chip is power-limited under MFMA load, so a concurrent copy
+        // slows the GEMM by more than the copy costs alone); 8x16x4096 ->
+        // 1792 bf16 (eager) 0.032 / 0.101 / 0.119.
+        const bool sequential = p->s.gather_out != 1;
+        if (sequential) {
+          int r = gather_rows(p, shard_ptrs, gathered, 0, c.s);
+          if (r != AGMM_OK) return r;
+          agmm::GemmProblem g = base_problem(p, dense_rows(gathered, p->m, p->k), p->m, B, C, 0);
+          with_splits(p, g);
+          return launch_gemm(p, c, g, c.s);
+        }
+        // side copy: the GEMM reads the shards on the caller's stream while
+        // the copy stream writes the gathered operand; the caller's stream
+        // then waits for the copy
         int r = fork_to(p, c, p->copy_stream);
         if (r != AGMM_OK) return r;
         r = copy_on_sdma(p, c, true)

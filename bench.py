@@ -397,6 +397,13 @@ class Bench:
             if not eager and ms < GRAPH_MAX_STEP_MS:
                 res["ms"], res["per_step"] = self.graph_steps(run, steps)
                 res["timing"] = "HIP-graph replay of the K steps"
+                if with_kernel and used in ("fused", "skinny"):
+                    # a graph-timed fused or skinny step holds nothing but the
+                    # dominant kernel (and its split-K reduction): its replay
+                    # time per step is that kernel's duration, free of the
+                    # per-launch event overhead of the eager hooks
+                    res["kernel_ms_events"] = res["kernel_ms"]
+                    res["kernel_ms"] = res["ms"] / res["launches_per_step"]
         finally:
             plan.close()
         return res
@@ -614,9 +621,11 @@ def main():
         # side copy on the gather kernel or on the SDMA engines
         if gather:
             G = torch.empty((w.m, w.k), dtype=b.tdt, device=b.dev)
-            for ce in (0, 1):
-                log(f"gather_out copy_engine={ce}")
-                op = b.plan(variant, copy_engine=ce)
+            for label, extra in (("side_kernel", {"gather_out": 1, "copy_engine": 0}),
+                                 ("side_sdma", {"gather_out": 1, "copy_engine": 1}),
+                                 ("sequential", {"gather_out": 2}), ("auto", {})):
+                log(f"gather_out {label}")
+                op = b.plan(variant, **extra)
                 try:
                     def orun(i, s, op=op):
                         sh, Bt, C = b.sets[i % b.nsets]
@@ -625,7 +634,7 @@ def main():
                     ms, _ = b.eager_steps(orun, max(5, args.steps // 2))
                 finally:
                     op.close()
-                gather["gather_out_ms_" + ("sdma" if ce else "kernel")] = round(ms, 5)
+                gather["gather_out_ms_" + label] = round(ms, 5)
             del G
         # the same problem through the other paths (overlap accounting)
         variants_ms = {}

@@ -180,8 +180,13 @@ int agmm_run_gathered(agmm_plan_t plan, const void *gathered, const void *B, voi
  *   staged plans:  each chunk is copied straight to its place in `gathered`
  *                  and that chunk's GEMM reads it from there (no ring slot);
  *   unfused plans: gather into `gathered`, then the GEMM reads it;
- *   fused, skinny and fp32 plans: the GEMM reads the shards on `stream`
- *                  while the plan's second stream writes `gathered`.
+ *   fused, skinny and fp32 plans: key "gather_out" 1: the GEMM reads the
+ *                  shards on `stream` while the plan's second stream writes
+ *                  `gathered`; 2: `gathered` is written first and the GEMM
+ *                  reads it (same tile and k order, so the same C);
+ *                  0 (default): 2, measured faster (the chip is power-limited
+ *                  under MFMA load, so a copy beside the GEMM slows it by more
+ *                  than the copy costs).
  * `gathered` is a caller-owned device buffer of the plan's dtype, 16-byte
  * aligned, not aliasing the shards, B or C.  Same stream rules and return
  * codes as agmm_run; work enqueued later on `stream` sees both outputs
@@ -275,6 +280,8 @@ int agmm_plan_autotune(agmm_plan_t plan, const void *const *shard_ptrs, const vo
  *                   copy: tpu-inference `all_gather_matmul`, a device's own
  *                   x block); the chunk GEMMs then cover the other shards'
  *                   rows.  The ring slots still hold every shard's rows.
+ *   "gather_out"    0, 1 or 2: how agmm_run_gather_out produces the gathered
+ *                   operand on fused, skinny and fp32 plans (see there)
  *   "debug_keep_slots" 0/1: staged variant uses one slot per chunk (nothing
  *                   is overwritten; for inspection by agmm_plan_slot_ptr)
  * A change waits for the plan's previous call to finish, then keeps the

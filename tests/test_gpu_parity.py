@@ -773,7 +773,9 @@ def test_run_gathered_matches_fused():
 @pytest.mark.parametrize("variant,dtype,rt,settings", [
     ("fused", BF16, False, {"tile": 6}), ("staged", FP16, True, {"pvalue": 1, "tile": 6}),
     ("unfused", BF16, True, {}), ("skinny", BF16, True, {}), ("fused", FP32, False, {}),
-    ("fused", BF16, True, {"copy_engine": 1}), ("staged", BF16, False, {"pvalue": 1, "copy_engine": 1}),
+    ("fused", BF16, True, {"copy_engine": 1, "gather_out": 1}), ("fused", BF16, False, {"gather_out": 1}),
+    ("fused", FP16, True, {"gather_out": 2}), ("skinny", BF16, True, {"gather_out": 2}),
+    ("staged", BF16, False, {"pvalue": 1, "copy_engine": 1}),
     ("unfused", BF16, False, {"copy_engine": 1})])
 def test_run_gather_out(variant, dtype, rt, settings):
     """C and the gathered operand from one call: the gathered buffer is the
