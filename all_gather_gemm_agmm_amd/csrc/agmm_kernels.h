@@ -90,9 +90,9 @@ constexpr int kTileBK = 64;
 hipError_t launch_gemm_mfma(const GemmProblem& p, int tile_cfg, int dtype, bool rhs_transpose,
                             hipStream_t stream);
 
-// Skinny-m kernel (tile kTileSkinny, B stored n x k): 64 x 16 output tiles,
-// each over the whole of k in one workgroup (no split, one launch; p.splits
-// is ignored).  C rows through the row map.
+// Skinny-m kernel (tile kTileSkinny, B stored n x k): small output tiles
+// (32 x 32 by default), each over the whole of k in one workgroup (no split,
+// one launch; p.splits is ignored).  C rows through the row map.
 // `shape` selects the tile: 0: 64 x 16, 1: 32 x 32, 2: 32 x 16, 3: 16 x 32,
 // 4: 64 x 32 (rows x columns) with 4 waves; 5: 32 x 32 and 6: 64 x 16 with
 // 8 waves (the LDS shared out over twice as many, half as deep, rings).

@@ -12,29 +12,35 @@
 // store).
 //
 // Design (MI355X-native, not a translation of either page):
-//  * 4 or 8 waves of 64 lanes per workgroup, 2 x (waves/2) over the tile.
-//  * v_mfma_f32_32x32x16_{bf16,f16}: the B tile is the MFMA's first operand
-//    and the A tile its second, so each lane ends up owning 4 consecutive
-//    output columns of one row (8-byte packed stores in the epilogue).
+//  * 4 waves of 64 lanes per workgroup, 2 x 2 over the output tile.
+//  * Two main-loop forms:
+//      - the part ring (gemm_m16_kernel, and gemm_mfma_kernel with
+//        kLoopParts): 64-deep k-tiles, LDS split into 5 slots that each hold
+//        one operand of one k-tile, so 2.5 k-tiles are resident and every
+//        load fetches whole 128-byte lines; one barrier per k-tile;
+//      - the stage ring (gemm_mfma_kernel, kLoopStages): 32-deep k-tiles in
+//        3-8 whole stages, for short k.
+//  * MFMAs: v_mfma_f32_16x16x32 (gemm_m16_kernel, the default for k >= 256;
+//    it holds a higher clock than the 32x32x16 form for the same work on this
+//    power-limited chip) or v_mfma_f32_32x32x16 (gemm_mfma_kernel), always
+//    with the B fragment as the first operand.
 //  * Every operand tile goes global -> LDS directly (global_load_lds_dwordx4:
 //    lane i of a wave writes bytes [16i, 16i+16) of a 1 KiB LDS block, so the
-//    LDS swizzle is chosen by which global chunk each lane fetches).
-//  * k-tiles of 32 elements in a ring of 3-4 LDS stages: the loads of the
-//    next 2-3 tiles are in flight while tile i is multiplied; each wave waits
-//    only for the tile it needs next (partial vmcnt), one barrier per k-tile
-//    placed between the two k16 halves, and the LDS reads and global->LDS
-//    loads are interleaved one by one with the MFMAs (sched_group_barrier).
-//  * k-contiguous tiles (A, and B when stored n x k): rows of 64 bytes, chunk
-//    c of row r at position c ^ ((r >> 2) & 3).  B stored k x n
-//    keeps its n-contiguous rows in LDS (chunk c of k-row r at c ^ f(r & 3),
-//    f = {0, 4, 10, 14}) and is transposed on the way out by
-//    ds_read_b64_tr_b16.  Both layouts are free of LDS bank conflicts for
-//    the fragment reads.
+//    LDS swizzle is chosen by which global chunk each lane fetches); each wave
+//    waits only for the k-tile it reads next (partial vmcnt).
+//  * k-contiguous tiles (A, and B when stored n x k) and n-contiguous B
+//    tiles (B stored k x n, transposed on the way out by ds_read_b64_tr_b16)
+//    use XOR swizzles measured free of LDS bank conflicts for each form's
+//    fragment reads.
 //  * Rows past m, columns past n and k past the end are fed from a zero
-//    block, so ragged tails need no masking inside the main loop.
+//    block, so ragged tails need no masking inside the main loop; interior
+//    tiles take an unmasked loop.
 //  * Tile order: XCD-aware remap of the workgroup id, grouped row blocks for
 //    L2 reuse, then the plan's row-block visit order (ring order from the
 //    local shard, or natural order).
+//  * Epilogue: round-to-nearest-even cast, C staged through LDS and stored
+//    as whole rows with 16-byte lanes (interior tiles), or fp32 partial sums
+//    for split-K followed by a fixed-order reduction launch.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 

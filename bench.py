@@ -75,6 +75,11 @@ def parse():
     ap.add_argument("--only-run", action="store_true",
                     help="warmup + settle + K steps of the main path, then 3 gather copies of the "
                          "same shards (the known-size copy that calibrates HBM counters); for profilers")
+    ap.add_argument("--no-settle", action="store_true",
+                    help="--only-run without the untimed settle steps (counter runs: each dispatch "
+                         "is slow under the profiler, and counters do not depend on the clock)")
+    ap.add_argument("--launches-per-step", type=int, default=1,
+                    help="--summarize-trace: dominant-kernel launches one step makes (staged: chunks)")
     ap.add_argument("--summarize-trace", metavar="DIR",
                     help="write the profiles/ summary of a rocprofv3 --kernel-trace --stats CSV run "
                          "of --only-run")
@@ -191,7 +196,7 @@ def summarize_trace(args, w, variant):
     disp.sort(key=lambda r: int(r["Start_Timestamp"]))
     main = next(k for k in MAIN_KERNELS if any(_short(r["Kernel_Name"]) == k for r in disp))
     mains = [r for r in disp if _short(r["Kernel_Name"]) == main]
-    k_launches = args.steps * int(os.environ.get("AGMM_LAUNCHES_PER_STEP", "1"))
+    k_launches = args.steps * args.launches_per_step
     timed = mains[-k_launches:]
     durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in timed]
     # the step's companion kernels (split-K reduction), same count
@@ -314,13 +319,13 @@ class Bench:
             plan.run(sh, Bt, C, stream=s)
         return run
 
-    def warm(self, run, warmup):
+    def warm(self, run, warmup, settle=True):
         torch = self.torch
         for i in range(warmup):
             run(i, self.stream)
         torch.cuda.synchronize()
         n, t0 = 0, time.time()
-        while time.time() - t0 < SETTLE_S:
+        while settle and time.time() - t0 < SETTLE_S:
             run(n, self.stream)
             n += 1
             if n % 8 == 0:
@@ -588,7 +593,7 @@ def main():
         plan = b.plan(variant)
         try:
             run = b.runner(plan)
-            b.warm(run, args.warmup)
+            b.warm(run, args.warmup, settle=not args.no_settle)
             ms, _ = b.eager_steps(run, args.steps)
             used = agmm.VARIANT_NAMES[plan.get("variant_used")]
         finally:
