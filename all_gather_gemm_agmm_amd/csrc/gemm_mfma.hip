@@ -161,6 +161,34 @@ __device__ __forceinline__ void load_lds16_at(const void* gsrc, uint32_t lds_add
                : "m0");
 }
 
+// Buffer-descriptor form of the same load: the 64-bit base sits in the
+// scalar descriptor, each lane adds a 32-bit offset (`voff`) and the wave a
+// scalar one (`soff`).  Interior tiles use it: their per-lane offsets stay
+// fixed over the k loop, so a load costs no vector address arithmetic (the
+// flat form adds a 64-bit k offset to every lane's pointer per load), and the
+// descriptor's record count bounds every lane's offset.  LDS placement is the
+// flat form's: lane i writes bytes [16i, 16i+16) of the block at `lds_addr`.
+__device__ __forceinline__ void load_lds16_buf(const u32x4_t& rsrc, uint32_t voff, uint32_t soff,
+                                               uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %3 offen lds"
+               :
+               : "v"(voff), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(lds_addr)),
+                 "s"(__builtin_amdgcn_readfirstlane(soff))
+               : "m0");
+}
+
+// Raw buffer descriptor (stride 0, so the record count is in bytes) over
+// `bytes` bytes from `base`; the last word is the gfx9 data-format word.
+__device__ __forceinline__ u32x4_t buffer_rsrc(const void* base, uint64_t bytes) {
+  const uint64_t b = (uint64_t)(uintptr_t)base;
+  u32x4_t r;
+  r[0] = __builtin_amdgcn_readfirstlane((uint32_t)b);
+  r[1] = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32) & 0xFFFFu);
+  r[2] = __builtin_amdgcn_readfirstlane((uint32_t)bytes);
+  r[3] = 0x00020000u;
+  return r;
+}
+
 __device__ __forceinline__ u32x2_t read_tr(const char* p) {
   i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(lds_char_t*)p);
   return __builtin_bit_cast(u32x2_t, v);
@@ -218,6 +246,10 @@ __device__ __forceinline__ void tile_coords(const TileOrder& o, int wg, int nwg,
 template <bool B>
 struct BoolTag {
   static constexpr bool value = B;
+};
+template <int V>
+struct IntTag {
+  static constexpr int value = V;
 };
 
 constexpr int kLoopStages = 0;
@@ -880,6 +912,50 @@ void gemm_m16_kernel(GemmProblem p) {
     }
   }
 
+  // ---- buffer-descriptor sources (interior tiles whose rows lie in one
+  // shard; see load_lds16_buf) ---------------------------------------------
+  // A: base = first row of the tile at k_begin, lane offset = row * lda + its
+  // chunk; B (n x k) likewise by tile column; B (k x n): base = k_begin row at
+  // column n0, lane offset = k-row * ldb + its chunk.  The k offset of k-tile
+  // t is a scalar: 128 bytes per k-tile (A, B n x k) or 64 rows of B (k x n).
+  // Each record count is the tile's whole extent from its base (lane plus
+  // scalar offsets), which must stay below 4 GiB.
+  const int g0 = m0 / p.rows.rows_per_group;
+  const int row0 = m0 - g0 * p.rows.rows_per_group;
+  const int64_t kspan = (int64_t)(k_end - k_begin) * 2;
+  const int64_t a_span = (int64_t)(BM - 1) * p.rows.a_ld * 2 + kspan;
+  const int64_t b_span = BT ? (int64_t)(BN - 1) * p.ldb * 2 + kspan
+                            : (int64_t)(k_end - k_begin - 1) * p.ldb * 2 + BN * 2;
+  const bool buf_ok = (row0 + BM <= p.rows.rows_per_group) && a_span < (1ll << 32) && b_span < (1ll << 32);
+  u32x4_t rsrc_a{}, rsrc_b{};
+  uint32_t a_voff[T::A_IPW], b_voff[T::B_IPW];
+  if (buf_ok) {
+    rsrc_a = buffer_rsrc(static_cast<const char*>(p.rows.a_group[g0]) +
+                             ((int64_t)row0 * p.rows.a_ld + k_begin) * 2, (uint64_t)a_span);
+    rsrc_b = buffer_rsrc(static_cast<const char*>(p.b) +
+                             (BT ? (int64_t)n0 * p.ldb + k_begin : (int64_t)k_begin * p.ldb + n0) * 2,
+                         (uint64_t)b_span);
+  }
+#pragma unroll
+  for (int j = 0; j < T::A_IPW; ++j) {
+    const int r = (wave * T::A_IPW + j) * T::RPI + lane / T::CPR;
+    const int c = (lane % T::CPR) ^ swz_k16(r);
+    a_voff[j] = (uint32_t)(((int64_t)r * p.rows.a_ld + c * 8) * 2);
+  }
+#pragma unroll
+  for (int j = 0; j < T::B_IPW; ++j) {
+    if constexpr (BT) {
+      const int r = (wave * T::B_IPW + j) * T::RPI + lane / T::CPR;
+      const int c = (lane % T::CPR) ^ swz_k16(r);
+      b_voff[j] = (uint32_t)(((int64_t)r * p.ldb + c * 8) * 2);
+    } else {
+      const int byte = (wave * T::B_IPW + j) * 1024 + lane * 16;
+      const int kr = byte / T::B_ROW;
+      const int c = ((byte % T::B_ROW) >> 4) ^ swz_n16(kr);
+      b_voff[j] = (uint32_t)(((int64_t)kr * p.ldb + c * 8) * 2);
+    }
+  }
+
   // ---- LDS fragment offsets --------------------------------------------------
   const int g4 = lane >> 4, i16 = lane & 15;
   int a_off[FM], a_x[FM];
@@ -980,8 +1056,11 @@ void gemm_m16_kernel(GemmProblem p) {
   constexpr int PB = T::PART_BYTES;
   constexpr int SPREAD = STEPS - 1;
   const bool interior = (m0 + BM <= M) && (n0 + BN <= N) && ((k_end - k_begin) % kBK == 0) && nk > 0;
+  // load modes: 0 edge tiles (masked flat loads), 1 interior (flat), 2
+  // interior in one shard (buffer descriptors)
   auto ring = [&](auto tag) {
-    constexpr bool FAST = decltype(tag)::value;
+    constexpr int MODE = decltype(tag)::value;
+    constexpr bool FAST = MODE >= 1;
     auto a_addr = [&](int j, int t) -> const char* {
       if constexpr (FAST) {
         const int kk = k_begin + (t < nk ? t : nk - 1) * kBK;
@@ -1005,15 +1084,26 @@ void gemm_m16_kernel(GemmProblem p) {
     const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_char_t*)smem;
     const uint32_t lds_a = lds0 + wave * (T::A_IPW * 1024);
     const uint32_t lds_b = lds0 + wave * (T::B_IPW * 1024);
+    // scalar k offsets of k-tile t (k-tiles past the end re-read the last)
+    auto a_soff = [&](int t) -> uint32_t { return (uint32_t)((t < nk ? t : nk - 1) * kBK * 2); };
+    auto b_soff = [&](int t) -> uint32_t {
+      return (uint32_t)((int64_t)(t < nk ? t : nk - 1) * kBK * 2 * (BT ? 1 : p.ldb));
+    };
     auto put_a = [&](int slot, int t, int j0, int j1) {
 #pragma unroll
-      for (int j = j0; j < j1; ++j) load_lds16_at(a_addr(j, t), lds_a + slot * PB + j * 1024);
+      for (int j = j0; j < j1; ++j) {
+        if constexpr (MODE == 2) load_lds16_buf(rsrc_a, a_voff[j], a_soff(t), lds_a + slot * PB + j * 1024);
+        else load_lds16_at(a_addr(j, t), lds_a + slot * PB + j * 1024);
+      }
+    };
+    auto put_b_one = [&](int slot, int t, int j) {
+      if constexpr (MODE == 2) load_lds16_buf(rsrc_b, b_voff[j], b_soff(t), lds_b + slot * PB + j * 1024);
+      else load_lds16_at(b_addr(j, t), lds_b + slot * PB + j * 1024);
     };
     auto put_b = [&](int slot, int t) {
 #pragma unroll
-      for (int j = 0; j < T::B_IPW; ++j) load_lds16_at(b_addr(j, t), lds_b + slot * PB + j * 1024);
+      for (int j = 0; j < T::B_IPW; ++j) put_b_one(slot, t, j);
     };
-    auto put_b_one = [&](int slot, int t, int j) { load_lds16_at(b_addr(j, t), lds_b + slot * PB + j * 1024); };
     // Four half-steps per k-tile, (step, half) = (0,0) (0,1) (1,0) (1,1):
     //   (0,0) MFMAs A0 x Ba; reads Bb = B(step 0, half 1)
     //   (0,1) MFMAs A0 x Bb; reads A1 = A(step 1), Ba = B(step 1, half 0)
@@ -1153,8 +1243,9 @@ void gemm_m16_kernel(GemmProblem p) {
     }
     if constexpr (kTied && FAST) mfma16_drain(acc);
   };
-  if (interior) ring(BoolTag<true>{});
-  else ring(BoolTag<false>{});
+  if (interior && buf_ok) ring(IntTag<2>{});
+  else if (interior) ring(IntTag<1>{});
+  else ring(IntTag<0>{});
   wait_vmcnt<0>();
 
   // ---- epilogue: acc[i][j][e] = C[m0 + wm*TM + 16i + i16][n0 + wn*TN + 16j + 4g4 + e]
