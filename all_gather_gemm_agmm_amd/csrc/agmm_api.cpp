@@ -66,6 +66,8 @@ int hip_err(hipError_t e, const char* what) {
 }
 
 constexpr int64_t kDimLimit = int64_t(1) << 30;
+// automatic transposed copy of B (stored k x n) from this many rows of m
+constexpr int64_t kBtMinRows = 24576;
 constexpr int kTimingPairs = 4096;
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -122,6 +124,7 @@ struct Settings {
   int gemm_streams = 2;   // staged: chunk GEMMs alternate over this many streams (1 or 2)
   int local_first = 0;    // staged: the local shard's rows first, straight from its buffer
   int debug_keep_slots = 0;
+  int b_transpose = -1;   // B stored k x n: -1 automatic, 0 never, 1 always transposed per call
 };
 
 // Everything derived from the problem and the settings.
@@ -134,7 +137,11 @@ struct Layout {
   // and on B [n][kp] (rhs_transpose) or [kp][np] in its own buffer
   bool padded = false;
   int64_t kp = 0, np = 0;
-  size_t padb_bytes = 0;
+  // B stored k x n, transposed per call into the B copy: the GEMM then reads
+  // B as n x k (its B fragments are single 16-byte LDS reads instead of two
+  // transposing reads each)
+  bool bt = false;
+  size_t padb_bytes = 0;   // the B copy: zero-padded (padded) or transposed (bt)
   int64_t rows_per_chunk = 0;
   int num_chunks = 1;
   int nslots = 0;
@@ -172,7 +179,7 @@ struct agmm_plan {
   size_t ws_cap = 0;
   char* ring = nullptr;
   float* partials = nullptr;
-  char* padb = nullptr;             // zero-padded B (padded layouts)
+  char* padb = nullptr;             // B copy: zero-padded (padded layouts) or transposed (bt)
   int32_t* d_order = nullptr;
   // last automatic group_m choice, keyed by the launch's block counts
   int64_t group_key_rb = -1, group_key_cb = -1;
@@ -189,6 +196,7 @@ struct agmm_plan {
   unsigned long long done_capture_id = 0;
   hipStream_t done_stream = nullptr;
   bool captured = false;            // some call was captured into a graph
+  unsigned long long staged_capture_id = 0;   // capture holding a staged call, or 0
   int broken = AGMM_OK;             // status that left the plan unusable, or AGMM_OK
   std::string broken_msg;
   // timing
@@ -208,7 +216,7 @@ int64_t ldc_of(const agmm_plan* p) { return p->s.ldc ? p->s.ldc : p->n; }
 
 // Tile choice for the MFMA path: fewest rounds of workgroups over the CUs,
 // weighted by the per-tile efficiency of the larger shapes.
-int choose_tile(const agmm_plan* p, const Settings& s, int64_t m) {
+int choose_tile(const agmm_plan* p, const Settings& s, int64_t m, bool bnk) {
   if (s.tile >= 0) return s.tile;
   struct Cand { int cfg; double eff; };
   // The 256x256 and 128x128 tiles run as the 64-deep part ring on 16x16x32
@@ -225,7 +233,7 @@ int choose_tile(const agmm_plan* p, const Settings& s, int64_t m) {
   int best = big;
   double best_cost = 1e300;
   for (const Cand& c : cands) {
-    if (c.cfg == agmm::kTile256x224m16 && !(deep && p->rt)) continue;
+    if (c.cfg == agmm::kTile256x224m16 && !(deep && bnk)) continue;
     const int64_t bm = agmm::tile_bm(c.cfg), bn = agmm::tile_bn(c.cfg);
     const int64_t tiles = cdiv(m, bm) * cdiv(p->n, bn);
     const int64_t waves = cdiv(tiles, p->cu_count);
@@ -323,8 +331,17 @@ int derive_launch(const agmm_plan* p, const Settings& s, Layout& L) {
                    "the gather copy needs 16-byte rows (k * elem_bytes %% 16 == 0)");
   L.variant_used = v;
 
+  // B stored k x n: transposed once per call into the workspace when the
+  // GEMM is large enough to repay it.  Measured on 8x4096x8192 -> 7168 bf16:
+  // the GEMM takes 2700 us on B k x n and 2619 us on B n x k, the transpose
+  // of the 117 MB B 44 us; the gain grows with m and breaks even near
+  // m = 18K rows (a GEMM about 3% faster against a copy of 2 k n e bytes).
+  L.bt = !is_f32(p) && !L.padded && !p->rt && v != AGMM_VARIANT_SKINNY &&
+         (s.b_transpose > 0 || (s.b_transpose < 0 && p->k >= 256 && p->m >= kBtMinRows));
+  const bool bnk = p->rt || L.bt;   // the GEMM reads B as n x k
+
   // tiles
-  if (!is_f32(p) && s.tile >= 0 && agmm::tile_needs_bt(s.tile) && !p->rt)
+  if (!is_f32(p) && s.tile >= 0 && agmm::tile_needs_bt(s.tile) && !bnk)
     return set_err(AGMM_ERR_UNSUPPORTED, "tile %d needs B stored n x k (rhs_transpose)", s.tile);
   if (is_f32(p)) {
     L.tile_used = -1;
@@ -345,9 +362,9 @@ int derive_launch(const agmm_plan* p, const Settings& s, Layout& L) {
     } else if (v == AGMM_VARIANT_STAGED) {
       // tile chosen for one chunk's launch (pvalue tile-rows of every shard)
       const int64_t chunk_m = (int64_t)p->N * std::min<int64_t>(p->m_s, (int64_t)s.pvalue * 256);
-      L.tile_used = choose_tile(p, s, chunk_m);
+      L.tile_used = choose_tile(p, s, chunk_m, bnk);
     } else {
-      L.tile_used = choose_tile(p, s, p->m);
+      L.tile_used = choose_tile(p, s, p->m, bnk);
     }
     L.bm = agmm::tile_bm(L.tile_used);
     L.bn = agmm::tile_bn(L.tile_used);
@@ -382,6 +399,7 @@ int derive_launch(const agmm_plan* p, const Settings& s, Layout& L) {
     L.ring_bytes = L.slot_bytes;
     if (L.padded) L.padb_bytes = (size_t)(p->rt ? p->n * L.kp : L.kp * L.np) * e;
   }
+  if (L.bt) L.padb_bytes = (size_t)p->n * p->k * e;
   // split-K: skinny problems always, the other variants when one launch has
   // too few output tiles to give every CU a workgroup.  A power of two of k
   // ranges (multiples of the k granularity), chosen so that splits * tiles
@@ -624,8 +642,8 @@ agmm::GemmProblem base_problem(agmm_plan* p, const agmm::RowMap& rows, int64_t m
   g.m = (int32_t)m_launch;
   g.n = (int32_t)p->n;
   g.k = (int32_t)p->k;
-  g.b = B;
-  g.ldb = ldb_of(p);
+  g.b = p->L.bt ? p->padb : B;
+  g.ldb = p->L.bt ? p->k : ldb_of(p);
   g.c = C;
   g.ldc = ldc_of(p);
   g.order.num_rb = (int32_t)cdiv(m_launch, p->L.bm);
@@ -671,7 +689,7 @@ int launch_gemm(agmm_plan* p, const Call& c, agmm::GemmProblem& g, hipStream_t s
   if (is_f32(p)) err = agmm::launch_gemm_f32(g, p->rt != 0, s);
   else if (p->L.tile_used == agmm::kTileSkinny)
     err = agmm::launch_skinny_fullk(g, p->dtype, p->L.skinny_shape_used, s);
-  else err = agmm::launch_gemm_mfma(g, p->L.tile_used, p->dtype, p->rt != 0, s);
+  else err = agmm::launch_gemm_mfma(g, p->L.tile_used, p->dtype, p->rt != 0 || p->L.bt, s);
   if (err != hipSuccess) return hip_err(err, "GEMM launch");
   if (timed) {
     hipEventRecord(p->tev[p->tev_used + 1], s);
@@ -905,6 +923,24 @@ int run_staged(agmm_plan* p, const Call& c, const void* const* shards, const voi
   // faster on 8x4096x8192 -> 7168, slower where the launches are small
   // (4x512x4096 -> 1024: 62 -> 75 us; with one chunk, 28 -> 43 us on
   // 8x16x4096 -> 1792, so it is never used with a single chunk).
+  // Under graph capture only the staged forms whose replays are tested are
+  // accepted: one staged call per captured graph, with no ring slot refilled
+  // within the call (at most as many chunks as slots; the gathered-output
+  // form never refills one).  A process once ended in a segmentation fault
+  // while capturing several staged calls of a plan that refills slots into
+  // one graph, and that case was never shown to be safe, so it is refused
+  // before anything is enqueued.
+  if (c.capturing) {
+    if (!gathered && p->L.num_chunks > p->L.nslots)
+      return set_err(AGMM_ERR_UNSUPPORTED,
+                     "staged plan with %d chunks over %d ring slots: not under graph capture "
+                     "(at most as many chunks as slots: raise nbuf or pvalue)",
+                     p->L.num_chunks, p->L.nslots);
+    if (p->staged_capture_id == c.capture_id)
+      return set_err(AGMM_ERR_UNSUPPORTED,
+                     "a staged call of this plan is already in this graph capture (one per graph)");
+    p->staged_capture_id = c.capture_id;
+  }
   const bool local_first = p->s.local_first && p->N > 1 && p->L.num_chunks > 1;
   const bool alt = p->s.gemm_streams == 2 && p->L.splits_used == 1 && (p->L.num_chunks > 1 || local_first);
   int rc = fork_to(p, c, p->copy_stream);
@@ -938,10 +974,20 @@ int run_padded(agmm_plan* p, const Call& c, const void* const* shards, const voi
   return launch_gemm(p, c, g, c.s);
 }
 
+// The transposed copy of B (plans with L.bt): B^T [n][k] into the B copy on
+// the caller's stream, ahead of every GEMM of the call.
+int transpose_b(agmm_plan* p, const void* B, hipStream_t s) {
+  if (!p->L.bt) return AGMM_OK;
+  const hipError_t err = agmm::launch_transpose16(B, ldb_of(p), p->k, p->n, p->padb, s);
+  return err == hipSuccess ? AGMM_OK : hip_err(err, "B transpose launch");
+}
+
 // agmm_run's work, after enter().
 int run_plan(agmm_plan* p, const Call& c, const void* const* shard_ptrs, const void* B, void* C) {
   int rc;
   if (p->L.padded) return run_padded(p, c, shard_ptrs, nullptr, B, C);
+  rc = transpose_b(p, B, c.s);
+  if (rc != AGMM_OK) return rc;
   switch (p->L.variant_used) {
     case AGMM_VARIANT_FUSED:
     case AGMM_VARIANT_SKINNY: {
@@ -1108,6 +1154,9 @@ int agmm_plan_set_int(agmm_plan_t p, const char* key, int64_t v) {
   } else if (k == "debug_keep_slots") {
     if (v != 0 && v != 1) return bad();
     s.debug_keep_slots = (int)v;
+  } else if (k == "b_transpose") {
+    if (v < -1 || v > 1) return bad();
+    s.b_transpose = (int)v;
   } else {
     return set_err(AGMM_ERR_INVALID_ARG, "unknown key '%s'", key);
   }
@@ -1143,6 +1192,8 @@ int agmm_plan_get_int(agmm_plan_t p, const char* key, int64_t* value) {
   else if (k == "gemm_streams") v = s.gemm_streams;
   else if (k == "local_first") v = s.local_first;
   else if (k == "debug_keep_slots") v = s.debug_keep_slots;
+  else if (k == "b_transpose") v = s.b_transpose;
+  else if (k == "b_transposed") v = L.bt ? 1 : 0;
   else if (k == "num_chunks") v = L.num_chunks;
   else if (k == "rows_per_chunk") v = L.rows_per_chunk;
   else if (k == "num_slots") v = L.nslots;
@@ -1250,9 +1301,9 @@ int agmm_plan_autotune(agmm_plan_t p, const void* const* shard_ptrs, const void*
     std::vector<int> tiles = {agmm::kTile256x256m16, agmm::kTile256x256r5, agmm::kTile256x256,
                               agmm::kTile256x128,    agmm::kTile128x128m16, agmm::kTile128x128r5,
                               agmm::kTile128x128};
-    if (p->rt) {
+    if (p->rt || p->L.bt) {   // tiles that read B as n x k only
       tiles.insert(tiles.begin(), agmm::kTile256x224m16);
-      tiles.insert(tiles.begin(), agmm::kTileSkinny);
+      if (p->rt) tiles.insert(tiles.begin(), agmm::kTileSkinny);
       tiles.push_back(agmm::kTile128x64r5);
       tiles.push_back(agmm::kTile128x64);
       tiles.push_back(agmm::kTile128x64s8);
@@ -1322,6 +1373,8 @@ int agmm_run_gathered(agmm_plan_t p, const void* gathered, const void* B, void* 
   std::lock_guard<std::mutex> lk(p->mu);
   return guarded(p, static_cast<hipStream_t>(stream), [&](const Call& c) {
     if (p->L.padded) return run_padded(p, c, nullptr, gathered, B, C);
+    const int rtb = transpose_b(p, B, c.s);
+    if (rtb != AGMM_OK) return rtb;
     agmm::GemmProblem g = base_problem(p, dense_rows(gathered, p->m, p->k), p->m, B, C, -1);
     with_splits(p, g);
     return launch_gemm(p, c, g, c.s);
@@ -1343,6 +1396,8 @@ int agmm_run_gather_out(agmm_plan_t p, const void* const* shard_ptrs, const void
       const int r = gather_rows(p, shard_ptrs, gathered, 0, c.s);
       return r != AGMM_OK ? r : run_padded(p, c, shard_ptrs, nullptr, B, C);
     }
+    const int rtb = transpose_b(p, B, c.s);
+    if (rtb != AGMM_OK) return rtb;
     switch (p->L.variant_used) {
       case AGMM_VARIANT_STAGED:
         return run_staged(p, c, shard_ptrs, B, C, gathered);
@@ -1467,6 +1522,7 @@ int agmm_run_noalloc(int num_shards, int64_t m_per_shard, int64_t k, int64_t n_l
   p.m = (int64_t)num_shards * m_per_shard;
   p.dtype = dtype;
   p.rt = rhs_transpose;
+  p.s.b_transpose = 0;   // the transposed copy of B needs a plan's workspace
   rc = check_ptrs(&p, shard_ptrs, B, C);
   if (rc != AGMM_OK) return rc;
   hipError_t err = hipGetDevice(&p.device);

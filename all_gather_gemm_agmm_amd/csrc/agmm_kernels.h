@@ -139,6 +139,12 @@ struct PadCopyProblem {
 };
 hipError_t launch_pad_copy(const PadCopyProblem& p, hipStream_t stream);
 
+// Transpose of a 16-bit matrix: out[c * rows + r] = in[r * ld_in + c] for
+// r < rows, c < cols.  rows, cols and ld_in multiples of 8, both pointers
+// 16-byte aligned (else hipErrorInvalidValue, nothing launched).
+hipError_t launch_transpose16(const void* in, int64_t ld_in, int64_t rows, int64_t cols, void* out,
+                              hipStream_t stream);
+
 // Size of the device scratch of the no-allocation entry point (one per GPU,
 // held for the life of the process; equal to AGMM_NOALLOC_SCRATCH_BYTES).
 constexpr size_t kNoallocScratchBytes = size_t(32) << 20;

@@ -196,6 +196,46 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmProblem p) {
   }
 }
 
+// 16-bit transpose: out[c][r] = in[r][c] for r < rows, c < cols (in: row
+// stride ld_in elements; out: dense rows of `rows` elements).  Each wave
+// covers a 64 x 64 tile; lane (8 * rb + cb) loads the 8 x 8 block at rows
+// 8rb.., columns 8cb.. as 8 row pieces of 16 bytes (a wave's loads cover 8
+// whole 128-byte row segments per instruction), transposes it in registers
+// and stores 8 output row pieces of 16 bytes (again 128-byte segments per
+// instruction).  rows and cols are multiples of 8, so a block is either
+// wholly inside or wholly outside.  The source is read once (non-temporal
+// loads); the destination keeps ordinary stores, so the GEMM that reads it
+// next finds it in the MALL.
+constexpr int kTrWaves = 4;
+__global__ __launch_bounds__(64 * kTrWaves) void transpose16_kernel(const uint16_t* __restrict__ in,
+                                                                    int64_t ld_in, int64_t rows,
+                                                                    int64_t cols, int64_t tiles_c,
+                                                                    int64_t tiles,
+                                                                    uint16_t* __restrict__ out) {
+  const int lane = threadIdx.x & 63;
+  const int64_t tile = (int64_t)blockIdx.x * kTrWaves + (threadIdx.x >> 6);
+  if (tile >= tiles) return;
+  const int64_t tr = tile / tiles_c, tc = tile - tr * tiles_c;
+  const int64_t r0 = tr * 64 + (lane >> 3) * 8, c0 = tc * 64 + (lane & 7) * 8;
+  if (r0 >= rows || c0 >= cols) return;
+  u32x4_t v[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    v[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(in + (r0 + i) * ld_in + c0));
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    // output row c0 + j: element i is v[i] element j (16-bit half j & 1 of
+    // 32-bit word j / 2); word d packs elements 2d (low half) and 2d + 1
+    u32x4_t o;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const uint32_t lo = v[2 * d][j >> 1], hi = v[2 * d + 1][j >> 1];
+      o[d] = (j & 1) ? ((lo >> 16) | (hi & 0xFFFF0000u)) : ((lo & 0xFFFFu) | (hi << 16));
+    }
+    *reinterpret_cast<u32x4_t*>(out + (c0 + j) * rows + r0) = o;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_gather(const GatherProblem& p, int max_workgroups, hipStream_t stream) {
@@ -224,6 +264,21 @@ hipError_t launch_pad_copy(const PadCopyProblem& p, hipStream_t stream) {
     hipLaunchKernelGGL(pad_copy_kernel<2>, dim3((unsigned)wgs), dim3(256), 0, stream, p);
   else
     hipLaunchKernelGGL(pad_copy_kernel<4>, dim3((unsigned)wgs), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_transpose16(const void* in, int64_t ld_in, int64_t rows, int64_t cols, void* out,
+                              hipStream_t stream) {
+  if (rows % 8 != 0 || cols % 8 != 0 || ld_in % 8 != 0 || ld_in < cols || rows < 0 || cols < 0 ||
+      (reinterpret_cast<uintptr_t>(in) & 15) != 0 || (reinterpret_cast<uintptr_t>(out) & 15) != 0)
+    return hipErrorInvalidValue;
+  const int64_t tiles_c = (cols + 63) / 64;
+  const int64_t tiles = ((rows + 63) / 64) * tiles_c;
+  if (tiles == 0) return hipSuccess;
+  const int64_t wgs = (tiles + kTrWaves - 1) / kTrWaves;
+  hipLaunchKernelGGL(transpose16_kernel, dim3((unsigned)wgs), dim3(64 * kTrWaves), 0, stream,
+                     static_cast<const uint16_t*>(in), ld_in, rows, cols, tiles_c, tiles,
+                     static_cast<uint16_t*>(out));
   return hipGetLastError();
 }
 

@@ -399,7 +399,9 @@ class Bench:
                    "ms": ms, "per_step": per, "tile": plan.get("tile"), "splits": plan.get("splits")}
             if with_kernel:
                 res["kernel_ms"], res["launches_per_step"] = self.kernel_ms(plan, run, steps)
-            if not eager and ms < GRAPH_MAX_STEP_MS:
+            # a graph holds at most one staged call of a plan (the library refuses
+            # more), so staged steps keep the eager timing
+            if not eager and ms < GRAPH_MAX_STEP_MS and used != "staged":
                 res["ms"], res["per_step"] = self.graph_steps(run, steps)
                 res["timing"] = "HIP-graph replay of the K steps"
                 if with_kernel and used in ("fused", "skinny"):

@@ -144,9 +144,15 @@ agmm_plan_t agmm_plan_create(int num_shards, int64_t m_per_shard, int64_t k, int
  * Within one graph capture calls are ordered the same way.  Across a capture
  * boundary (a graph replay against eager calls) no event links them: the
  * caller orders replays with its streams, as for any graph.
+ * Graph capture of the staged variant is limited to the replayed and tested
+ * form: one staged call of a plan per captured graph, and at most as many
+ * chunks as ring slots (ceil(m_per_shard / (pvalue * tile rows)) <= nbuf);
+ * other staged calls under capture return AGMM_ERR_UNSUPPORTED before
+ * enqueuing anything (the capture stays valid).
  * Returns AGMM_OK, AGMM_ERR_INVALID_ARG (NULL plan/pointer),
- * AGMM_ERR_UNSUPPORTED (misaligned pointer), AGMM_ERR_HIP (launch failed), or
- * the status that left the plan unusable (see agmm_plan_set_int).
+ * AGMM_ERR_UNSUPPORTED (misaligned pointer, staged form not capturable),
+ * AGMM_ERR_HIP (launch failed), or the status that left the plan unusable
+ * (see agmm_plan_set_int).
  */
 int agmm_run(agmm_plan_t plan, const void *const *shard_ptrs, const void *B, void *C,
              void *stream);
@@ -232,7 +238,8 @@ int agmm_plan_autotune(agmm_plan_t plan, const void *const *shard_ptrs, const vo
  *                   in the 16x16x32 ring (rhs_transpose only; automatic where
  *                   its 224-column tiles fill whole rounds of workgroups that
  *                   256x256 tiles would leave partly idle).  A tile that
- *                   needs rhs_transpose on a plan without it is rejected
+ *                   needs rhs_transpose on a plan without it (and without
+ *                   the transposed copy of B, "b_transpose") is rejected
  *                   with AGMM_ERR_UNSUPPORTED.
  *   "splits"        0: automatic, else k-splits (fp32 partial sums, then a
  *                   fixed-order reduction) of every bf16/fp16 launch (for the
@@ -284,6 +291,18 @@ int agmm_plan_autotune(agmm_plan_t plan, const void *const *shard_ptrs, const vo
  *                   operand on fused, skinny and fp32 plans (see there)
  *   "debug_keep_slots" 0/1: staged variant uses one slot per chunk (nothing
  *                   is overwritten; for inspection by agmm_plan_slot_ptr)
+ *   "b_transpose"   -1 (automatic, the default), 0 or 1: for bf16/fp16 B
+ *                   stored k x n (no rhs_transpose; rows of whole 16-byte
+ *                   vectors) on the fused, unfused and staged variants, each
+ *                   call first writes B^T [n_local][k] into the workspace
+ *                   (a bit copy) and the GEMM then reads B as n x k: a
+ *                   plain 16-byte LDS read per B fragment instead of two
+ *                   transposing reads.  Automatic: on for k >= 256 and
+ *                   m >= 24576 (measured on 8x4096x8192 -> 7168 bf16: GEMM
+ *                   2700 -> 2619 us for a 44 us transpose; break-even near
+ *                   m = 18K).  The tile, k order and so the result are those
+ *                   of reading B directly.  get "b_transposed" reads 1 when
+ *                   the copy is in use.
  * A change waits for the plan's previous call to finish, then keeps the
  * workspace allocation if the new layout fits in it and reallocates it
  * otherwise.  It is all or nothing: when the new value is rejected (range,
@@ -302,13 +321,14 @@ int agmm_plan_set_int(agmm_plan_t plan, const char *key, int64_t value);
 /* Read a plan setting (keys above, plus "num_chunks", "rows_per_chunk",
  * "num_slots", "tile_bm", "tile_bn", "k_per_split", "num_row_blocks",
  * "cu_count", the resolved "variant_used", "group_m_used": the row-block
- * group a launch over the whole problem uses, "captured": 1 once a call was
- * captured into a graph, and "usable": 0 after a failed reconfiguration left
- * the plan without a workspace).  value: host pointer.  Returns AGMM_OK or
+ * group a launch over the whole problem uses, "b_transposed": 1 when calls
+ * copy B transposed first, "captured": 1 once a call was captured into a
+ * graph, and "usable": 0 after a failed reconfiguration left the plan
+ * without a workspace).  value: host pointer.  Returns AGMM_OK or
  * AGMM_ERR_INVALID_ARG. */
 int agmm_plan_get_int(agmm_plan_t plan, const char *key, int64_t *value);
 
-/* Bytes of device workspace the plan holds (ring, partials, tables; the
+/* Bytes of device workspace the plan holds (ring, partials, B copy, tables; the
  * allocation is kept when a new layout needs less). */
 size_t agmm_plan_workspace_bytes(agmm_plan_t plan);
 

@@ -266,9 +266,11 @@ def test_workload5_every_tile_every_variant():
     remain.  The oracle checks two rows of every 256-row block (one in each
     128-row wave half, at offsets that vary from block to block) over all
     7168 columns: every one of the 3584 output tiles and every wave's
-    sub-tile.  The three paths use the same tile and the same k order per
-    element, so their outputs must also be bit-identical, which covers every
-    element of the staged and unfused outputs."""
+    sub-tile.  The three paths use tiles of the 16x16x32 ring (the staged
+    chunks may take 256x224 tiles where the fused launch takes 256x256), which
+    share the k order per element, and the same splits, so their outputs must
+    also be bit-identical, which covers every element of the staged and
+    unfused outputs."""
     w, shards, B, sd, bd = workload_inputs(5)
     rows = block_rows(w.m, seed=5)
     outs = {}
@@ -290,7 +292,9 @@ def test_workload5_every_tile_every_variant():
         if variant == "fused":
             C_fused = C
         else:
-            assert outs[variant] == outs["fused"], (variant, outs)
+            ring16 = {agmm.TILES["256x256_m16"], agmm.TILES["128x128_m16"], agmm.TILES["256x224_m16"]}
+            assert {outs[variant][0], outs["fused"][0]} <= ring16, (variant, outs)
+            assert outs[variant][1] == outs["fused"][1], (variant, outs)
             assert torch.equal(C.view(torch.int16), C_fused.view(torch.int16)), variant
             del C
 
@@ -752,6 +756,141 @@ def test_graph_capture_replays(variant, settings):
         del g
     finally:
         plan.close()
+
+
+def test_graph_capture_refuses_untested_staged_forms():
+    """Under graph capture a staged plan accepts one call per graph with at
+    most as many chunks as ring slots; a plan that refills slots within a call,
+    or a second staged call in the same capture, is refused before anything is
+    enqueued, and the capture and the plan stay usable."""
+    N, k, n, dtype, rt = 4, 256, 136, BF16, True
+    # (a) 4 chunks over 2 slots: eager runs work, capture refuses
+    w, shards, B = make_case(N, 400, k, n, dtype, rt, seed=940)
+    plan = agmm.Plan(N, 400, k, n, dtype, rt, variant="staged", pvalue=1, tile=1, nbuf=2)
+    try:
+        assert plan.get("num_chunks") == 4 and plan.get("num_slots") == 2
+        sd = [to_device(x, dtype) for x in shards]
+        bd = to_device(B, dtype)
+        C = torch.empty((N * 400, n), dtype=torch.bfloat16, device="cuda")
+        plan.run(sd, bd, C)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            with pytest.raises(agmm.AgmmError) as ei:
+                plan.run(sd, bd, C)
+            assert ei.value.status == agmm.AGMM_ERR_UNSUPPORTED
+            C.fill_(0.0)                  # the capture goes on
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert not torch.any(C).item()
+        del g
+        C2 = plan.run(sd, bd)             # still usable eagerly
+        torch.cuda.synchronize()
+        check_against_oracle(w, shards, B, C2)
+    finally:
+        plan.close()
+    # (b) 2 chunks over 2 slots: the first call is captured, a second is refused
+    w, shards, B = make_case(N, 160, k, n, dtype, rt, seed=941)
+    plan = agmm.Plan(N, 160, k, n, dtype, rt, variant="staged", pvalue=1, tile=1, nbuf=2)
+    try:
+        assert plan.get("num_chunks") == 2 and plan.get("num_slots") == 2
+        sd = [to_device(x, dtype) for x in shards]
+        bd = to_device(B, dtype)
+        C = torch.empty((N * 160, n), dtype=torch.bfloat16, device="cuda")
+        C_other = torch.empty_like(C)
+        plan.run(sd, bd, C)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            plan.run(sd, bd, C)
+            with pytest.raises(agmm.AgmmError) as ei:
+                plan.run(sd, bd, C_other)
+            assert ei.value.status == agmm.AGMM_ERR_UNSUPPORTED
+        torch.cuda.synchronize()
+        C.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        check_against_oracle(w, shards, B, C)
+        del g
+    finally:
+        plan.close()
+
+
+# ------------------------------------------- transposed copy of B (stored k x n)
+@pytest.mark.parametrize("variant,dtype,settings", [
+    ("fused", BF16, {"tile": 9}), ("fused", FP16, {"tile": 8}), ("fused", BF16, {"tile": 9, "splits": 2}),
+    ("unfused", BF16, {"tile": 9}), ("staged", FP16, {"tile": 9, "pvalue": 1}),
+    ("fused", BF16, {"tile": 1})])
+def test_b_transposed_copy_bit_identical(variant, dtype, settings):
+    """B stored k x n with the plan's transposed copy (b_transpose 1): the GEMM
+    reads B^T as n x k.  Same tile and k order as reading B directly, so the
+    output is bit-identical to b_transpose 0, and it matches the oracle (ragged
+    m, n and tiles; also the 32x32 stage-ring tile)."""
+    N, m_s, k, n = 3, 200, 384, 392
+    w, shards, B = make_case(N, m_s, k, n, dtype, False, seed=960 + len(variant))
+    sd = [to_device(x, dtype) for x in shards]
+    bd = to_device(B, dtype)
+    outs = []
+    for bt in (1, 0):
+        plan = agmm.Plan(N, m_s, k, n, dtype, False, variant=variant, b_transpose=bt, **settings)
+        try:
+            assert plan.get("b_transposed") == bt
+            outs.append(plan.run(sd, bd))
+            torch.cuda.synchronize()
+        finally:
+            plan.close()
+    check_against_oracle(w, shards, B, outs[0])
+    assert np.array_equal(to_bits(outs[0]), to_bits(outs[1]))
+
+
+def test_b_transposed_copy_strided_and_gathered_calls():
+    """The transposed copy with a row-strided B (ldb > n, NaN in the gaps), the
+    n x k-only 256x224 tile, and through agmm_run_gathered / agmm_run_gather_out."""
+    N, m_s, k, n, dtype = 2, 300, 512, 456, BF16
+    w, shards, B = make_case(N, m_s, k, n, dtype, False, seed=971)
+    sd = [to_device(x, dtype) for x in shards]
+    ldb = n + 24
+    Bp = torch.full((k, ldb), float("nan"), dtype=torch.bfloat16, device="cuda")
+    Bp[:, :n] = to_device(B, dtype)
+    bview = Bp[:, :n]
+    plan = agmm.Plan(N, m_s, k, n, dtype, False, variant="fused", b_transpose=1, ldb=ldb,
+                     tile=agmm.TILES["256x224_m16"])
+    try:
+        assert plan.get("b_transposed") == 1 and plan.get("tile") == agmm.TILES["256x224_m16"]
+        C = plan.run(sd, bview)
+        torch.cuda.synchronize()
+        check_against_oracle(w, shards, B, C)
+        C2, G = plan.run_gather_out(sd, bview)
+        C3 = plan.run_gathered(G, bview)
+        torch.cuda.synchronize()
+        assert np.array_equal(to_bits(G), np.concatenate(shards, axis=0))
+        assert np.array_equal(to_bits(C2), to_bits(C))
+        assert np.array_equal(to_bits(C3), to_bits(C))
+    finally:
+        plan.close()
+
+
+def test_b_transposed_copy_automatic_choice():
+    """Automatic: B stored k x n is copied transposed for large m only (never
+    for B stored n x k, skinny plans or fp32), and a tile that reads B as
+    n x k only is refused on B k x n without the copy."""
+    big = agmm.Plan(8, 4096, 8192, 7168, BF16, False)
+    small = agmm.Plan(4, 512, 4096, 1024, BF16, False)
+    nk = agmm.Plan(8, 4096, 8192, 7168, BF16, True)
+    try:
+        assert big.get("b_transposed") == 1
+        assert small.get("b_transposed") == 0 and nk.get("b_transposed") == 0
+        with pytest.raises(agmm.AgmmError):
+            small.set("tile", agmm.TILES["256x224_m16"])
+        small.set("b_transpose", 1)
+        small.set("tile", agmm.TILES["256x224_m16"])
+        assert small.get("b_transposed") == 1
+    finally:
+        big.close()
+        small.close()
+        nk.close()
 
 
 def test_run_gathered_matches_fused():
