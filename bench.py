@@ -165,7 +165,8 @@ MAIN_KERNELS = ("gemm_m16_kernel", "gemm_mfma_kernel", "skinny_splitk_kernel", "
 
 
 def _short(name: str) -> str:
-    for key in MAIN_KERNELS + ("splitk_reduce_kernel", "skinny_reduce_kernel", "gather_kernel"):
+    for key in MAIN_KERNELS + ("splitk_reduce_kernel", "skinny_reduce_kernel", "gather_kernel",
+                               "transpose16_kernel"):
         if key in name:
             return key
     return name[:48]
@@ -199,10 +200,12 @@ def summarize_trace(args, w, variant):
     k_launches = args.steps * args.launches_per_step
     timed = mains[-k_launches:]
     durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in timed]
-    # the step's companion kernels (split-K reduction), same count
+    # the step's companion kernels (split-K reduction, transposed copy of B),
+    # one per dominant launch or one per step
     side = {}
-    for key in ("splitk_reduce_kernel", "skinny_reduce_kernel"):
-        rs = [r for r in disp if _short(r["Kernel_Name"]) == key][-k_launches:]
+    for key in ("splitk_reduce_kernel", "skinny_reduce_kernel", "transpose16_kernel"):
+        n_side = args.steps if key == "transpose16_kernel" else k_launches
+        rs = [r for r in disp if _short(r["Kernel_Name"]) == key][-n_side:]
         if rs:
             side[key] = sum((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rs) / len(rs)
     summary = {"workload": w.name, "variant": variant, "kernel": main, "kernel_sha": kernel_source_sha(),
@@ -260,6 +263,9 @@ def summarize_traffic(args, w, variant):
         if key in fetch:
             extra = {"reduce_kernel": key, "reduce_fetch_bytes": fetch[key] * 1024.0 * f_scale,
                      "reduce_write_bytes": write[key] * 1024.0 * w_scale}
+    if "transpose16_kernel" in fetch:
+        extra["transpose_fetch_bytes"] = fetch["transpose16_kernel"] * 1024.0 * f_scale
+        extra["transpose_write_bytes"] = write["transpose16_kernel"] * 1024.0 * w_scale
     d = {"workload": w.name, "variant": variant, "kernel": main,
          "kernel_sha": kernel_source_sha(),
          "fetch_kib_raw": fetch[main], "write_kib_raw": write[main],
@@ -441,7 +447,10 @@ class Bench:
             per_unit = flops_per_launch
             unit_peak = peak * 1e12
         if prof is not None:
-            us = prof["avg_us"] + sum(prof.get("companion_avg_us", {}).values())
+            # the GEMM launch the library times includes its split-K reduction,
+            # not the transposed copy of B that precedes it
+            us = prof["avg_us"] + sum(v for k, v in prof.get("companion_avg_us", {}).items()
+                                      if k != "transpose16_kernel")
             r["profile"] = {"file": f"profiles/kernel_trace_{w.name}_{variant}.json",
                             "kernel_us": round(us, 2), "median_us": round(prof["median_us"], 2),
                             "frac": round(per_unit / (us * 1e-6) / unit_peak, 4)}
