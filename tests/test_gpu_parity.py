@@ -823,12 +823,14 @@ def test_graph_capture_refuses_untested_staged_forms():
     ("fused", BF16, {"tile": 9}), ("fused", FP16, {"tile": 8}), ("fused", BF16, {"tile": 9, "splits": 2}),
     ("unfused", BF16, {"tile": 9}), ("staged", FP16, {"tile": 9, "pvalue": 1}),
     ("fused", BF16, {"tile": 1})])
-def test_b_transposed_copy_bit_identical(variant, dtype, settings):
+@pytest.mark.parametrize("k", [384, 328])
+def test_b_transposed_copy_bit_identical(variant, dtype, settings, k):
     """B stored k x n with the plan's transposed copy (b_transpose 1): the GEMM
     reads B^T as n x k.  Same tile and k order as reading B directly, so the
     output is bit-identical to b_transpose 0, and it matches the oracle (ragged
-    m, n and tiles; also the 32x32 stage-ring tile)."""
-    N, m_s, k, n = 3, 200, 384, 392
+    m, n and tiles, whole and ragged last k-tiles (k = 328: the transpose's
+    last row tile is partial too); also the 32x32 stage-ring tile)."""
+    N, m_s, n = 3, 200, 392
     w, shards, B = make_case(N, m_s, k, n, dtype, False, seed=960 + len(variant))
     sd = [to_device(x, dtype) for x in shards]
     bd = to_device(B, dtype)
@@ -843,6 +845,42 @@ def test_b_transposed_copy_bit_identical(variant, dtype, settings):
             plan.close()
     check_against_oracle(w, shards, B, outs[0])
     assert np.array_equal(to_bits(outs[0]), to_bits(outs[1]))
+
+
+def test_b_transposed_copy_graph_capture():
+    """A plan that copies B transposed, captured into a HIP graph (the
+    transpose and the GEMM are both in it) and replayed on new inputs: every
+    replay matches the oracle and is bit-identical to an eager run."""
+    N, m_s, k, n, dtype = 2, 256, 512, 264, BF16
+    w, shards, B = make_case(N, m_s, k, n, dtype, False, seed=980)
+    plan = agmm.Plan(N, m_s, k, n, dtype, False, variant="fused", b_transpose=1)
+    try:
+        assert plan.get("b_transposed") == 1
+        sd = [to_device(x, dtype) for x in shards]
+        bd = to_device(B, dtype)
+        C = torch.empty((N * m_s, n), dtype=torch.bfloat16, device="cuda")
+        plan.run(sd, bd, C)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            plan.run(sd, bd, C)
+        torch.cuda.synchronize()
+        for rep in range(3):
+            w2, sh2, B2 = make_case(N, m_s, k, n, dtype, False, seed=981 + rep)
+            for d, h in zip(sd, sh2):
+                d.copy_(to_device(h, dtype))
+            bd.copy_(to_device(B2, dtype))
+            C.fill_(float("nan"))
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            check_against_oracle(w2, sh2, B2, C)
+            C_eager = plan.run(sd, bd)
+            torch.cuda.synchronize()
+            assert np.array_equal(to_bits(C), to_bits(C_eager))
+        del g
+    finally:
+        plan.close()
 
 
 def test_b_transposed_copy_strided_and_gathered_calls():
