@@ -86,6 +86,9 @@ def parse():
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/ traffic summary from rocprofv3 --pmc FETCH_SIZE and "
                          "--pmc WRITE_SIZE CSV runs of --only-run")
+    ap.add_argument("--summarize-timeline", metavar="DIR",
+                    help="write the profiles/ kernel timeline (copy / GEMM overlap) of a rocprofv3 "
+                         "--kernel-trace CSV run of --only-run")
     ap.add_argument("--command", default="", help="profiler command line, recorded in summaries")
     return ap.parse_args()
 
@@ -221,6 +224,61 @@ def summarize_trace(args, w, variant):
         lines += ["", "Companion kernels per step (avg us): " +
                   ", ".join(f"{k} {v:.2f}" for k, v in side.items())]
     lines += ["", "Full kernel symbols:", ""] + [f"- `{o['kernel']}`" for o in out]
+    with open(os.path.join(ROOT, "profiles", name + ".md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    with open(os.path.join(ROOT, "profiles", name + ".json"), "w") as f:
+        json.dump(summary, f, indent=1)
+    print(os.path.join("profiles", name + ".md"), json.dumps(summary))
+
+
+def summarize_timeline(args, w, variant):
+    """Kernel timeline of the K timed steps of a `--only-run` trace: how much
+    of the gather copies' time ran beside a GEMM launch, and the dispatches of
+    the last two steps with their start and end times."""
+    disp = _csv_rows(args.summarize_timeline, "kernel_trace.csv")
+    disp = [r for r in disp if "rocclr" not in r["Kernel_Name"]]
+    disp.sort(key=lambda r: int(r["Start_Timestamp"]))
+    gathers = [i for i, r in enumerate(disp) if _short(r["Kernel_Name"]) == "gather_kernel"]
+    disp = disp[:gathers[-3]]   # the 3 calibration copies run last
+    main = next(k for k in MAIN_KERNELS if any(_short(r["Kernel_Name"]) == k for r in disp))
+    gemm_idx = [i for i, r in enumerate(disp) if _short(r["Kernel_Name"]) == main]
+    k_launches = args.steps * args.launches_per_step
+    first = gemm_idx[-k_launches]
+    # the timed steps start with the copy that feeds their first GEMM
+    lo = max([i for i in range(first) if _short(disp[i]["Kernel_Name"]) == "gather_kernel"] or [first])
+    window = disp[lo:]
+    iv = [(int(r["Start_Timestamp"]), int(r["End_Timestamp"]), _short(r["Kernel_Name"])) for r in window]
+    t0 = iv[0][0]
+    gemm_iv = sorted((a, b) for a, b, k in iv if k == main)
+    copy_iv = [(a, b) for a, b, k in iv if k == "gather_kernel"]
+
+    def overlap(a, b):
+        return sum(max(0, min(b, y) - max(a, x)) for x, y in gemm_iv)
+
+    copy_ns = sum(b - a for a, b in copy_iv)
+    copy_beside = sum(overlap(a, b) for a, b in copy_iv)
+    wall_us = (max(b for _, b, _ in iv) - t0) / 1e3
+    summary = {"workload": w.name, "variant": variant, "steps": args.steps, "step_us": wall_us / args.steps,
+               "gemm_launches": len(gemm_iv), "copies": len(copy_iv),
+               "copy_us_per_step": copy_ns / 1e3 / args.steps,
+               "copy_us_beside_gemm_per_step": copy_beside / 1e3 / args.steps,
+               "copy_frac_beside_gemm": copy_beside / copy_ns if copy_ns else 0.0,
+               "gemm_us_per_step": sum(b - a for a, b in gemm_iv) / 1e3 / args.steps,
+               "kernel_sha": kernel_source_sha(), "command": args.command}
+    name = f"timeline_{w.name}_{variant}"
+    lines = [f"# rocprofv3 kernel timeline: {w.name}, {variant} path", "", f"command: `{args.command}`", "",
+             f"Over the {args.steps} timed steps: {summary['step_us']:.1f} us per step; gather copies "
+             f"{summary['copy_us_per_step']:.1f} us per step, of which {summary['copy_us_beside_gemm_per_step']:.1f} us "
+             f"({100 * summary['copy_frac_beside_gemm']:.0f}%) ran while a `{main}` launch was running; "
+             f"GEMM launches {summary['gemm_us_per_step']:.1f} us per step (summed over launches, which may overlap).",
+             "", "Dispatches of the last two steps (us from the first listed):", "",
+             "| kernel | stream | start | end | duration |", "|---|---|---|---|---|"]
+    per_step = max(1, len(window) // args.steps)
+    for r in window[-2 * per_step:]:
+        a, b = int(r["Start_Timestamp"]), int(r["End_Timestamp"])
+        base = int(window[-2 * per_step]["Start_Timestamp"])
+        lines.append(f"| {_short(r['Kernel_Name'])} | {r.get('Stream_Id', r.get('Queue_Id', ''))} | "
+                     f"{(a - base) / 1e3:.1f} | {(b - base) / 1e3:.1f} | {(b - a) / 1e3:.1f} |")
     with open(os.path.join(ROOT, "profiles", name + ".md"), "w") as f:
         f.write("\n".join(lines) + "\n")
     with open(os.path.join(ROOT, "profiles", name + ".json"), "w") as f:
@@ -571,12 +629,14 @@ def cpu_baseline(args, w, shards_np, B_np, I, np):
 def main():
     faulthandler.enable()   # a native crash prints the Python stack
     args = parse()
-    if args.summarize_trace or args.summarize_traffic:
+    if args.summarize_trace or args.summarize_traffic or args.summarize_timeline:
         from all_gather_gemm_agmm_amd import inputs as I
         w = I.WORKLOADS[args.workload]
         variant = resolve_variant(w, args.variant)
         if args.summarize_trace:
             summarize_trace(args, w, variant)
+        if args.summarize_timeline:
+            summarize_timeline(args, w, variant)
         if args.summarize_traffic:
             summarize_traffic(args, w, variant)
         return
