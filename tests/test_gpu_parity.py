@@ -313,6 +313,52 @@ def test_gather_bit_exact(dtype):
     assert np.array_equal(to_bits(G), oracle.gather(shards, dtype))
 
 
+@pytest.mark.parametrize("dtype,k,lda", [
+    (BF16, 8, 0), (BF16, 56, 0), (BF16, 264, 0), (BF16, 2040, 0), (BF16, 2048, 0),
+    (BF16, 2056, 0), (FP16, 8000, 0), (FP32, 4, 0), (FP32, 1028, 0), (BF16, 264, 280)])
+def test_gather_row_shapes_bit_exact(dtype, k, lda):
+    """The gather copy's work split: rows shorter than 256 16-byte chunks
+    packed several to a workgroup (with a partial last workgroup), rows of
+    exactly 256 chunks, rows with a partial last 256-chunk block, and a
+    row-strided source (lda > k, NaN in the gaps)."""
+    N, m_s = 5, 37
+    w, shards, B = make_case(N, m_s, k, 8, dtype, False, seed=990 + k)
+    tdt = torch_dtype(dtype)
+    if lda:
+        sd = []
+        for x in shards:
+            t = torch.full((m_s, lda), float("nan"), dtype=tdt, device="cuda")
+            t[:, :k] = to_device(x, dtype)
+            sd.append(t[:, :k])
+    else:
+        sd = [to_device(x, dtype) for x in shards]
+    plan = agmm.Plan(N, m_s, k, 8, dtype, False, **({"lda": lda} if lda else {}))
+    try:
+        G = torch.full((N * m_s, k), float("nan"), dtype=tdt, device="cuda")
+        plan.gather(sd, G)
+        torch.cuda.synchronize()
+    finally:
+        plan.close()
+    assert np.array_equal(to_bits(G), oracle.gather(shards, dtype))
+
+
+def test_gather_capped_grid_strides_bit_exact():
+    """A copy whose grid is capped below its work items (the side copy of
+    agmm_run_gather_out with copy_wgs 3) walks the items in strides: the
+    gathered output is still the bit-exact concatenation, and C matches."""
+    N, m_s, k, n, dtype = 4, 300, 2056, 72, BF16
+    w, shards, B = make_case(N, m_s, k, n, dtype, True, seed=995)
+    sd = [to_device(x, dtype) for x in shards]
+    plan = agmm.Plan(N, m_s, k, n, dtype, True, variant="fused", gather_out=1, copy_wgs=3)
+    try:
+        C, G = plan.run_gather_out(sd, to_device(B, dtype))
+        torch.cuda.synchronize()
+    finally:
+        plan.close()
+    assert np.array_equal(to_bits(G), np.concatenate(shards, axis=0))
+    check_against_oracle(w, shards, B, C)
+
+
 def test_gather_larger_than_mall_bit_exact():
     """A gather above 256 MiB (workload 5's 8 shards x 4096 x 8192 bf16 =
     512 MiB; the copy then uses non-temporal stores): bit-exact against the
