@@ -376,7 +376,9 @@ void agmm_plan_destroy(agmm_plan_t plan);
  * the first call on each device (make that first call outside graph
  * capture).  Arguments, layouts (dense rows), alignment and stream rules are
  * agmm_run's.  Tile visit order is the natural one (the values do not depend
- * on it), so C is bit-identical to agmm_run's on a default plan.
+ * on it), and B stored k x n is read directly (the transposed copy of B,
+ * "b_transpose", needs a plan's workspace; it does not change the bits), so
+ * C is bit-identical to agmm_run's on a default plan.
  * Every call on one GPU shares that GPU's scratch and leaves its partial sums
  * there: calls whose work overlaps on one GPU (different streams without an
  * ordering between them, or host threads) race and may return wrong values;
