@@ -24,10 +24,14 @@
 //    it holds a higher clock than the 32x32x16 form for the same work on this
 //    power-limited chip) or v_mfma_f32_32x32x16 (gemm_mfma_kernel), always
 //    with the B fragment as the first operand.
-//  * Every operand tile goes global -> LDS directly (global_load_lds_dwordx4:
-//    lane i of a wave writes bytes [16i, 16i+16) of a 1 KiB LDS block, so the
-//    LDS swizzle is chosen by which global chunk each lane fetches); each wave
-//    waits only for the k-tile it reads next (partial vmcnt).
+//  * Every operand tile goes global -> LDS directly (lane i of a wave writes
+//    bytes [16i, 16i+16) of a 1 KiB LDS block, so the LDS swizzle is chosen
+//    by which global chunk each lane fetches); each wave waits only for the
+//    k-tile it reads next (partial vmcnt).  gemm_m16_kernel loads interior
+//    tiles whose rows lie in one shard through buffer descriptors
+//    (buffer_load_dwordx4 ... lds: scalar base and k offset, fixed 32-bit
+//    lane offsets); other tiles use global_load_lds_dwordx4 with 64-bit lane
+//    addresses.
 //  * k-contiguous tiles (A, and B when stored n x k) and n-contiguous B
 //    tiles (B stored k x n, transposed on the way out by ds_read_b64_tr_b16)
 //    use XOR swizzles measured free of LDS bank conflicts for each form's
