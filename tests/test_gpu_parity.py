@@ -1259,3 +1259,75 @@ def test_oom_hook_reports_status(monkeypatch):
     with pytest.raises(agmm.AgmmError) as ei:
         agmm.Plan(2, 512, 256, 256, BF16, False, variant="unfused")
     assert ei.value.status == agmm.AGMM_ERR_OOM
+
+
+# -------------------------------- randomized sweep of layouts and copies of B
+def _random_layout_case(seed):
+    """A seeded random problem for the layout-related settings the sweep above
+    leaves out: the transposed copy of B (b_transpose), row strides (lda,
+    ldb) and padded shapes (k not a multiple of 8), across variants, tiles
+    and k splits."""
+    rng = np.random.default_rng(7000 + seed)
+    dtype = [BF16, FP16, BF16, FP32][seed % 4]
+    variant = ["fused", "staged", "unfused", "fused", "skinny", "auto"][seed % 6]
+    rt = bool(rng.integers(0, 2)) and seed % 3 != 0
+    N = int(rng.integers(1, 7))
+    m_s = int(rng.integers(1, 32)) if variant == "skinny" else int(rng.integers(1, 170))
+    k = int(rng.integers(1, 66)) * 8
+    n = int(rng.integers(1, 300))
+    if dtype != FP32 and not rt:
+        n = max(8, n - n % 8)          # whole 16-byte B rows
+    padded = dtype != FP32 and seed % 7 == 3
+    if padded:
+        k += int(rng.integers(1, 8))   # rows that are not 16-byte vectors
+    settings = {}
+    if dtype != FP32 and variant not in ("skinny", "auto"):
+        bt = not rt and not padded and rng.random() < 0.8
+        if bt:
+            settings["b_transpose"] = 1    # first, so that n x k-only tiles are allowed
+        tiles = [0, 1, 2, 5, 6, 8, 9] + ([3, 4, 7, 11] if (rt or bt) else [])
+        settings["tile"] = int(rng.choice(tiles))
+        settings["splits"] = int(rng.integers(0, 4))
+    if variant == "staged":
+        settings["pvalue"] = int(rng.integers(1, 4))
+        settings["nbuf"] = int(rng.integers(1, 4))
+    e = 4 if dtype == FP32 else 2
+    lda = ldb = 0
+    if not padded and rng.integers(0, 2) == 0:
+        # at least the row length, and a whole number of 16-byte vectors
+        vec = 16 // e
+        lda = k + vec * int(rng.integers(1, 4))
+        row_b = k if rt else n
+        ldb = row_b + (-row_b) % vec + vec * int(rng.integers(1, 4))
+    return variant, dtype, rt, N, m_s, k, n, settings, lda, ldb
+
+
+@pytest.mark.parametrize("seed", list(range(24)))
+def test_randomized_layouts_against_oracle(seed):
+    variant, dtype, rt, N, m_s, k, n, settings, lda, ldb = _random_layout_case(seed)
+    w, shards, B = make_case(N, m_s, k, n, dtype, rt, seed=8000 + seed)
+    plan = agmm.Plan(N, m_s, k, n, dtype, rt, variant=variant, **settings)
+    try:
+        if lda:
+            plan.set("lda", lda)
+        if ldb:
+            plan.set("ldb", ldb)
+        sd = [to_device(x, dtype) for x in shards]
+        bd = to_device(B, dtype)
+        if lda:
+            sd = [strided(t, lda) for t in sd]
+        if ldb:
+            bd = strided(bd, ldb)
+        C = torch.full((w.m, n), float("nan"), dtype=torch_dtype(dtype), device="cuda")
+        plan.run(sd, bd, C)
+        torch.cuda.synchronize()
+        desc = (f"{variant} dtype {dtype} rt {int(rt)} {N}x{m_s}x{k}->{n} {settings} lda {lda} ldb {ldb} "
+                f"-> tile {plan.get('tile')} splits {plan.get('splits')} variant_used "
+                f"{plan.get('variant_used')} b_transposed {plan.get('b_transposed')}")
+    finally:
+        plan.close()
+    assert not torch.isnan(C.float()).any().item(), desc
+    try:
+        check_against_oracle(w, shards, B, C)
+    except AssertionError as err:
+        raise AssertionError(f"{desc}: {err}") from None
