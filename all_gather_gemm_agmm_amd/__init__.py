@@ -231,9 +231,14 @@ def _torch_dtype(dtype: int):
     return {AGMM_BF16: torch.bfloat16, AGMM_FP16: torch.float16, AGMM_FP32: torch.float32}[dtype]
 
 
-def _stream_handle(stream) -> int:
+def _stream_handle(stream, device_index=None) -> int:
+    """The raw hipStream_t of `stream`, or of the current stream of the given
+    (else the current) device."""
     import torch
     if stream is None:
+        raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+        if raw is not None:   # the pointer alone, without a Stream object
+            return int(raw(torch.cuda.current_device() if device_index is None else device_index))
         stream = torch.cuda.current_stream()
     return int(stream.cuda_stream)
 
@@ -247,24 +252,45 @@ class Plan:
         self.num_shards, self.m_per_shard, self.k, self.n_local = num_shards, m_per_shard, k, n_local
         self.dtype, self.rhs_transpose = dtype, bool(rhs_transpose)
         self.handle = agmm_plan_create(num_shards, m_per_shard, k, n_local, dtype, rhs_transpose)
+        self._tdt = _torch_dtype(dtype)
+        self._ptrs = (ctypes.c_void_p * num_shards)()   # shard pointer table, reused per call
+        self._read_strides()
         for key, val in settings.items():
             if val is not None:
                 self.set(key, VARIANTS[val] if key == "variant" and isinstance(val, str) else val)
+
+    def _read_strides(self):
+        # row strides in use, kept here so that per-call checks need no
+        # call into the library
+        self._ld = {k: agmm_plan_get_int(self.handle, k) for k in ("lda", "ldb", "ldc")}
 
     @property
     def m(self) -> int:
         return self.num_shards * self.m_per_shard
 
     def set(self, key: str, value: int) -> None:
-        agmm_plan_set_int(self.handle, key, value)
+        try:
+            agmm_plan_set_int(self.handle, key, value)
+        finally:
+            self._read_strides()
 
     def get(self, key: str) -> int:
         return agmm_plan_get_int(self.handle, key)
 
-    def _check_tensor(self, t, shape, name, ld_key=None):
+    def _check_tensor(self, t, shape, name, ld_key=None, index=None):
         """Shape / dtype / device checks.  With `ld_key` ("lda", "ldb", "ldc")
         the tensor may be a row-strided view whose row stride is the plan's
         setting for that key; otherwise it must be dense row-major."""
+        ld = self._ld[ld_key] if ld_key else shape[1]
+        try:   # the common case in a few attribute reads
+            st = t.stride()
+            if (t.dtype is self._tdt and t.is_cuda and t.shape == shape and st[1] == 1 and
+                    (shape[0] <= 1 or st[0] == ld)):
+                return
+        except (AttributeError, TypeError, IndexError):
+            pass
+        if index is not None:
+            name = f"{name}[{index}]"
         import torch
         if not isinstance(t, torch.Tensor):
             raise TypeError(f"{name} must be a torch.Tensor")
@@ -274,7 +300,6 @@ class Plan:
             raise TypeError(f"{name} has dtype {t.dtype}, plan expects {_torch_dtype(self.dtype)}")
         if tuple(t.shape) != tuple(shape):
             raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
-        ld = self.get(ld_key) if ld_key else shape[1]
         if t.stride(1) != 1 or (shape[0] > 1 and t.stride(0) != ld):
             raise ValueError(f"{name} must be row-major with rows {ld} elements apart "
                              f"(stride {tuple(t.stride())})")
@@ -282,24 +307,25 @@ class Plan:
     def _new_c(self, device):
         """A C buffer with the plan's row stride (a view when ldc > n_local)."""
         import torch
-        ldc = self.get("ldc")
+        ldc = self._ld["ldc"]
         return torch.empty((self.m, ldc), dtype=_torch_dtype(self.dtype), device=device)[:, :self.n_local]
 
     def b_shape(self):
         return (self.n_local, self.k) if self.rhs_transpose else (self.k, self.n_local)
 
     def run(self, shards, B, C=None, stream=None):
-        import torch
         if len(shards) != self.num_shards:
             raise ValueError(f"expected {self.num_shards} shards, got {len(shards)}")
+        shape, ptrs = (self.m_per_shard, self.k), self._ptrs
         for r, s in enumerate(shards):
-            self._check_tensor(s, (self.m_per_shard, self.k), f"shards[{r}]", "lda")
+            self._check_tensor(s, shape, "shards", "lda", r)
+            ptrs[r] = s.data_ptr()
         self._check_tensor(B, self.b_shape(), "B", "ldb")
         if C is None:
             C = self._new_c(B.device)
         self._check_tensor(C, (self.m, self.n_local), "C", "ldc")
-        agmm_run(self.handle, [s.data_ptr() for s in shards], B.data_ptr(), C.data_ptr(),
-                 _stream_handle(stream))
+        _check(load_library().agmm_run(self.handle, ptrs, B.data_ptr(), C.data_ptr(),
+                                       _stream_handle(stream, B.device.index)))
         return C
 
     def run_gather_out(self, shards, B, C=None, gathered=None, stream=None):
@@ -308,7 +334,7 @@ class Plan:
         if len(shards) != self.num_shards:
             raise ValueError(f"expected {self.num_shards} shards, got {len(shards)}")
         for r, s in enumerate(shards):
-            self._check_tensor(s, (self.m_per_shard, self.k), f"shards[{r}]", "lda")
+            self._check_tensor(s, (self.m_per_shard, self.k), "shards", "lda", r)
         self._check_tensor(B, self.b_shape(), "B", "ldb")
         if C is None:
             C = self._new_c(B.device)
@@ -317,7 +343,7 @@ class Plan:
         self._check_tensor(C, (self.m, self.n_local), "C", "ldc")
         self._check_tensor(gathered, (self.m, self.k), "gathered")
         agmm_run_gather_out(self.handle, [s.data_ptr() for s in shards], B.data_ptr(), C.data_ptr(),
-                            gathered.data_ptr(), _stream_handle(stream))
+                            gathered.data_ptr(), _stream_handle(stream, B.device.index))
         return C, gathered
 
     def autotune(self, shards, B, C=None, iters=3, stream=None) -> float:
@@ -326,7 +352,7 @@ class Plan:
         if len(shards) != self.num_shards:
             raise ValueError(f"expected {self.num_shards} shards, got {len(shards)}")
         for r, s in enumerate(shards):
-            self._check_tensor(s, (self.m_per_shard, self.k), f"shards[{r}]", "lda")
+            self._check_tensor(s, (self.m_per_shard, self.k), "shards", "lda", r)
         self._check_tensor(B, self.b_shape(), "B", "ldb")
         if C is None:
             C = self._new_c(B.device)
@@ -337,11 +363,12 @@ class Plan:
     def gather(self, shards, out=None, stream=None):
         import torch
         for r, s in enumerate(shards):
-            self._check_tensor(s, (self.m_per_shard, self.k), f"shards[{r}]", "lda")
+            self._check_tensor(s, (self.m_per_shard, self.k), "shards", "lda", r)
         if out is None:
             out = torch.empty((self.m, self.k), dtype=_torch_dtype(self.dtype), device=shards[0].device)
         self._check_tensor(out, (self.m, self.k), "gathered")
-        agmm_gather(self.handle, [s.data_ptr() for s in shards], out.data_ptr(), _stream_handle(stream))
+        agmm_gather(self.handle, [s.data_ptr() for s in shards], out.data_ptr(),
+                    _stream_handle(stream, out.device.index))
         return out
 
     def run_gathered(self, gathered, B, C=None, stream=None):
@@ -352,7 +379,7 @@ class Plan:
             C = self._new_c(B.device)
         self._check_tensor(C, (self.m, self.n_local), "C", "ldc")
         agmm_run_gathered(self.handle, gathered.data_ptr(), B.data_ptr(), C.data_ptr(),
-                          _stream_handle(stream))
+                          _stream_handle(stream, B.device.index))
         return C
 
     def tile_order(self, chunk: int = 0):
