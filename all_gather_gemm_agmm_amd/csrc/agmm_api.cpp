@@ -307,6 +307,17 @@ void ring_order(const agmm_plan* p, const Settings& s, int64_t rpg, int64_t row_
   std::stable_sort(out.begin(), out.end(), [&](int32_t a, int32_t b) { return key[a] < key[b]; });
 }
 
+// Output tile (rows x columns) and waves of each skinny kernel shape.
+struct SkinnyDims {
+  int rows, cols, waves;
+};
+constexpr int kSkinnyShapes = 8;
+SkinnyDims skinny_dims(int shape) {
+  static const SkinnyDims d[kSkinnyShapes] = {{64, 16, 4}, {32, 32, 4}, {32, 16, 4}, {16, 32, 4},
+                                              {64, 32, 4}, {32, 32, 8}, {64, 16, 8}, {64, 64, 4}};
+  return d[shape >= 0 && shape < kSkinnyShapes ? shape : 5];
+}
+
 // Derive the launch layout of a plan from its problem and the settings:
 // variant, tiles, chunks, split-K and sizes (not the tile-order tables).
 // Host only; touches nothing of the plan and allocates nothing.
@@ -370,14 +381,19 @@ int derive_launch(const agmm_plan* p, const Settings& s, Layout& L) {
     L.bn = agmm::tile_bn(L.tile_used);
   }
 
-  // whole-k skinny tile shape: 32 x 32 with 8 waves (2-3% faster than 4 on
-  // four skinny shapes) unless 64 x 16 gives more workgroups (small m: m 32,
-  // n 1024, k 4096 measured 10.1 us against 10.9)
+  // skinny tile shape: 32 x 32 with 8 waves (2-3% faster than 4 on four
+  // skinny shapes), its k split to fill the CUs (below); 64 x 64 (4 waves,
+  // k split to fill the CUs) where 32 x 32 tiles would take more than one
+  // round of workgroups and 64 x 64 tiles take at most one.  Measured per
+  // call in graph replay (us): 8x16x14336 -> 4096: 32 x 32 whole k 64.2,
+  // 64 x 64 with 2 splits 41.7; 4x16x8192 -> 1024: whole k 19.0, 4 splits
+  // 11.5; 8x16x4096 -> 512: 8.3, 4 splits 7.6; the skinny workload
+  // 8x16x4096 -> 1792 (224 tiles): whole k 11.5, 64 x 64 with 4 splits 13.3.
   if (s.skinny_shape >= 0) {
     L.skinny_shape_used = s.skinny_shape;
   } else {
-    const int64_t t32 = cdiv(p->m, 32) * cdiv(p->n, 32), t64 = cdiv(p->m, 64) * cdiv(p->n, 16);
-    L.skinny_shape_used = t64 > t32 ? 0 : 5;
+    const int64_t t32 = cdiv(p->m, 32) * cdiv(p->n, 32), t64 = cdiv(p->m, 64) * cdiv(p->n, 64);
+    L.skinny_shape_used = t32 > p->cu_count && t64 <= p->cu_count ? 7 : 5;
   }
 
   // chunking (staged) / split-K
@@ -410,7 +426,15 @@ int derive_launch(const agmm_plan* p, const Settings& s, Layout& L) {
     const int64_t launch_m = v == AGMM_VARIANT_STAGED ? (int64_t)p->N * L.rows_per_chunk : p->m;
     const int64_t tiles = cdiv(launch_m, L.bm) * cdiv(p->n, L.bn);
     int64_t want = s.splits;
-    if (L.tile_used == agmm::kTileSkinny) want = 1;   // whole k per workgroup, no partials
+    int64_t tiles_k = tiles;   // output tiles of one launch, for the automatic split
+    int64_t min_k = v == AGMM_VARIANT_SKINNY ? agmm::kTileBK : 1024;   // shortest automatic k range
+    if (L.tile_used == agmm::kTileSkinny) {
+      // the skinny kernel's waves take a k range's 64-deep k-tiles round
+      // robin: at least one each
+      const SkinnyDims d = skinny_dims(L.skinny_shape_used);
+      tiles_k = cdiv(launch_m, d.rows) * cdiv(p->n, d.cols);
+      min_k = std::max<int64_t>(min_k, (int64_t)d.waves * agmm::kTileBK);
+    }
     if (want <= 0) {
       want = 1;
       // workgroup slots: the CUs times the workgroups of this tile one CU
@@ -421,11 +445,10 @@ int derive_launch(const agmm_plan* p, const Settings& s, Layout& L) {
       const int64_t slots = v == AGMM_VARIANT_SKINNY
                                 ? p->cu_count
                                 : (int64_t)p->cu_count * agmm::tile_occ(L.tile_used);
-      if (v == AGMM_VARIANT_SKINNY || 2 * tiles <= slots) {
+      if (v == AGMM_VARIANT_SKINNY || 2 * tiles_k <= slots) {
         // long enough k ranges that the partial sums stay small next to the
         // operand traffic (skinny problems have no other way to fill the GPU)
-        const int64_t min_k = v == AGMM_VARIANT_SKINNY ? agmm::kTileBK : 1024;
-        while (want * 2 * tiles <= slots && L.kp / (want * 2) >= min_k) want *= 2;
+        while (want * 2 * tiles_k <= slots && L.kp / (want * 2) >= min_k) want *= 2;
       }
     }
     want = std::max<int64_t>(1, std::min<int64_t>(want, cdiv(L.kp, agmm::kTileBK)));
@@ -1143,7 +1166,7 @@ int agmm_plan_set_int(agmm_plan_t p, const char* key, int64_t v) {
     if (v < 0 || v > 1 << 20) return bad();
     s.copy_wgs = (int)v;
   } else if (k == "skinny_shape") {
-    if (v < -1 || v > 6) return bad();
+    if (v < -1 || v >= kSkinnyShapes) return bad();
     s.skinny_shape = (int)v;
   } else if (k == "copy_engine") {
     if (v < 0 || v > 1) return bad();
@@ -1310,24 +1333,32 @@ int agmm_plan_autotune(agmm_plan_t p, const void* const* shard_ptrs, const void*
     }
     const int splits_c[] = {0, 1, 2, 4, 8};
     const int groups_c[] = {4, 8};
-    std::vector<std::array<int, 3>> seen;
+    std::vector<std::array<int, 4>> seen;
     struct Timed {
       double ms;
       Settings s;
     };
     std::vector<Timed> timed;
+    // the skinny tile also over its 32 x 32 and 64 x 64 shapes
+    const int shapes_skinny[] = {5, 7}, shapes_other[] = {-1};
     for (int t : tiles)
+      for (int sh : t == agmm::kTileSkinny ? std::vector<int>(std::begin(shapes_skinny), std::end(shapes_skinny))
+                                           : std::vector<int>(std::begin(shapes_other), std::end(shapes_other)))
       for (int sp : splits_c)
         for (int gm : groups_c) {
           Settings s2 = base;
           s2.tile = t;
           s2.splits = sp;
           s2.group_m = gm;
+          if (sh >= 0) s2.skinny_shape = sh;
           if (mark_done() != AGMM_OK || apply(p, s2) != AGMM_OK) {
             if (p->broken != AGMM_OK) break;
             continue;
           }
-          const std::array<int, 3> key = {p->L.tile_used, p->L.splits_used, p->s.group_m};
+          // the skinny kernel has its own tile order (no group_m)
+          const bool sk = p->L.tile_used == agmm::kTileSkinny;
+          const std::array<int, 4> key = {p->L.tile_used, p->L.splits_used, sk ? -1 : p->s.group_m,
+                                          sk ? p->L.skinny_shape_used : -1};
           if (std::find(seen.begin(), seen.end(), key) != seen.end()) continue;
           seen.push_back(key);
           double ms = 0;

@@ -91,12 +91,19 @@ hipError_t launch_gemm_mfma(const GemmProblem& p, int tile_cfg, int dtype, bool 
                             hipStream_t stream);
 
 // Skinny-m kernel (tile kTileSkinny, B stored n x k): small output tiles
-// (32 x 32 by default), each over the whole of k in one workgroup (no split,
-// one launch; p.splits is ignored).  C rows through the row map.
+// (32 x 32 by default), each over the whole of k in one workgroup (one
+// launch), or with p.splits > 1 over one of p.splits k ranges of
+// p.k_per_split elements (a multiple of 64) into p.partials [splits][m][n]
+// fp32, then launch_splitk_reduce.  C rows through the row map.
 // `shape` selects the tile: 0: 64 x 16, 1: 32 x 32, 2: 32 x 16, 3: 16 x 32,
-// 4: 64 x 32 (rows x columns) with 4 waves; 5: 32 x 32 and 6: 64 x 16 with
-// 8 waves (the LDS shared out over twice as many, half as deep, rings).
+// 4: 64 x 32, 7: 64 x 64 (rows x columns) with 4 waves; 5: 32 x 32 and 6:
+// 64 x 16 with 8 waves (the LDS shared out over twice as many, half as
+// deep, rings).
 hipError_t launch_skinny_fullk(const GemmProblem& p, int dtype, int shape, hipStream_t stream);
+
+// Fixed-order sum of p.partials [p.splits][p.m][p.n] fp32 (split 0 first),
+// cast to the output dtype and stored to C through the row map.
+hipError_t launch_splitk_reduce(const GemmProblem& p, int dtype, hipStream_t stream);
 
 // fp32 inputs, fp64 accumulate, fp32 output (any shape).
 hipError_t launch_gemm_f32(const GemmProblem& p, bool rhs_transpose, hipStream_t stream);

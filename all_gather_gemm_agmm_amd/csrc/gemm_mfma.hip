@@ -1508,4 +1508,16 @@ hipError_t launch_gemm_mfma(const GemmProblem& p, int tile_cfg, int dtype, bool 
   }
 }
 
+hipError_t launch_splitk_reduce(const GemmProblem& p, int dtype, hipStream_t stream) {
+  if (dtype != kDtypeBf16 && dtype != kDtypeFp16) return hipErrorInvalidValue;
+  if (p.splits < 1 || p.partials == nullptr) return hipErrorInvalidValue;
+  const int64_t blocks = ((int64_t)p.m * ((p.n + 3) / 4) + 255) / 256;
+  if (blocks < 1 || blocks > INT32_MAX) return hipErrorInvalidValue;
+  if (dtype == kDtypeBf16)
+    hipLaunchKernelGGL((splitk_reduce_kernel<kDtypeBf16>), dim3((unsigned)blocks), dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL((splitk_reduce_kernel<kDtypeFp16>), dim3((unsigned)blocks), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
 }  // namespace agmm

@@ -1,16 +1,21 @@
-// Skinny-m all-gather matmul on gfx950 without a k split: C[m, n] =
-// concat_r(A_r) @ B^T for small m (a few shards of a few rows, decode-like)
-// with B stored n x k (tpu-inference "all_gather_matmul.py", `_do_mxu` with
-// rhs_transpose: the dot_general contracts dimension 1 of both operands;
-// fp32 accumulation over the k blocks, cast to the input dtype at the end).
+// Skinny-m all-gather matmul on gfx950: C[m, n] = concat_r(A_r) @ B^T for
+// small m (a few shards of a few rows, decode-like) with B stored n x k
+// (tpu-inference "all_gather_matmul.py", `_do_mxu` with rhs_transpose: the
+// dot_general contracts dimension 1 of both operands; fp32 accumulation over
+// the k blocks, cast to the input dtype at the end).
 //
-// At these shapes the work is one pass over B.  The split-K tiles spread B
-// over the CUs by splitting k, which costs fp32 partial sums and a second,
-// reduction launch.  Here every workgroup takes the whole of k for a narrow
-// tile instead (32 x 32 by default), so m = 128, n = 1792 gives 224
-// workgroups, each reading 256 KiB of B and 256 KiB of A (A's 1 MiB is
+// At these shapes the work is one pass over B, and a CU streams its operands
+// at a fixed rate (about 26 bytes per clock here: the L2 reads one CU keeps
+// in flight, over their latency), so the time is set by the bytes one CU
+// reads.  Each workgroup takes a narrow tile (32 x 32 by default) over the
+// whole of k when that gives every CU a workgroup: m = 128, n = 1792 gives
+// 224 workgroups, each reading 256 KiB of B and 256 KiB of A (A's 1 MiB is
 // shared by all workgroups through L2; B comes from HBM once, its column
 // block shared by the 4 row blocks on one XCD).  No partials, one launch.
+// With fewer tiles than CUs, or (64 x 64) to halve the bytes per CU where
+// 32 x 32 tiles would take several rounds, the skinny_splitk_kernel form
+// takes one of several k ranges and writes its fp32 sums; a second launch
+// adds the ranges in a fixed order.
 //
 //  * The waves (4 or 8) take the k-tiles (64 deep) round robin and
 //    accumulate separately; each streams its own k-tiles through a private
@@ -141,9 +146,10 @@ __device__ __forceinline__ void wait_tiles(int after) {
   }
 }
 
-template <int DT, int ROWS, int COLS, int WAVES>
-__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(WAVES / 4, WAVES / 4)))
-void skinny_fullk_kernel(GemmProblem p) {
+// One output tile over one k range: the whole of k, or (SPLIT) k range
+// `split` of p.splits, whose fp32 sums go to p.partials[split][row][col].
+template <int DT, int ROWS, int COLS, int WAVES, bool SPLIT>
+__device__ __forceinline__ void skinny_body(const GemmProblem& p) {
   using S = Shape<ROWS, COLS, WAVES>;
   constexpr int kWaves = S::kWaves, kThreads = 64 * WAVES;
   constexpr int kRows = S::kRows, kCols = S::kCols, kALoads = S::kALoads, kBLoads = S::kBLoads;
@@ -159,17 +165,23 @@ void skinny_fullk_kernel(GemmProblem p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int M = p.m, N = p.n, K = p.k;
   const int RB = (M + kRows - 1) / kRows, CB = (N + kCols - 1) / kCols;
-  // logical tile: XCD x (= workgroup id mod 8) gets a contiguous range, row
-  // blocks fastest, so the row blocks of one column block share an XCD
-  int tile;
+  // logical unit: XCD x (= workgroup id mod 8) gets a contiguous range, row
+  // blocks fastest, so the row blocks of one column block share an XCD;
+  // then column blocks, then k ranges (an XCD's units share few A slices)
+  int tile, split = 0;
   {
-    const int T = RB * CB, wg = blockIdx.x;
+    const int T = RB * CB * (SPLIT ? p.splits : 1), wg = blockIdx.x;
     const int xcd = wg & 7, local = wg >> 3, per = T >> 3, rem = T & 7;
-    tile = xcd * per + (xcd < rem ? xcd : rem) + local;
+    const int u = xcd * per + (xcd < rem ? xcd : rem) + local;
+    tile = u % (RB * CB);
+    if constexpr (SPLIT) split = u / (RB * CB);
   }
   const int rb = tile % RB, cb = tile / RB;
   const int row0 = rb * kRows, n0 = cb * kCols;
-  const int nkt = (K + kKT - 1) / kKT;
+  // k range [kb, kend): multiples of the k-tile except at the end of k
+  const int kb = SPLIT ? split * p.k_per_split : 0;
+  const int kend = SPLIT ? min(K, kb + p.k_per_split) : K;
+  const int nkt = kend > kb ? (kend - kb + kKT - 1) / kKT : 0;
   const int rpg = p.rows.rows_per_group;
   const float inv = 1.0f / (float)rpg;
 
@@ -209,13 +221,13 @@ void skinny_fullk_kernel(GemmProblem p) {
   // this wave's k-tiles: wave, wave + 4, ...
   const int nt = nkt > wave ? (nkt - wave + kWaves - 1) / kWaves : 0;
   auto issue = [&](int j) {   // k-tile number j of this wave into slot j % kSlots
-    const int kk = (wave + kWaves * j) * kKT;
+    const int kk = kb + (wave + kWaves * j) * kKT;
     const uint32_t dst = ring_lds + (j % kSlots) * kSlotBytes;
 #pragma unroll
     for (int q = 0; q < kALoads; ++q) {
       const int r = 8 * q + (lane >> 3);
       const int ke = kk + 8 * ((lane & 7) ^ swz(r));
-      const void* src = (((a_ok >> q) & 1u) && ke < K) ? (const void*)(asrc[q] + (int64_t)kk * 2)
+      const void* src = (((a_ok >> q) & 1u) && ke < kend) ? (const void*)(asrc[q] + (int64_t)kk * 2)
                                                        : (const void*)sk_zero16;
       dma16(src, dst + q * 1024);
     }
@@ -223,7 +235,7 @@ void skinny_fullk_kernel(GemmProblem p) {
     for (int q = 0; q < kBLoads; ++q) {
       const int r = 8 * q + (lane >> 3);
       const int ke = kk + 8 * ((lane & 7) ^ swz(r));
-      const void* src = (((b_ok >> q) & 1u) && ke < K) ? (const void*)(bsrc[q] + (int64_t)kk * 2)
+      const void* src = (((b_ok >> q) & 1u) && ke < kend) ? (const void*)(bsrc[q] + (int64_t)kk * 2)
                                                        : (const void*)sk_zero16;
       dma16(src, dst + (kALoads + q) * 1024);
     }
@@ -263,23 +275,28 @@ void skinny_fullk_kernel(GemmProblem p) {
     // k-tiles issued after j and still allowed in flight
     wait_tiles<kLoads, kSlots - 1>(min(kSlots - 1, nt - 1 - j));
     const char* slot = ring + (j % kSlots) * kSlotBytes;
+    // all of k-tile j's fragments into registers, the slot's refill issued,
+    // then the MFMAs: the ring stays full while they run
+    u32x4_t bf[2][FN], af[2][FM];
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
-      u32x4_t bf[FN];
 #pragma unroll
       for (int f = 0; f < FN; ++f)
-        bf[f] = *reinterpret_cast<const u32x4_t*>(slot + b_off[f] + (((4 * st) ^ b_x[f]) << 4));
+        bf[st][f] = *reinterpret_cast<const u32x4_t*>(slot + b_off[f] + (((4 * st) ^ b_x[f]) << 4));
 #pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        const u32x4_t af = *reinterpret_cast<const u32x4_t*>(slot + a_off[i] + (((4 * st) ^ a_x[i]) << 4));
-#pragma unroll
-        for (int f = 0; f < FN; ++f) acc[i][f] = mfma16<DT>(bf[f], af, acc[i][f]);
-      }
+      for (int i = 0; i < FM; ++i)
+        af[st][i] = *reinterpret_cast<const u32x4_t*>(slot + a_off[i] + (((4 * st) ^ a_x[i]) << 4));
     }
     if (j + kSlots < nt) {
       lds_reads_done();   // k-tile j's fragments are in registers: its slot is free
       issue(j + kSlots);
     }
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int f = 0; f < FN; ++f) acc[i][f] = mfma16<DT>(bf[st][f], af[st][i], acc[i][f]);
   }
   wait_vmcnt<0>();
   lds_reads_done();
@@ -306,6 +323,22 @@ void skinny_fullk_kernel(GemmProblem p) {
     v += *reinterpret_cast<const f32x4_t*>(reinterpret_cast<const float*>(smem + w * kWaveBytes) +
                                            row * RLD + c4);
   const int gr = row0 + row, gc = n0 + c4;
+  if constexpr (SPLIT) {
+    // fp32 sums of this k range, rows in launch order (the reduction maps
+    // them to C)
+    if (gr < M) {
+      float* prow = p.partials + ((int64_t)split * M + gr) * N;
+      if (gc + 3 < N && (N % 4) == 0) {
+        *reinterpret_cast<f32x4_t*>(prow + gc) = v;
+      } else {
+        if (gc + 0 < N) prow[gc + 0] = v[0];
+        if (gc + 1 < N) prow[gc + 1] = v[1];
+        if (gc + 2 < N) prow[gc + 2] = v[2];
+        if (gc + 3 < N) prow[gc + 3] = v[3];
+      }
+    }
+    continue;
+  }
   if (gr < M) {
     int g, t;
     split_row(gr, rpg, inv, g, t);
@@ -324,13 +357,38 @@ void skinny_fullk_kernel(GemmProblem p) {
   }
 }
 
+template <int DT, int ROWS, int COLS, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(WAVES / 4, WAVES / 4)))
+void skinny_fullk_kernel(GemmProblem p) {
+  skinny_body<DT, ROWS, COLS, WAVES, false>(p);
+}
+
+template <int DT, int ROWS, int COLS, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(WAVES / 4, WAVES / 4)))
+void skinny_splitk_kernel(GemmProblem p) {
+  skinny_body<DT, ROWS, COLS, WAVES, true>(p);
+}
+
 }  // namespace
 
 template <int ROWS, int COLS, int WAVES = 4>
 hipError_t launch_shape(const GemmProblem& p, int dtype, hipStream_t stream) {
   const int64_t tiles = (int64_t)((p.m + ROWS - 1) / ROWS) * ((p.n + COLS - 1) / COLS);
-  if (tiles > (int64_t(1) << 30)) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)tiles), block(64 * WAVES);
+  const bool split = p.splits > 1;
+  if (tiles * (split ? p.splits : 1) > (int64_t(1) << 30)) return hipErrorInvalidValue;
+  if (split && (p.partials == nullptr || p.k_per_split < kKT || p.k_per_split % kKT != 0 ||
+                (int64_t)p.splits * p.k_per_split < p.k))
+    return hipErrorInvalidValue;
+  const dim3 grid((unsigned)(tiles * (split ? p.splits : 1))), block(64 * WAVES);
+  if (split) {
+    if (dtype == kDtypeBf16)
+      hipLaunchKernelGGL((skinny_splitk_kernel<kDtypeBf16, ROWS, COLS, WAVES>), grid, block, 0, stream, p);
+    else
+      hipLaunchKernelGGL((skinny_splitk_kernel<kDtypeFp16, ROWS, COLS, WAVES>), grid, block, 0, stream, p);
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    return launch_splitk_reduce(p, dtype, stream);
+  }
   if (dtype == kDtypeBf16)
     hipLaunchKernelGGL((skinny_fullk_kernel<kDtypeBf16, ROWS, COLS, WAVES>), grid, block, 0, stream, p);
   else
@@ -351,6 +409,7 @@ hipError_t launch_skinny_fullk(const GemmProblem& p, int dtype, int shape, hipSt
     case 4: return launch_shape<64, 32>(p, dtype, stream);
     case 5: return launch_shape<32, 32, 8>(p, dtype, stream);
     case 6: return launch_shape<64, 16, 8>(p, dtype, stream);
+    case 7: return launch_shape<64, 64>(p, dtype, stream);
     default: return hipErrorInvalidValue;
   }
 }

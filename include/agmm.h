@@ -232,9 +232,10 @@ int agmm_plan_autotune(agmm_plan_t plan, const void *const *shard_ptrs, const vo
  *                   (rhs_transpose only) with 64-deep k-tiles in a 5-slot
  *                   operand ring, 8 256x256 and 9 128x128 in the same ring on
  *                   16x16x32 MFMAs (the automatic choices for k >= 256),
- *                   10 the whole-k skinny kernel (rhs_transpose only; tile
- *                   from "skinny_shape"; no k split; the automatic skinny
- *                   choice for m <= 128; 7 for 128 < m <= 256), 11 256x224
+ *                   10 the skinny kernel (rhs_transpose only; tile from
+ *                   "skinny_shape"; whole k per workgroup, or k ranges as
+ *                   "splits" says; the automatic skinny choice for
+ *                   m <= 128; 7 for 128 < m <= 256), 11 256x224
  *                   in the 16x16x32 ring (rhs_transpose only; automatic where
  *                   its 224-column tiles fill whole rounds of workgroups that
  *                   256x256 tiles would leave partly idle).  A tile that
@@ -244,9 +245,10 @@ int agmm_plan_autotune(agmm_plan_t plan, const void *const *shard_ptrs, const vo
  *   "splits"        0: automatic, else k-splits (fp32 partial sums, then a
  *                   fixed-order reduction) of every bf16/fp16 launch (for the
  *                   staged variant: of each chunk's launch); automatic splits
- *                   are used by the split-K skinny tiles and by launches
- *                   whose output tiles fill at most half of the workgroup
- *                   slots; tile 10 ignores it
+ *                   are used by the skinny tiles (as many k ranges as
+ *                   fill the CUs, each at least 64 elements per wave of
+ *                   tile 10) and by launches whose output tiles fill at
+ *                   most half of the workgroup slots
  *   "local_shard"   0 .. num_shards-1: where the ring order starts
  *   "order"         0: ring order from local_shard, 1: natural order
  *   "group_m"       row blocks walked together (L2 reuse); 0 (default):
@@ -256,10 +258,11 @@ int agmm_plan_autotune(agmm_plan_t plan, const void *const *shard_ptrs, const vo
  *   "copy_wgs"      >= 0: workgroups of each staged chunk copy (0 = auto:
  *                   sized to the whole GPU) and of the side gather of
  *                   agmm_run_gather_out (0 = one per CU)
- *   "skinny_shape"  -1 (automatic: 5, or 0 when 64 x 16 gives more
- *                   workgroups than 32 x 32) or 0..6: output tile of the
- *                   whole-k skinny kernel (tile 10), rows x columns: 0 64 x 16,
- *                   1 32 x 32, 2 32 x 16, 3 16 x 32, 4 64 x 32 (4 waves);
+ *   "skinny_shape"  -1 (automatic: 5, or 7 where 32 x 32 tiles would
+ *                   need more than one workgroup per CU and 64 x 64 tiles
+ *                   would not) or 0..7: output tile of the skinny kernel
+ *                   (tile 10), rows x columns: 0 64 x 16, 1 32 x 32,
+ *                   2 32 x 16, 3 16 x 32, 4 64 x 32, 7 64 x 64 (4 waves);
  *                   5 32 x 32, 6 64 x 16 (8 waves).  Reads back the shape in
  *                   use.
  *   "copy_engine"   0 (default) or 1: what performs the copies that run

@@ -106,20 +106,25 @@ SKINNY_FULLK = [
     (1, 7, 72, 33, BF16, {}),           # a single short k-tile: waves 2, 3 have none
     (8, 16, 4096, 1792, BF16, {}),      # the decode-like workload's shape
     (9, 30, 640, 130, FP16, {}),        # 9 shards, row blocks across shard boundaries
-    (2, 100, 3000, 520, BF16, {"splits": 4}),   # splits ignored: whole k per workgroup
+    (2, 100, 3000, 520, BF16, {"splits": 4}),   # 4 k ranges of 768 (the last 696)
     (3, 40, 264, 100, BF16, {"lda": 272, "ldb": 280, "ldc": 103}),
     (5, 13, 8, 16, BF16, {}),           # k = 8: one chunk of one k-tile
 ]
 
 
-@pytest.mark.parametrize("shape", [0, 1, 2, 3, 4, 5, 6])
+@pytest.mark.parametrize("split_mode", ["whole_k", "auto"])
+@pytest.mark.parametrize("shape", [0, 1, 2, 3, 4, 5, 6, 7])
 @pytest.mark.parametrize("case", SKINNY_FULLK, ids=lambda c: f"{c[0]}x{c[1]}x{c[2]}x{c[3]}-d{c[4]}-{len(c[5])}")
-def test_skinny_fullk_tile(case, shape):
-    """The whole-k skinny tile (tiles over the whole of k, wave-private LDS rings), every
-    tile shape (64x16, 32x32, 32x16, 16x32, 64x32), against the oracle on
-    ragged m, n and k, strided operands; C's row padding untouched; a second
-    run bit-identical."""
+def test_skinny_fullk_tile(case, shape, split_mode):
+    """The skinny tile (wave-private LDS rings), every tile shape (64x16,
+    32x32, 32x16, 16x32, 64x32, 64x64), over the whole of k and with the
+    automatic k split (fp32 partial sums of each k range, then the
+    fixed-order reduction), against the oracle on ragged m, n and k, strided
+    operands; C's row padding untouched; a second run bit-identical."""
     N, m_s, k, n, dtype, extra = case
+    extra = dict(extra)
+    if split_mode == "whole_k":
+        extra.setdefault("splits", 1)
     w, shards, B = make_case(N, m_s, k, n, dtype, True, seed=2200 + N + m_s + k + n)
     lda, ldb, ldc = extra.get("lda", k), extra.get("ldb", k), extra.get("ldc", n)
     dt = torch_dtype(dtype)
@@ -133,7 +138,9 @@ def test_skinny_fullk_tile(case, shape):
     C = torch.full((N * m_s, ldc), float("nan"), dtype=dt, device="cuda")
     plan = agmm.Plan(N, m_s, k, n, dtype, True, variant="skinny", tile=agmm.TILE_SKINNY, skinny_shape=shape, **extra)
     try:
-        assert plan.get("tile") == agmm.TILE_SKINNY and plan.get("splits") == 1 and plan.get("skinny_shape") == shape
+        assert plan.get("tile") == agmm.TILE_SKINNY and plan.get("skinny_shape") == shape
+        if "splits" in extra:
+            assert plan.get("splits") == min(extra["splits"], -(-k // 64))
         plan.run(sd, bfull[:, :k], C[:, :n])
         torch.cuda.synchronize()
         first = to_bits(C[:, :n])
@@ -147,17 +154,50 @@ def test_skinny_fullk_tile(case, shape):
         plan.close()
 
 
-@pytest.mark.parametrize("shape,tile,skinny_shape", [
-    ((8, 16, 4096, 1792), 10, 5), ((2, 16, 4096, 1024), 10, 0), ((16, 16, 4096, 1792), 7, None)])
-def test_skinny_automatic_choice(shape, tile, skinny_shape):
-    """The skinny variant's automatic tile: the whole-k kernel for m <= 128
-    (64 x 16 when that gives more workgroups than 32 x 32), the split-K
-    128x64 part ring for 128 < m <= 256."""
+@pytest.mark.parametrize("shape,tile,skinny_shape,splits", [
+    ((8, 16, 4096, 1792), 10, 5, 1),       # 224 tiles of 32 x 32: whole k
+    ((2, 16, 4096, 1024), 10, 5, 8),       # 32 tiles: 8 k ranges of 512
+    ((4, 16, 8192, 1024), 10, 5, 4),       # 64 tiles: 4 k ranges
+    ((2, 16, 4096, 256), 10, 5, 8),        # 8 tiles: k ranges of at least one k-tile per wave
+    ((8, 16, 14336, 4096), 10, 7, 2),      # 512 tiles of 32 x 32, 128 of 64 x 64: 2 k ranges
+    ((8, 16, 8192, 8192), 10, 7, 1),       # 256 tiles of 64 x 64: whole k
+    ((16, 16, 4096, 1792), 7, None, None)])
+def test_skinny_automatic_choice(shape, tile, skinny_shape, splits):
+    """The skinny variant's automatic tile: for m <= 128 the skinny kernel,
+    32 x 32 with k split into as many ranges as fill the CUs (each at least
+    one 64-deep k-tile per wave), or 64 x 64 where 32 x 32 tiles would take
+    more than one round of workgroups; the split-K 128x64 part ring for
+    128 < m <= 256."""
     plan = agmm.Plan(*shape, BF16, True, variant="skinny")
     try:
         assert plan.get("tile") == tile
         if skinny_shape is not None:
             assert plan.get("skinny_shape") == skinny_shape
+        if splits is not None:
+            assert plan.get("splits") == splits
+    finally:
+        plan.close()
+
+
+@pytest.mark.parametrize("dims,dtype", [((8, 16, 14336, 4096), BF16), ((4, 16, 8192, 1024), FP16)])
+def test_skinny_split_large_against_oracle(dims, dtype):
+    """Decode-like shapes on which the automatic skinny choice splits k
+    (64 x 64 tiles with 2 k ranges; 32 x 32 with 4), checked in full against
+    the oracle, and the second run bit-identical."""
+    w, shards, B = make_case(*dims, dtype, True, seed=2400 + dims[2])
+    sd = [to_device(x, dtype) for x in shards]
+    bd = to_device(B, dtype)
+    plan = agmm.Plan(*dims, dtype, True)
+    try:
+        assert plan.get("tile") == agmm.TILE_SKINNY and plan.get("splits") > 1
+        C = torch.full((w.m, dims[3]), float("nan"), dtype=torch_dtype(dtype), device="cuda")
+        plan.run(sd, bd, C)
+        torch.cuda.synchronize()
+        first = to_bits(C)
+        check_against_oracle(w, shards, B, C)
+        plan.run(sd, bd, C)
+        torch.cuda.synchronize()
+        assert np.array_equal(first, to_bits(C))
     finally:
         plan.close()
 

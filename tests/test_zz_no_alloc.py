@@ -24,6 +24,7 @@ BF16, FP16 = I.DTYPE_BF16, I.DTYPE_FP16
 CASES = [
     (4, 48, 4096, 1024, BF16, True),   # m 192: the split-K 128x64 skinny tile, 8 k ranges
     (2, 64, 2048, 256, FP16, False),   # m 128, B k x n: the 128x128 tile, 16 k ranges
+    (4, 16, 8192, 1024, BF16, True),   # m 64: the skinny 32x32 tile, 4 k ranges
 ]
 
 
