@@ -801,6 +801,7 @@ def test_repeated_runs_fresh_inputs():
 
 @pytest.mark.parametrize("variant,settings", [
     ("fused", {}), ("skinny", {}), ("unfused", {}), ("fused", {"splits": 3}),
+    ("skinny", {"splits": 3}),                                   # the skinny kernel's k ranges + reduction
     ("staged", {"pvalue": 1, "tile": 1, "nbuf": 2}),
     ("staged", {"pvalue": 1, "tile": 6, "nbuf": 2, "splits": 2})])
 def test_graph_capture_replays(variant, settings):
@@ -1258,7 +1259,8 @@ def _spin_cycles_per_ms():
 @pytest.mark.parametrize("variant,settings", [
     ("staged", {"pvalue": 1, "nbuf": 2, "tile": 6}),            # 4 chunks through 2 slots
     ("fused", {"tile": 1, "splits": 3}),                         # split-K partials
-    ("skinny", {"tile": 7, "splits": 4})])
+    ("skinny", {"tile": 7, "splits": 4}),
+    ("skinny", {"tile": 10, "splits": 4})])                      # the skinny kernel's k ranges
 def test_serial_calls_on_two_streams_are_ordered(variant, settings):
     """Call 1 on stream s1 (queued behind a ~150 ms spin kernel), then at once
     call 2 with other inputs on stream s2, no host synchronisation between
