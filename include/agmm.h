@@ -82,10 +82,12 @@ typedef enum {
   AGMM_VARIANT_UNFUSED = 3, /* gather all of A, then one GEMM, one stream (the
                                decomposed approach the tutorial compares to) */
   AGMM_VARIANT_SKINNY = 4   /* small m, from the shard buffers: with B
-                               stored n x k and m <= 128 a kernel that takes
-                               all of k per workgroup (no k split, one
-                               launch); otherwise split-K with a fixed-order
-                               reduction launch (tpu-inference `grid_k`) */
+                               stored n x k and m <= 128 a kernel of narrow
+                               tiles over all of k (one launch) where those
+                               tiles give every CU a workgroup, over k ranges
+                               otherwise; other shapes split-K GEMM tiles;
+                               k ranges are added by a fixed-order reduction
+                               launch (tpu-inference `grid_k`) */
 } agmm_variant;
 
 /*
@@ -93,7 +95,9 @@ typedef enum {
  * Returns AGMM_OK if agmm_plan_create would accept it, otherwise the status
  * it would fail with (and sets agmm_last_error()).
  *   num_shards    1 .. 64
- *   m_per_shard, k, n_local >= 1, with m*k, k*n_local, m*n_local < 2^31
+ *   m_per_shard, k, n_local >= 1, with m = num_shards * m_per_shard, k and
+ *                 n_local < 2^30 and m*k, k*n_local, m*n_local < 2^40
+ *                 (else AGMM_ERR_UNSUPPORTED)
  *   dtype         agmm_dtype
  *   rhs_transpose 0: B is [k, n_local]; 1: B is [n_local, k]
  * Any k and n_local are accepted.  bf16/fp16 rows that are not whole

@@ -56,6 +56,27 @@ def test_validate_rejects(args, status, fragment):
     assert fragment in agmm.agmm_last_error()
 
 
+@pytest.mark.parametrize("args,ok", [
+    ((64, 1, 8, 8), True),                        # the most shards
+    ((1, (1 << 30) - 1, 1, 1), True),             # m just below 2^30
+    ((2, 1 << 29, 1, 1), False),                  # m = 2^30
+    ((1, 1, (1 << 30) - 1, 1), True),             # k just below 2^30
+    ((1, 1, 1, 1 << 30), False),                  # n = 2^30
+    ((1, 1 << 20, (1 << 20) - 1, 8), True),       # m*k just below 2^40
+    ((1, 1 << 20, 1 << 20, 8), False),            # m*k = 2^40
+    ((4, 1 << 18, 8, 1 << 20), False),            # m*n = 2^40
+    ((1, 8, 1 << 20, (1 << 20) - 1), True),       # k*n just below 2^40
+])
+def test_validate_size_limits(args, ok):
+    """m, k and n_local below 2^30 and their products below 2^40, exactly at
+    the boundaries."""
+    st = agmm.load_library().agmm_plan_validate(*args, 0, 0)
+    if ok:
+        assert st == agmm.AGMM_OK, agmm.agmm_last_error()
+    else:
+        assert st == agmm.AGMM_ERR_UNSUPPORTED and "too large" in agmm.agmm_last_error()
+
+
 def test_validate_accepts_ragged_and_odd_shapes():
     assert agmm.agmm_plan_validate(3, 100, 200, 136, 0, 0) == agmm.AGMM_OK
     assert agmm.agmm_plan_validate(3, 100, 200, 130, 1, 1) == agmm.AGMM_OK  # n free with B^T
