@@ -117,7 +117,7 @@ struct Settings {
   int group_m = 0;        // 0: chosen per launch shape (pick_group_m)
   int xcd_remap = 1;
   int copy_wgs = 0;
-  int skinny_shape = -1;  // tile shape of the whole-k skinny kernel; -1 automatic
+  int skinny_shape = -1;  // tile shape of the skinny kernel; -1 automatic
   int copy_engine = 0;    // copies beside a GEMM: 0 gather kernel (CUs), 1 SDMA engines
   int gather_out = 0;     // agmm_run_gather_out on fused/skinny plans: 0 automatic, 1 side copy, 2 sequential
   int64_t lda = 0, ldb = 0, ldc = 0;   // element strides between rows (0: dense)
@@ -359,10 +359,11 @@ int derive_launch(const agmm_plan* p, const Settings& s, Layout& L) {
     L.bm = L.bn = 64;
   } else {
     if (v == AGMM_VARIANT_SKINNY) {
-      // B stored n x k, m <= 128: the whole-k skinny kernel (one launch, no
-      // partial sums).  Measured per call in graph replay (us, whole-k against
-      // the best split-K tile): m 128, n 1792, k 4096: 11.8 / 16.4; m 128,
-      // n 512: 8.6 / 14.4; m 64, n 3584, k 8192: 21.6 / 32.3.  For m 256 the
+      // B stored n x k, m <= 128: the skinny kernel (its tile shape and k
+      // ranges below).  Measured per call in graph replay (us, skinny kernel
+      // over whole k against the best split-K GEMM tile): m 128, n 1792,
+      // k 4096: 11.8 / 16.4; m 128, n 512: 8.6 / 14.4; m 64, n 3584, k 8192:
+      // 21.6 / 32.3.  For m 256 the
       // split-K 128x64 part ring was fastest (19.7 against 20.7 whole-k and
       // 24.8 for the 256x128 tile).  Split-K tiles put all of m in one row
       // block and split k over narrow column blocks, so that enough

@@ -91,7 +91,7 @@ def test_tiles_ragged(tile, dtype, rt, k):
     ragged last k-tile, k = 384 is whole 64-deep k-tiles, so interior tiles
     take the unmasked load path."""
     if tile in agmm.TILES_NEED_BT and not rt:
-        pytest.skip("the 128x64 and skinny whole-k tiles take B stored n x k only")
+        pytest.skip("the 128x64 and skinny tiles take B stored n x k only")
     w, shards, B = make_case(3, 200, k, 392, dtype, rt, seed=900 + tile + k)
     shards_d = [to_device(s, dtype) for s in shards]
     B_d = to_device(B, dtype)
@@ -99,7 +99,7 @@ def test_tiles_ragged(tile, dtype, rt, k):
     check_against_oracle(w, shards, B, C)
 
 
-# ------------------------------------------------- skinny kernel, whole k
+# ------------------------------------------- skinny kernel, whole k or k ranges
 SKINNY_FULLK = [
     # N, m_s, k, n, dtype, extra plan settings
     (3, 50, 1000, 200, FP16, {}),       # 3 row blocks of 64 (the last ragged), ragged k-tile, ragged n
@@ -228,7 +228,7 @@ def test_skinny_fullk_needs_transposed_b():
 
 
 def test_skinny_fullk_in_staged_chunks():
-    """The whole-k skinny tile under the staged variant: chunk launches map their rows to C
+    """The skinny tile under the staged variant: chunk launches map their rows to C
     through the chunk's row offset."""
     w, shards, B = make_case(3, 200, 384, 130, BF16, True, seed=2300)
     C, _ = run_variant(w, [to_device(x, BF16) for x in shards], to_device(B, BF16), "staged",
@@ -1169,7 +1169,7 @@ def test_run_rejects_misaligned_pointer():
 
 
 def test_set_int_rejection_keeps_the_plan():
-    """A rejected setting (the whole-k skinny tile on a plan whose B is
+    """A rejected setting (the skinny tile on a plan whose B is
     stored k x n) leaves every setting as it was: the plan still runs with
     its previous tile and computes the oracle's values."""
     w, shards, B = make_case(2, 16, 64, 64, BF16, False, seed=84)
