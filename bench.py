@@ -69,7 +69,7 @@ def parse():
                     help="other workloads measured into the `workloads` field ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-compare", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--eager", action="store_true",
                     help="time the K steps as K eager calls even when they are launch-bound")
     ap.add_argument("--only-run", action="store_true",
@@ -593,7 +593,7 @@ def cpu_baseline(args, w, shards_np, B_np, I, np):
     import oracle
     threads = oracle.num_threads()
     # bounded sample: whole output rows (all n_local columns, full k), grown
-    # until about --cpu-seconds / 4 of oracle work
+    # until one run of the oracle over them takes about --cpu-seconds
     rows, nrows, t_cpu = [0], 1, 0.0
     while True:
         sel = [int(r) for r in np.linspace(0, w.m - 1, nrows)]
@@ -601,9 +601,9 @@ def cpu_baseline(args, w, shards_np, B_np, I, np):
         oracle.agmm_f64(shards_np, B_np, w.dtype, w.rhs_transpose, rows=sel)
         t_cpu = time.perf_counter() - t1
         rows = sel
-        if t_cpu > args.cpu_seconds / 4 or nrows >= w.m:
+        if t_cpu >= 0.8 * args.cpu_seconds or nrows >= w.m:
             break
-        nrows = min(w.m, max(nrows * 2, int(nrows * (args.cpu_seconds / 4) / max(t_cpu, 1e-3))))
+        nrows = min(w.m, max(nrows * 2, int(nrows * args.cpu_seconds / max(t_cpu, 1e-3))))
     cpu_flops = 2.0 * len(rows) * w.k * w.n_local
     out = {"value": round(cpu_flops / t_cpu / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
            "kind": "oracle", "cpu_model": cpu_model(),
