@@ -353,6 +353,29 @@ def test_gather_bit_exact(dtype):
     assert np.array_equal(to_bits(G), oracle.gather(shards, dtype))
 
 
+@pytest.mark.parametrize("variant,dtype,rt,m_s,settings", [
+    ("fused", BF16, False, 5, {}), ("fused", FP16, True, 9, {"tile": 11}),
+    ("staged", BF16, True, 7, {"pvalue": 1, "nbuf": 2}), ("unfused", FP16, False, 3, {}),
+    ("skinny", BF16, True, 2, {}), ("skinny", BF16, True, 1, {"splits": 3}),
+    ("skinny", FP16, True, 4, {"skinny_shape": 7, "splits": 2}), ("fused", FP32, False, 3, {})])
+def test_most_shards(variant, dtype, rt, m_s, settings):
+    """64 shards, the largest pointer table a call can pass: every variant
+    (with the skinny kernel over whole k and over k ranges) against the
+    oracle, and the gather of all 64 bit-exact."""
+    N, k, n = 64, 328, 136
+    w, shards, B = make_case(N, m_s, k, n, dtype, rt, seed=3100 + m_s)
+    sd = [to_device(x, dtype) for x in shards]
+    C, _ = run_variant(w, sd, to_device(B, dtype), variant, **settings)
+    check_against_oracle(w, shards, B, C)
+    plan = agmm.Plan(N, m_s, k, n, dtype, rt)
+    try:
+        G = plan.gather(sd)
+        torch.cuda.synchronize()
+    finally:
+        plan.close()
+    assert np.array_equal(to_bits(G), oracle.gather(shards, dtype))
+
+
 @pytest.mark.parametrize("dtype,k,lda", [
     (BF16, 8, 0), (BF16, 56, 0), (BF16, 264, 0), (BF16, 2040, 0), (BF16, 2048, 0),
     (BF16, 2056, 0), (FP16, 8000, 0), (FP32, 4, 0), (FP32, 1028, 0), (BF16, 264, 280)])
