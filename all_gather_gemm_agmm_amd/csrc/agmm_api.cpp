@@ -331,15 +331,17 @@ int derive_launch(const agmm_plan* p, const Settings& s, Layout& L) {
     else v = AGMM_VARIANT_FUSED;
   }
   if (is_f32(p) && v == AGMM_VARIANT_SKINNY) v = AGMM_VARIANT_FUSED;
-  L.padded = needs_pad(p->dtype, p->k, p->n, p->rt);
-  L.kp = L.padded ? round8(p->k) : p->k;
-  L.np = L.padded && !p->rt ? round8(p->n) : p->n;
+  // fp32 rows that are not whole 16-byte vectors: the fp32 GEMM reads any
+  // row length, but the gathering variants copy rows with 16-byte vectors,
+  // so they gather zero-padded rows (k rounded up to 4) instead
+  const bool f32_pad = is_f32(p) && (v == AGMM_VARIANT_STAGED || v == AGMM_VARIANT_UNFUSED) &&
+                       (p->k * e) % 16 != 0;
+  L.padded = needs_pad(p->dtype, p->k, p->n, p->rt) || f32_pad;
+  L.kp = !L.padded ? p->k : is_f32(p) ? (p->k + 3) / 4 * 4 : round8(p->k);
+  L.np = L.padded && !p->rt && !is_f32(p) ? round8(p->n) : p->n;
   // padded operands are gathered (with the zero fill) into the ring first:
   // every requested variant runs as gather-then-GEMM
   if (L.padded) v = AGMM_VARIANT_UNFUSED;
-  if ((v == AGMM_VARIANT_STAGED || v == AGMM_VARIANT_UNFUSED) && !L.padded && (p->k * e) % 16 != 0)
-    return set_err(AGMM_ERR_UNSUPPORTED,
-                   "the gather copy needs 16-byte rows (k * elem_bytes %% 16 == 0)");
   L.variant_used = v;
 
   // B stored k x n: transposed once per call into the workspace when the

@@ -105,8 +105,9 @@ typedef enum {
  * computed on zero-padded copies of A ([m][k rounded up to 8]) and B that the
  * plan keeps in its workspace, the way the Ascend tutorial's kernel masks its
  * K and N tails: every requested variant then runs as gather-then-GEMM.  The
- * staged and unfused variants of fp32 plans need k % 4 == 0 (16-byte rows
- * for the gather copy).  (The tpu-inference page's own `validate_inputs`
+ * staged and unfused variants of fp32 plans with k % 4 != 0 run the same way
+ * (on rows zero-padded to a multiple of 4; the fused fp32 path reads any
+ * row length).  (The tpu-inference page's own `validate_inputs`
  * rules - 2-D inputs, equal dtypes, matching k - are implied by this
  * signature; its TPU tiling rules are not imposed.)
  */
