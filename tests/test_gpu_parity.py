@@ -817,6 +817,8 @@ def _random_cases(count, seed):
             settings["tile"] = int(rng.choice(tiles))
             if variant in ("fused", "unfused", "skinny", "staged") and rng.random() < 0.5:
                 settings["splits"] = int(rng.integers(1, 6))
+            if settings["tile"] == agmm.TILE_SKINNY:
+                settings["skinny_shape"] = int(rng.integers(0, 8))
         if variant == "staged":
             settings["pvalue"] = int(rng.integers(1, 3))
             settings["nbuf"] = int(rng.integers(1, 4))
@@ -826,7 +828,7 @@ def _random_cases(count, seed):
     return cases
 
 
-@pytest.mark.parametrize("case", _random_cases(48, 2024), ids=lambda c: f"{c[0]}x{c[1]}x{c[2]}x{c[3]}-d{c[4]}-t{int(c[5])}-{c[6]}")
+@pytest.mark.parametrize("case", _random_cases(96, 2024), ids=lambda c: f"{c[0]}x{c[1]}x{c[2]}x{c[3]}-d{c[4]}-t{int(c[5])}-{c[6]}")
 def test_random_problems(case):
     """Randomized cross-check of every variant, tile and split setting against
     the oracle on small ragged problems (fixed seed, so failures reproduce)."""
