@@ -404,3 +404,48 @@ class Plan:
 
     def __exit__(self, *exc):
         self.close()
+
+
+# ------------------------------------------------ one call, cached plans
+_PLAN_CACHE: dict = {}
+_PLAN_CACHE_LOCK = None
+
+
+def all_gather_matmul(shards, B, rhs_transpose: bool = False, C=None, stream=None):
+    """C = concat_r(shards[r]) @ B, or @ B^T with rhs_transpose (B stored
+    [n_local, k]): the tpu-inference page's `all_gather_matmul` on one GPU,
+    with the shards as separate tensors.  The first call for a problem
+    shape, dtype and device creates a plan with the automatic settings and
+    keeps it (its workspace stays allocated until clear_plan_cache()); later
+    calls reuse it.  Returns C [num_shards * m_per_shard, n_local]."""
+    import threading
+    global _PLAN_CACHE_LOCK
+    if _PLAN_CACHE_LOCK is None:
+        _PLAN_CACHE_LOCK = threading.Lock()
+    if len(shards) == 0:
+        raise ValueError("all_gather_matmul needs at least one shard")
+    m_s, k = shards[0].shape
+    n = B.shape[0] if rhs_transpose else B.shape[1]
+    dtype = {"torch.bfloat16": AGMM_BF16, "torch.float16": AGMM_FP16,
+             "torch.float32": AGMM_FP32}.get(str(B.dtype))
+    if dtype is None:
+        raise ValueError(f"unsupported dtype {B.dtype}")
+    key = (len(shards), int(m_s), int(k), int(n), dtype, bool(rhs_transpose), B.device.index)
+    with _PLAN_CACHE_LOCK:
+        plan = _PLAN_CACHE.get(key)
+        if plan is None:
+            plan = Plan(len(shards), int(m_s), int(k), int(n), dtype, bool(rhs_transpose))
+            _PLAN_CACHE[key] = plan
+    return plan.run(shards, B, C, stream=stream)
+
+
+def clear_plan_cache() -> None:
+    """Destroy the plans all_gather_matmul keeps (after the work queued on
+    them has finished: destroying a plan waits for it)."""
+    if _PLAN_CACHE_LOCK is None:
+        return
+    with _PLAN_CACHE_LOCK:
+        plans = list(_PLAN_CACHE.values())
+        _PLAN_CACHE.clear()
+    for p in plans:
+        p.close()

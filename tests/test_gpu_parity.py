@@ -1077,6 +1077,32 @@ def test_b_transposed_copy_automatic_choice():
         nk.close()
 
 
+@pytest.mark.parametrize("dtype,rt", [(BF16, False), (FP16, True), (FP32, False)])
+def test_all_gather_matmul_one_call(dtype, rt):
+    """The one-call form: the same bits as a plan's run, the plan created
+    once and reused for the same problem, a new one for another shape."""
+    w, shards, B = make_case(3, 40, 264, 136, dtype, rt, seed=3500 + dtype)
+    sd = [to_device(x, dtype) for x in shards]
+    bd = to_device(B, dtype)
+    agmm.clear_plan_cache()
+    try:
+        C1 = agmm.all_gather_matmul(sd, bd, rhs_transpose=rt)
+        C2 = agmm.all_gather_matmul(sd, bd, rhs_transpose=rt)
+        torch.cuda.synchronize()
+        assert len(agmm._PLAN_CACHE) == 1
+        with agmm.Plan(3, 40, 264, 136, dtype, rt) as plan:
+            C_ref = plan.run(sd, bd)
+            torch.cuda.synchronize()
+        assert np.array_equal(to_bits(C1), to_bits(C_ref)) and np.array_equal(to_bits(C2), to_bits(C_ref))
+        check_against_oracle(w, shards, B, C1)
+        agmm.all_gather_matmul(sd[:2], bd, rhs_transpose=rt)
+        torch.cuda.synchronize()
+        assert len(agmm._PLAN_CACHE) == 2
+    finally:
+        agmm.clear_plan_cache()
+    assert len(agmm._PLAN_CACHE) == 0
+
+
 def test_run_gathered_matches_fused():
     w, shards, B = make_case(2, 256, 512, 256, FP16, True, seed=82)
     sd = [to_device(s, FP16) for s in shards]
