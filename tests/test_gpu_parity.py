@@ -1077,6 +1077,41 @@ def test_b_transposed_copy_automatic_choice():
         nk.close()
 
 
+SPECIAL_BITS = {BF16: (0x7F80, 0xFF80, 0x7FC0), FP16: (0x7C00, 0xFC00, 0x7E00),
+                FP32: (0x7F800000, 0xFF800000, 0x7FC00000)}   # +inf, -inf, NaN
+
+
+@pytest.mark.parametrize("variant,dtype,rt,k,settings", [
+    ("fused", BF16, False, 384, {}), ("fused", FP16, True, 384, {"splits": 3}),
+    ("staged", BF16, True, 384, {"pvalue": 1}), ("unfused", FP16, False, 384, {}),
+    ("skinny", BF16, True, 384, {}), ("skinny", FP16, True, 1024, {"splits": 4}),
+    ("fused", BF16, False, 13, {}), ("fused", FP32, False, 200, {})])
+def test_special_values_propagate(variant, dtype, rt, k, settings):
+    """IEEE specials in A (+inf, -inf, both in one row, NaN) give the
+    oracle's specials in C: an output is NaN, +inf or -inf exactly where
+    the fp64 oracle's is, whatever the summation order; every other output
+    is within the usual bound."""
+    N, m_s, n = 3, 40, 136
+    w, shards, B = make_case(N, m_s, k, n, dtype, rt, seed=3700 + k + dtype)
+    pinf, ninf, nan = SPECIAL_BITS[dtype]
+    shards = [s.copy() for s in shards]
+    shards[0][1, 3] = pinf          # row 1: +-inf by the sign of B's row 3
+    shards[0][5, 2] = ninf          # row 5: -+inf
+    shards[1][7, 0] = pinf          # row m_s + 7: +inf and -inf: NaN where both terms meet
+    shards[1][7, k - 1] = ninf
+    shards[2][9, k // 2] = nan      # row 2 m_s + 9: all NaN
+    sd = [to_device(x, dtype) for x in shards]
+    C, _ = run_variant(w, sd, to_device(B, dtype), variant, **settings)
+    ref = oracle.agmm_f64(shards, B, dtype, rt)
+    got = oracle.decode(to_bits(C), dtype)
+    for cls in (np.isnan, np.isposinf, np.isneginf):
+        assert np.array_equal(cls(got), cls(ref)), f"{cls.__name__} positions differ"
+    assert np.isnan(ref).any() and np.isposinf(ref).any() and np.isneginf(ref).any()
+    fin = np.isfinite(ref)
+    err = rel_err(got[fin], ref[fin])
+    assert err <= BOUND[dtype], f"max rel err {err:.3e}"
+
+
 @pytest.mark.parametrize("dtype,rt", [(BF16, False), (FP16, True), (FP32, False)])
 def test_all_gather_matmul_one_call(dtype, rt):
     """The one-call form: the same bits as a plan's run, the plan created
