@@ -271,6 +271,43 @@ def test_handworked_golden():
     pin_golden(oracle.default())
 
 
+SPECIALS = {I.DTYPE_BF16: (0x7F80, 0xFF80, 0x7FC0), I.DTYPE_FP16: (0x7C00, 0xFC00, 0x7E00),
+            I.DTYPE_FP32: (0x7F800000, 0xFF800000, 0x7FC00000)}   # +inf, -inf, NaN
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("rhs_transpose", [False, True])
+def test_special_values_follow_ieee(dtype, rhs_transpose):
+    """Infinities and NaN in A: the oracle's outputs equal a plain Python
+    float loop over the same decoded values (IEEE double arithmetic), NaN
+    where that loop gives NaN; finite values are small integers, so every
+    finite output is exact.  B holds zeros too, so inf * 0 = NaN is met."""
+    N, m_s, k, n = 2, 3, 4, 5
+    shards = [I.small_int_bits((m_s, k), 40 + r, dtype, lo=-3, hi=3) for r in range(N)]
+    bshape = (n, k) if rhs_transpose else (k, n)
+    B = I.small_int_bits(bshape, 47, dtype, lo=-2, hi=2)
+    pinf, ninf, nan = SPECIALS[dtype]
+    shards[0][0, 1] = pinf
+    shards[0][2, 0] = ninf
+    shards[1][1, 0] = pinf
+    shards[1][1, 3] = ninf
+    shards[1][2, 2] = nan
+    got = oracle.agmm_f64(shards, B, dtype, rhs_transpose)
+    A = np.concatenate([I.bits_to_f64(x, dtype) for x in shards])
+    Bv = I.bits_to_f64(B, dtype)
+    for i in range(N * m_s):
+        for j in range(n):
+            acc = 0.0
+            for t in range(k):
+                b = float(Bv[j, t] if rhs_transpose else Bv[t, j])
+                acc += float(A[i, t]) * b
+            if acc != acc:
+                assert np.isnan(got[i, j]), (i, j)
+            else:
+                assert got[i, j] == acc, (i, j, got[i, j], acc)
+    assert np.isnan(got).any() and np.isinf(got).any()
+
+
 def test_decode_fp16_all_patterns():
     bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
     got = oracle.decode(bits, I.DTYPE_FP16)
