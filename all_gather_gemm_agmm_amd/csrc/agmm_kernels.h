@@ -68,7 +68,7 @@ enum TileCfg : int {
   kTile128x64r5 = 7,     // same ring, 128x64; B stored n x k only
   kTile256x256m16 = 8,   // part ring, 256x256, on 16x16x32 MFMAs (automatic for k >= 256)
   kTile128x128m16 = 9,   // part ring, 128x128, on 16x16x32 MFMAs
-  kTileSkinny = 10,      // whole k per workgroup, wave-private LDS rings (launch_skinny_fullk); B n x k only
+  kTileSkinny = 10,      // narrow tiles over all of k or k ranges, wave-private LDS rings (launch_skinny_fullk); B n x k only
   kTile256x224m16 = 11,  // part ring, 256x224 on 16x16x32 MFMAs (7 column blocks per wave); B n x k only
   kTileCount = 12,
 };
