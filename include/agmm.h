@@ -402,7 +402,9 @@ int agmm_run_noalloc(int num_shards, int64_t m_per_shard, int64_t k, int64_t n_l
                      int rhs_transpose, const void *const *shard_ptrs, const void *B, void *C,
                      void *stream);
 
-/* Thread-local status / message of the last failing call (AGMM_OK / "" if none). */
+/* Thread-local status / message of this thread's most recent call into the
+ * library (AGMM_OK and "" after a call that succeeded; calls on other threads
+ * never change them). */
 int agmm_last_status(void);
 const char *agmm_last_error(void);
 

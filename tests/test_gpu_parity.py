@@ -1416,6 +1416,61 @@ def test_serial_calls_on_two_streams_are_ordered(variant, settings):
         check_against_oracle(w, sh, B, C)
 
 
+def test_concurrent_plans_from_host_threads():
+    """Three host threads, each with its own plan (fused split-K, skinny k
+    ranges, staged) and its own stream, call at the same time; every output
+    is bit-identical to the same call made alone, and each thread's error
+    status stays its own (a rejected call in one thread does not disturb
+    the others)."""
+    import threading
+    specs = [((3, 100, 512, 264, BF16, True), {"variant": "fused", "splits": 3}),
+             ((4, 16, 2048, 512, BF16, True), {"variant": "skinny"}),
+             ((2, 300, 384, 136, FP16, False), {"variant": "staged", "pvalue": 1, "nbuf": 2})]
+    cases = []
+    for i, ((N, m_s, k, n, dtype, rt), settings) in enumerate(specs):
+        w, shards, B = make_case(N, m_s, k, n, dtype, rt, seed=3900 + i)
+        cases.append((w, [to_device(x, dtype) for x in shards], to_device(B, dtype), settings))
+    refs = []
+    for w, sd, bd, settings in cases:
+        with agmm.Plan(w.num_shards, w.m_per_shard, w.k, w.n_local, w.dtype, w.rhs_transpose, **settings) as plan:
+            refs.append(to_bits(plan.run(sd, bd)))
+            torch.cuda.synchronize()
+    errors, outs = [], [None] * len(cases)
+    start = threading.Barrier(len(cases))
+
+    def worker(i):
+        try:
+            w, sd, bd, settings = cases[i]
+            stream = torch.cuda.Stream()
+            with agmm.Plan(w.num_shards, w.m_per_shard, w.k, w.n_local, w.dtype, w.rhs_transpose,
+                           **settings) as plan:
+                C = torch.empty((w.m, w.n_local), dtype=torch_dtype(w.dtype), device="cuda")
+                start.wait()
+                for it in range(30):
+                    plan.run(sd, bd, C, stream=stream)
+                    if i == 0 and it == 10:
+                        # rejected here, in this thread only (the C call alone:
+                        # the binding's own follow-up calls would reset it)
+                        st = agmm.load_library().agmm_plan_set_int(plan.handle, b"tile", 99)
+                        assert st == agmm.AGMM_ERR_INVALID_ARG
+                        time.sleep(0.01)   # the other threads' calls succeed meanwhile
+                        assert agmm.agmm_last_status() == agmm.AGMM_ERR_INVALID_ARG
+                        assert "tile" in agmm.agmm_last_error()
+                stream.synchronize()
+                outs[i] = to_bits(C)
+        except Exception as e:   # reported on the main thread
+            errors.append(repr(e))
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(len(cases))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=60)
+    assert not errors, errors
+    for i, (out, ref) in enumerate(zip(outs, refs)):
+        assert out is not None and np.array_equal(out, ref), f"thread {i}: output differs"
+
+
 def test_oom_hook_reports_status(monkeypatch):
     monkeypatch.setenv("AGMM_TEST_FAIL_ALLOC", "1")
     with pytest.raises(agmm.AgmmError) as ei:
