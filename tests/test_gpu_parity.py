@@ -1471,6 +1471,46 @@ def test_concurrent_plans_from_host_threads():
         assert out is not None and np.array_equal(out, ref), f"thread {i}: output differs"
 
 
+def test_runs_allocate_nothing(monkeypatch):
+    """Once the plans exist, every workspace allocation is made to fail
+    (the test hook): runs on every path, the gather, the gathered-output
+    and already-gathered entry points all still succeed and match the
+    oracle, so none of them allocates."""
+    specs = [((3, 100, 512, 264, BF16, False), {"variant": "fused"}),
+             ((3, 100, 512, 264, FP16, True), {"variant": "staged", "pvalue": 1, "nbuf": 2}),
+             ((3, 100, 512, 264, BF16, True), {"variant": "unfused"}),
+             ((4, 16, 2048, 512, BF16, True), {"variant": "skinny"}),
+             ((2, 50, 13, 20, BF16, False), {}),                        # padded copies
+             ((2, 64, 200, 96, FP32, False), {"variant": "fused"})]
+    made = []
+    try:
+        for i, ((N, m_s, k, n, dtype, rt), settings) in enumerate(specs):
+            w, shards, B = make_case(N, m_s, k, n, dtype, rt, seed=4000 + i)
+            plan = agmm.Plan(N, m_s, k, n, dtype, rt, **settings)
+            made.append((w, shards, B, plan, [to_device(x, dtype) for x in shards], to_device(B, dtype)))
+        monkeypatch.setenv("AGMM_TEST_FAIL_ALLOC", "1")
+        for w, shards, B, plan, sd, bd in made:
+            C = plan.run(sd, bd)
+            C2, G = plan.run_gather_out(sd, bd)
+            torch.cuda.synchronize()
+            check_against_oracle(w, shards, B, C)
+            assert np.array_equal(to_bits(C2), to_bits(C))
+            assert np.array_equal(to_bits(G), oracle.gather(shards, w.dtype))
+            C3 = plan.run_gathered(G, bd)
+            G2 = plan.gather(sd)
+            torch.cuda.synchronize()
+            check_against_oracle(w, shards, B, C3)
+            assert np.array_equal(to_bits(G2), to_bits(G))
+        # the hook is live: a new plan that needs a workspace fails to get one
+        with pytest.raises(agmm.AgmmError) as ei:
+            agmm.Plan(2, 512, 256, 256, BF16, False, variant="unfused")
+        assert ei.value.status == agmm.AGMM_ERR_OOM
+    finally:
+        monkeypatch.delenv("AGMM_TEST_FAIL_ALLOC", raising=False)
+        for m in made:
+            m[3].close()
+
+
 def test_oom_hook_reports_status(monkeypatch):
     monkeypatch.setenv("AGMM_TEST_FAIL_ALLOC", "1")
     with pytest.raises(agmm.AgmmError) as ei:
