@@ -167,7 +167,10 @@ int agmm_run(agmm_plan_t plan, const void *const *shard_ptrs, const void *B, voi
  * a bit-exact copy.  gathered is a device buffer [m, k] of the plan's dtype,
  * 16-byte aligned (rows of any length: a vector copy for whole 16-byte rows,
  * an element copy otherwise).  (The gathered operand the tpu-inference kernel returns as
- * its second output, `x_hbm_scratch`.)  Same stream rules as agmm_run.
+ * its second output, `x_hbm_scratch`.)  Same pointer and stream rules as
+ * agmm_run.  It uses none of the plan's workspace and so takes no part in
+ * the ordering between the plan's calls: order it against other work that
+ * reads or writes `gathered` with the caller's streams.
  */
 int agmm_gather(agmm_plan_t plan, const void *const *shard_ptrs, void *gathered, void *stream);
 
