@@ -107,3 +107,45 @@ def test_null_handles_are_rejected_without_touching_the_gpu():
 def test_missing_library_fails_loudly(tmp_path):
     with pytest.raises(RuntimeError, match="no CPU fallback"):
         agmm.load_library(str(tmp_path / "libagmm.so"))
+
+
+def _header_rule_statuses(N, m_s, k, n, dtype, rt):
+    """Statuses the header's agmm_plan_validate rules give a problem (an empty
+    set: accepted)."""
+    out = set()
+    if N < 1 or min(m_s, k, n) < 1 or dtype not in (0, 1, 2) or rt not in (0, 1):
+        out.add(agmm.AGMM_ERR_INVALID_ARG)
+    if N > 64:
+        out.add(agmm.AGMM_ERR_UNSUPPORTED)
+    if not out:
+        m = N * m_s
+        if max(m, k, n) >= 1 << 30 or max(m * k, k * n, m * n) >= 1 << 40:
+            out.add(agmm.AGMM_ERR_UNSUPPORTED)
+    return out
+
+
+def test_validate_follows_the_header_rules():
+    """agmm_plan_validate against the header's rules, restated here, on drawn
+    problems: sizes around 1, around the 2^30 and 2^40 limits and anywhere in
+    between, in- and out-of-range dtypes, layout flags and shard counts."""
+    hyp = pytest.importorskip("hypothesis")
+    st = hyp.strategies
+    size = st.one_of(st.integers(-2, 3), st.integers(1, 1 << 12),
+                     st.integers((1 << 20) - 2, (1 << 20) + 2), st.integers((1 << 30) - 2, (1 << 30) + 1),
+                     st.integers(1, (1 << 31) - 1))
+    lib = agmm.load_library()
+
+    @hyp.settings(max_examples=3000, deadline=None, derandomize=True)
+    @hyp.given(N=st.integers(-1, 70), m_s=size, k=size, n=size, dtype=st.integers(-1, 3),
+               rt=st.integers(-1, 2))
+    def check(N, m_s, k, n, dtype, rt):
+        want = _header_rule_statuses(N, m_s, k, n, dtype, rt)
+        got = lib.agmm_plan_validate(N, m_s, k, n, dtype, rt)
+        if want:
+            assert got in want, (N, m_s, k, n, dtype, rt, got, agmm.agmm_last_error())
+            assert agmm.agmm_last_status() == got and agmm.agmm_last_error() != ""
+        else:
+            assert got == agmm.AGMM_OK, (N, m_s, k, n, dtype, rt, agmm.agmm_last_error())
+            assert agmm.agmm_last_error() == ""
+
+    check()
