@@ -199,17 +199,36 @@ def agmm_run_noalloc(num_shards, m_per_shard, k, n_local, dtype, rhs_transpose,
 def run_noalloc(shards, B, C, rhs_transpose: bool, stream=None):
     """agmm_run_noalloc on torch tensors: dense row-major shards [m_s, k], B
     [k, n] (or [n, k] with rhs_transpose) and a caller-provided C [m, n]."""
+    import torch
+    if len(shards) == 0:
+        raise ValueError("agmm_run_noalloc needs at least one shard")
+    tensors = list(shards) + [B, C]
+    if not all(isinstance(t, torch.Tensor) for t in tensors):
+        raise TypeError("shards, B and C must be torch tensors")
+    dtype = {torch.bfloat16: AGMM_BF16, torch.float16: AGMM_FP16,
+             torch.float32: AGMM_FP32}.get(B.dtype)
+    if dtype is None:
+        raise TypeError(f"unsupported dtype {B.dtype}")
+    device = B.device
+    if device.type != "cuda":
+        raise ValueError("B must be on the GPU")
+    for t in tensors:
+        if t.device != device:
+            raise ValueError(f"every tensor must be on {device} (found one on {t.device})")
+        if t.dtype != B.dtype:
+            raise TypeError(f"every tensor must have dtype {B.dtype} (found {t.dtype})")
+        if t.dim() != 2 or not t.is_contiguous():
+            raise ValueError("agmm_run_noalloc takes dense row-major 2-D tensors")
     m_s, k = shards[0].shape
+    if any(tuple(t.shape) != (m_s, k) for t in shards):
+        raise ValueError(f"every shard must have shape {(m_s, k)}")
     n = B.shape[0] if rhs_transpose else B.shape[1]
-    dtype = {"torch.bfloat16": AGMM_BF16, "torch.float16": AGMM_FP16,
-             "torch.float32": AGMM_FP32}[str(B.dtype)]
-    for t in list(shards) + [B, C]:
-        if not t.is_contiguous():
-            raise ValueError("agmm_run_noalloc takes dense row-major tensors")
+    if (B.shape[1] if rhs_transpose else B.shape[0]) != k:
+        raise ValueError(f"B has shape {tuple(B.shape)}, which does not match k = {k}")
     if tuple(C.shape) != (len(shards) * m_s, n):
         raise ValueError(f"C has shape {tuple(C.shape)}, expected {(len(shards) * m_s, n)}")
     agmm_run_noalloc(len(shards), m_s, k, n, dtype, rhs_transpose, [s.data_ptr() for s in shards],
-                     B.data_ptr(), C.data_ptr(), _stream_handle(stream))
+                     B.data_ptr(), C.data_ptr(), _stream_handle(stream, device.index))
     return C
 
 
@@ -252,6 +271,8 @@ class Plan:
         self.num_shards, self.m_per_shard, self.k, self.n_local = num_shards, m_per_shard, k, n_local
         self.dtype, self.rhs_transpose = dtype, bool(rhs_transpose)
         self.handle = agmm_plan_create(num_shards, m_per_shard, k, n_local, dtype, rhs_transpose)
+        import torch
+        self.device = torch.cuda.current_device()   # the device the library created the plan on
         self._tdt = _torch_dtype(dtype)
         self._ptrs = (ctypes.c_void_p * num_shards)()   # shard pointer table, reused per call
         self._read_strides()
@@ -284,8 +305,8 @@ class Plan:
         ld = self._ld[ld_key] if ld_key else shape[1]
         try:   # the common case in a few attribute reads
             st = t.stride()
-            if (t.dtype is self._tdt and t.is_cuda and t.shape == shape and st[1] == 1 and
-                    (shape[0] <= 1 or st[0] == ld)):
+            if (t.dtype is self._tdt and t.is_cuda and t.get_device() == self.device and
+                    t.shape == shape and st[1] == 1 and (shape[0] <= 1 or st[0] == ld)):
                 return
         except (AttributeError, TypeError, IndexError):
             pass
@@ -296,6 +317,8 @@ class Plan:
             raise TypeError(f"{name} must be a torch.Tensor")
         if t.device.type != "cuda":
             raise ValueError(f"{name} must be on the GPU")
+        if t.get_device() != self.device:
+            raise ValueError(f"{name} is on {t.device}; the plan was created on cuda:{self.device}")
         if t.dtype != _torch_dtype(self.dtype):
             raise TypeError(f"{name} has dtype {t.dtype}, plan expects {_torch_dtype(self.dtype)}")
         if tuple(t.shape) != tuple(shape):
@@ -358,10 +381,12 @@ class Plan:
             C = self._new_c(B.device)
         self._check_tensor(C, (self.m, self.n_local), "C", "ldc")
         return agmm_plan_autotune(self.handle, [s.data_ptr() for s in shards], B.data_ptr(),
-                                  C.data_ptr(), _stream_handle(stream), iters)
+                                  C.data_ptr(), _stream_handle(stream, B.device.index), iters)
 
     def gather(self, shards, out=None, stream=None):
         import torch
+        if len(shards) != self.num_shards:
+            raise ValueError(f"expected {self.num_shards} shards, got {len(shards)}")
         for r, s in enumerate(shards):
             self._check_tensor(s, (self.m_per_shard, self.k), "shards", "lda", r)
         if out is None:
@@ -430,11 +455,15 @@ def all_gather_matmul(shards, B, rhs_transpose: bool = False, C=None, stream=Non
              "torch.float32": AGMM_FP32}.get(str(B.dtype))
     if dtype is None:
         raise ValueError(f"unsupported dtype {B.dtype}")
+    if B.device.type != "cuda":
+        raise ValueError("B must be on the GPU")
+    import torch
     key = (len(shards), int(m_s), int(k), int(n), dtype, bool(rhs_transpose), B.device.index)
     with _PLAN_CACHE_LOCK:
         plan = _PLAN_CACHE.get(key)
         if plan is None:
-            plan = Plan(len(shards), int(m_s), int(k), int(n), dtype, bool(rhs_transpose))
+            with torch.cuda.device(B.device):
+                plan = Plan(len(shards), int(m_s), int(k), int(n), dtype, bool(rhs_transpose))
             _PLAN_CACHE[key] = plan
     return plan.run(shards, B, C, stream=stream)
 

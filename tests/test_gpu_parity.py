@@ -1288,6 +1288,46 @@ def test_run_rejects_misaligned_pointer():
         plan.close()
 
 
+def test_binding_rejects_misplaced_tensors():
+    """The torch binding's host checks: a tensor on the CPU, of another
+    dtype or shape, or a short shard list is refused with an exception before
+    any pointer reaches the library (which would otherwise read host memory
+    or past the pointer table on the GPU)."""
+    w, shards, B = make_case(2, 8, 64, 64, BF16, True, seed=85)
+    sd = [to_device(s, BF16) for s in shards]
+    bd = to_device(B, BF16)
+    C = torch.zeros((16, 64), dtype=torch.bfloat16, device="cuda")
+    plan = agmm.Plan(2, 8, 64, 64, BF16, True)
+    try:
+        with pytest.raises(ValueError, match="expected 2 shards"):
+            plan.gather(sd[:1])
+        with pytest.raises(ValueError, match="on the GPU"):
+            plan.run([sd[0], sd[1].cpu()], bd)
+        with pytest.raises(ValueError, match="on the GPU"):
+            plan.run_gathered(torch.zeros((16, 64), dtype=torch.bfloat16), bd)
+        with pytest.raises(TypeError, match="dtype"):
+            plan.run(sd, bd.half())
+        with pytest.raises(ValueError, match="shape"):
+            plan.run(sd, bd[:, :32])
+    finally:
+        plan.close()
+    # the plan-free entry point
+    with pytest.raises(ValueError, match="on cuda"):
+        agmm.run_noalloc(sd, bd, C.cpu(), True)
+    with pytest.raises(TypeError, match="dtype"):
+        agmm.run_noalloc(sd, bd, C.half(), True)
+    with pytest.raises(ValueError, match="every shard"):
+        agmm.run_noalloc([sd[0], sd[1][:4]], bd, C, True)
+    with pytest.raises(ValueError, match="does not match k"):
+        agmm.run_noalloc(sd, bd[:, :32].contiguous(), C, True)
+    with pytest.raises(ValueError, match="on the GPU"):
+        agmm.run_noalloc([s.cpu() for s in sd], bd.cpu(), C.cpu(), True)
+    # the checks above changed nothing: a correct call still runs
+    agmm.run_noalloc(sd, bd, C, True)
+    torch.cuda.synchronize()
+    check_against_oracle(w, shards, B, C)
+
+
 def test_set_int_rejection_keeps_the_plan():
     """A rejected setting (the skinny tile on a plan whose B is
     stored k x n) leaves every setting as it was: the plan still runs with
