@@ -297,6 +297,100 @@ def test_workload4_every_tile():
     assert torch.equal(C.view(torch.int16), outs["unfused"][0].view(torch.int16))
 
 
+@pytest.mark.parametrize("wid", [2, 3])
+def test_workload_graph_of_calls_over_buffer_sets(wid):
+    """Workloads 2 and 3 in the form their short steps are timed: 20 calls
+    of one plan (the automatic path: split-K 128x128 tiles, the skinny
+    kernel) captured into one HIP graph on a side stream, each call on the
+    next of several buffer sets.  Here every set holds its own seeded inputs,
+    so a call that read another set's operands or wrote another set's output
+    would show: two replays, every set's C against the oracle and
+    bit-identical to an eager call on that set."""
+    w = I.WORKLOADS[wid]
+    nsets, calls = 8, 20
+    sets, host = [], []
+    for i in range(nsets):
+        shards, B = I.make_inputs(w, seed_base=5000 + 10 * wid + i)
+        host.append((shards, B))
+        sets.append(([to_device(x, w.dtype) for x in shards], to_device(B, w.dtype),
+                     torch.empty((w.m, w.n_local), dtype=torch_dtype(w.dtype), device="cuda")))
+    plan = agmm.Plan(w.num_shards, w.m_per_shard, w.k, w.n_local, w.dtype, w.rhs_transpose)
+    try:
+        assert plan.get("splits") > 1 or plan.get("tile") == agmm.TILE_SKINNY
+        eager = []
+        for sd, bd, _ in sets:
+            eager.append(to_bits(plan.run(sd, bd)))
+        torch.cuda.synchronize()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(g, stream=side):
+                for c in range(calls):
+                    sd, bd, C = sets[c % nsets]
+                    plan.run(sd, bd, C, stream=side)
+        torch.cuda.synchronize()
+        for rep in range(2):
+            for _, _, C in sets:
+                C.fill_(float("nan"))
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            for i, ((shards, B), (_, _, C)) in enumerate(zip(host, sets)):
+                bits = to_bits(C)
+                assert np.array_equal(bits, eager[i]), f"replay {rep}, set {i}: differs from eager"
+                if rep == 0:
+                    check_against_oracle(w, shards, B, C)
+        del g
+    finally:
+        plan.close()
+
+
+def test_workload2_staged_one_call_graphs_over_buffer_sets():
+    """Workload 2 staged (pvalue 2, two slots) in the form its steps are
+    timed: one HIP graph per buffer set, each holding one staged call, the
+    graphs replayed in turn.  Every set has its own inputs; every replay of
+    every set matches the oracle and an eager call bit for bit."""
+    w = I.WORKLOADS[2]
+    nsets = 4
+    host, sets = [], []
+    for i in range(nsets):
+        shards, B = I.make_inputs(w, seed_base=5100 + i)
+        host.append((shards, B))
+        sets.append(([to_device(x, w.dtype) for x in shards], to_device(B, w.dtype),
+                     torch.empty((w.m, w.n_local), dtype=torch_dtype(w.dtype), device="cuda")))
+    plan = agmm.Plan(w.num_shards, w.m_per_shard, w.k, w.n_local, w.dtype, w.rhs_transpose,
+                     variant="staged", pvalue=2, nbuf=2)
+    try:
+        assert plan.get("num_chunks") <= plan.get("num_slots")
+        eager = [to_bits(plan.run(sd, bd)) for sd, bd, _ in sets]
+        torch.cuda.synchronize()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        graphs = []
+        for sd, bd, C in sets:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.stream(side):
+                with torch.cuda.graph(g, stream=side):
+                    plan.run(sd, bd, C, stream=side)
+            graphs.append(g)
+        torch.cuda.synchronize()
+        for rep in range(2):
+            for _, _, C in sets:
+                C.fill_(float("nan"))
+            torch.cuda.synchronize()
+            for g in graphs:
+                g.replay()
+            torch.cuda.synchronize()
+            for i, ((shards, B), (_, _, C)) in enumerate(zip(host, sets)):
+                assert np.array_equal(to_bits(C), eager[i]), f"replay {rep}, set {i}"
+                if rep == 0:
+                    check_against_oracle(w, shards, B, C)
+        del graphs
+    finally:
+        plan.close()
+
+
 def test_workload5_every_tile_every_variant():
     """Workload 5, the benchmarked configuration (8 x 4096 x 8192 -> 7168
     bf16), through the fused, staged (pvalue 2, 2 slots: 8 chunks, each slot
