@@ -1344,20 +1344,20 @@ int agmm_plan_autotune(agmm_plan_t p, const void* const* shard_ptrs, const void*
     std::vector<Timed> timed;
     // the skinny tile also over its 32 x 32 and 64 x 64 shapes
     const int shapes_skinny[] = {5, 7}, shapes_other[] = {-1};
+    // a candidate whose workspace could not be allocated, with the previous
+    // one not restorable either, leaves the plan unusable: stop there
     for (int t : tiles)
       for (int sh : t == agmm::kTileSkinny ? std::vector<int>(std::begin(shapes_skinny), std::end(shapes_skinny))
                                            : std::vector<int>(std::begin(shapes_other), std::end(shapes_other)))
       for (int sp : splits_c)
         for (int gm : groups_c) {
+          if (p->broken != AGMM_OK) continue;
           Settings s2 = base;
           s2.tile = t;
           s2.splits = sp;
           s2.group_m = gm;
           if (sh >= 0) s2.skinny_shape = sh;
-          if (mark_done() != AGMM_OK || apply(p, s2) != AGMM_OK) {
-            if (p->broken != AGMM_OK) break;
-            continue;
-          }
+          if (mark_done() != AGMM_OK || apply(p, s2) != AGMM_OK) continue;
           // the skinny kernel has its own tile order (no group_m)
           const bool sk = p->L.tile_used == agmm::kTileSkinny;
           const std::array<int, 4> key = {p->L.tile_used, p->L.splits_used, sk ? -1 : p->s.group_m,
@@ -1381,7 +1381,7 @@ int agmm_plan_autotune(agmm_plan_t p, const void* const* shard_ptrs, const void*
     std::vector<double> sum(timed.size(), 0.0);
     std::vector<int> cnt(timed.size(), 0);
     for (int round = 0; round < 3 && timed.size() > 1 && p->broken == AGMM_OK; ++round)
-      for (size_t i = 0; i < timed.size(); ++i) {
+      for (size_t i = 0; i < timed.size() && p->broken == AGMM_OK; ++i) {
         double ms = 0;
         if (mark_done() != AGMM_OK || apply(p, timed[i].s) != AGMM_OK) continue;
         if (time_current(ms) != AGMM_OK) {

@@ -1496,6 +1496,48 @@ def test_set_int_oom_unrecoverable_plan_refuses_runs(monkeypatch):
         plan.close()
 
 
+def test_autotune_under_allocation_limits(monkeypatch):
+    """Autotune when workspace allocations fail (test hook).  With no
+    allocation larger than the plan's current workspace, the candidates that
+    need more are skipped and the plan keeps a correct configuration that
+    fits.  With every allocation failing, a candidate that needs a larger
+    workspace leaves the plan without one: autotune stops, reports
+    AGMM_ERR_OOM, and the plan then refuses runs."""
+    w, shards, B = make_case(3, 200, 512, 136, BF16, True, seed=87)
+    sd = [to_device(x, BF16) for x in shards]
+    bd = to_device(B, BF16)
+    plan = agmm.Plan(3, 200, 512, 136, BF16, True, variant="unfused")
+    try:
+        limit = plan.workspace_bytes()
+        monkeypatch.setenv("AGMM_TEST_FAIL_ALLOC", str(limit))
+        C = torch.full((w.m, w.n_local), float("nan"), dtype=torch.bfloat16, device="cuda")
+        plan.autotune(sd, bd, C, iters=1)
+        monkeypatch.delenv("AGMM_TEST_FAIL_ALLOC")
+        assert plan.get("usable") == 1 and plan.workspace_bytes() <= limit
+        C2 = plan.run(sd, bd)
+        torch.cuda.synchronize()
+        check_against_oracle(w, shards, B, C)
+        check_against_oracle(w, shards, B, C2)
+    finally:
+        plan.close()
+    plan = agmm.Plan(3, 200, 512, 136, BF16, True, variant="unfused")
+    try:
+        monkeypatch.setenv("AGMM_TEST_FAIL_ALLOC", "1")
+        with pytest.raises(agmm.AgmmError) as ei:
+            plan.autotune(sd, bd, iters=1)
+        assert ei.value.status == agmm.AGMM_ERR_OOM
+        monkeypatch.delenv("AGMM_TEST_FAIL_ALLOC")
+        assert plan.get("usable") == 0
+        C = torch.full((w.m, w.n_local), float("nan"), dtype=torch.bfloat16, device="cuda")
+        with pytest.raises(agmm.AgmmError) as ei:
+            plan.run(sd, bd, C)
+        assert ei.value.status == agmm.AGMM_ERR_OOM
+        torch.cuda.synchronize()
+        assert torch.isnan(C.float()).all().item()
+    finally:
+        plan.close()
+
+
 def _spin_cycles_per_ms():
     """Rate of torch's bounded spin kernel (torch.cuda._sleep) on this GPU.
     The kernel runs once untimed first: the first launch in a process also
