@@ -76,8 +76,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         return _lib
     if not os.path.exists(path):
         raise RuntimeError(
-            f"{path} is missing: build it with `python -m all_gather_gemm_agmm_amd._build` "
-            "(or __graft_entry__.build()); the all-gather matmul has no CPU fallback")
+            f"{path} is missing: build it with `python -m all_gather_gemm_agmm_amd._build`; "
+            "the all-gather matmul has no CPU fallback")
     lib = ctypes.CDLL(path)
     for name, res, args in EXPORTS:
         fn = getattr(lib, name)
