@@ -171,14 +171,44 @@ __device__ __forceinline__ void load_lds16_at(const void* gsrc, uint32_t lds_add
 // fixed over the k loop, so a load costs no vector address arithmetic (the
 // flat form adds a 64-bit k offset to every lane's pointer per load), and the
 // descriptor's record count bounds every lane's offset.  LDS placement is the
-// flat form's: lane i writes bytes [16i, 16i+16) of the block at `lds_addr`.
-__device__ __forceinline__ void load_lds16_buf(const u32x4_t& rsrc, uint32_t voff, uint32_t soff,
-                                               uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %3 offen lds"
-               :
-               : "v"(voff), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(lds_addr)),
-                 "s"(__builtin_amdgcn_readfirstlane(soff))
-               : "m0");
+// flat form's: lane i writes bytes [16i, 16i+16) of a 1 KiB block.
+// The load goes into block R (0..3) of a 4 KiB LDS group: the instruction's
+// offset field, R KiB, moves the LDS destination and the memory address
+// alike, so `voff` is the lane's offset less R KiB.  With SET the load first
+// writes the group's base into M0; without it M0 must already hold that
+// base (the previous load of the group set it, and nothing between writes
+// M0).  Writing M0 right before a DMA load costs the issuing wave about nine
+// cycles beside its MFMA stream, against about one for the load alone
+// (measured on MI355X), so one write serves four loads.
+template <int R, bool SET>
+__device__ __forceinline__ void load_lds16_buf_grp(const u32x4_t& rsrc, uint32_t voff, uint32_t soff,
+                                                   uint32_t group_lds) {
+  static_assert(R >= 0 && R < 4, "block of a 4 KiB group");
+  if constexpr (SET)
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %3 offen offset:%4 lds"
+                 :
+                 : "v"(voff), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(group_lds)),
+                   "s"(__builtin_amdgcn_readfirstlane(soff)), "n"(R * 1024)
+                 : "m0");
+  else
+    asm volatile("buffer_load_dwordx4 %0, %1, %2 offen offset:%3 lds"
+                 :
+                 : "v"(voff), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(soff)), "n"(R * 1024)
+                 : "memory");
+}
+
+// Load j of a part: block j % 4 of group j / 4; M0 is written at the first
+// block of each group.  A part's loads are issued in increasing j with no
+// other M0 write between them.
+__device__ __forceinline__ void load_lds16_buf_j(int j, const u32x4_t& rsrc, uint32_t voff_shifted,
+                                                 uint32_t soff, uint32_t part_lds) {
+  const uint32_t grp = part_lds + (uint32_t)(j & ~3) * 1024u;
+  switch (j & 3) {
+    case 0: load_lds16_buf_grp<0, true>(rsrc, voff_shifted, soff, grp); break;
+    case 1: load_lds16_buf_grp<1, false>(rsrc, voff_shifted, soff, grp); break;
+    case 2: load_lds16_buf_grp<2, false>(rsrc, voff_shifted, soff, grp); break;
+    default: load_lds16_buf_grp<3, false>(rsrc, voff_shifted, soff, grp); break;
+  }
 }
 
 // Raw buffer descriptor (stride 0, so the record count is in bytes) over
@@ -930,7 +960,18 @@ void gemm_m16_kernel(GemmProblem p) {
   const int64_t a_span = (int64_t)(BM - 1) * p.rows.a_ld * 2 + kspan;
   const int64_t b_span = BT ? (int64_t)(BN - 1) * p.ldb * 2 + kspan
                             : (int64_t)(k_end - k_begin - 1) * p.ldb * 2 + BN * 2;
-  const bool buf_ok = (row0 + BM <= p.rows.rows_per_group) && a_span < (1ll << 32) && b_span < (1ll << 32);
+  // Load j of a wave lands in block j % 4 of its 4 KiB LDS group, reached
+  // through the instruction's offset field, so its lane offsets are stored
+  // less (j % 4) KiB.  Wave 0's first lane has the smallest offset of load j:
+  // row 8j (A, B n x k: 8 rows per load) or k-row floor(1 KiB j / B_ROW)
+  // (B k x n), so row strides of at least 64 elements (A, B n x k) and
+  // 512 / floor(1 KiB / B_ROW) elements (B k x n) keep every shifted offset
+  // non-negative; interior tiles always meet them (k, ldb >= a 64-deep
+  // k-tile; ldb >= n >= BN).
+  const bool shift_ok = p.rows.a_ld >= 64 &&
+                        (BT ? p.ldb >= 64 : (int64_t)p.ldb * 2 * (1024 / T::B_ROW) >= 1024);
+  const bool buf_ok = (row0 + BM <= p.rows.rows_per_group) && a_span < (1ll << 32) && b_span < (1ll << 32) &&
+                      shift_ok;
   u32x4_t rsrc_a{}, rsrc_b{};
   uint32_t a_voff[T::A_IPW], b_voff[T::B_IPW];
   if (buf_ok) {
@@ -944,19 +985,19 @@ void gemm_m16_kernel(GemmProblem p) {
   for (int j = 0; j < T::A_IPW; ++j) {
     const int r = (wave * T::A_IPW + j) * T::RPI + lane / T::CPR;
     const int c = (lane % T::CPR) ^ swz_k16(r);
-    a_voff[j] = (uint32_t)(((int64_t)r * p.rows.a_ld + c * 8) * 2);
+    a_voff[j] = (uint32_t)(((int64_t)r * p.rows.a_ld + c * 8) * 2 - (j & 3) * 1024);
   }
 #pragma unroll
   for (int j = 0; j < T::B_IPW; ++j) {
     if constexpr (BT) {
       const int r = (wave * T::B_IPW + j) * T::RPI + lane / T::CPR;
       const int c = (lane % T::CPR) ^ swz_k16(r);
-      b_voff[j] = (uint32_t)(((int64_t)r * p.ldb + c * 8) * 2);
+      b_voff[j] = (uint32_t)(((int64_t)r * p.ldb + c * 8) * 2 - (j & 3) * 1024);
     } else {
       const int byte = (wave * T::B_IPW + j) * 1024 + lane * 16;
       const int kr = byte / T::B_ROW;
       const int c = ((byte % T::B_ROW) >> 4) ^ swz_n16(kr);
-      b_voff[j] = (uint32_t)(((int64_t)kr * p.ldb + c * 8) * 2);
+      b_voff[j] = (uint32_t)(((int64_t)kr * p.ldb + c * 8) * 2 - (j & 3) * 1024);
     }
   }
 
@@ -1096,12 +1137,12 @@ void gemm_m16_kernel(GemmProblem p) {
     auto put_a = [&](int slot, int t, int j0, int j1) {
 #pragma unroll
       for (int j = j0; j < j1; ++j) {
-        if constexpr (MODE == 2) load_lds16_buf(rsrc_a, a_voff[j], a_soff(t), lds_a + slot * PB + j * 1024);
+        if constexpr (MODE == 2) load_lds16_buf_j(j, rsrc_a, a_voff[j], a_soff(t), lds_a + slot * PB);
         else load_lds16_at(a_addr(j, t), lds_a + slot * PB + j * 1024);
       }
     };
     auto put_b_one = [&](int slot, int t, int j) {
-      if constexpr (MODE == 2) load_lds16_buf(rsrc_b, b_voff[j], b_soff(t), lds_b + slot * PB + j * 1024);
+      if constexpr (MODE == 2) load_lds16_buf_j(j, rsrc_b, b_voff[j], b_soff(t), lds_b + slot * PB);
       else load_lds16_at(b_addr(j, t), lds_b + slot * PB + j * 1024);
     };
     auto put_b = [&](int slot, int t) {

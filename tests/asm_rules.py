@@ -10,6 +10,12 @@ recognizer does not see those as MFMAs, so the kernel source promises:
 
 `check_function` verifies all three on the text `clang -S` emits, where each
 inline-assembly statement sits between `;;#ASMSTART` and `;;#ASMEND`.
+
+The buffer-descriptor loads into LDS share one M0 write among the loads of
+a 4 KiB LDS group: a load that does not write M0 itself relies on the group's
+first load having done so, with nothing writing M0 in between.
+`check_m0` verifies that M0 is written only by inline assembly and that on
+every path to such a load the last M0 write came from inline assembly.
 Test infrastructure only; nothing here is part of the product path."""
 import re
 
@@ -33,7 +39,7 @@ def functions(asm_text: str):
         i = j
 
 
-def _blocks(lines):
+def _blocks(lines, tag_asm=False):
     blocks, cur, in_asm = [], [None, []], False
     for line in lines:
         m = re.match(r"^(\.LBB\S+):", line)
@@ -54,6 +60,8 @@ def _blocks(lines):
         t = t.split(";")[0].strip()
         if in_asm and t.startswith("v_mfma"):
             t = "ASM " + t
+        elif in_asm and tag_asm:
+            t = "INL " + t
         cur[1].append(t)
         if t.startswith(("s_branch", "s_cbranch", "s_endpgm", "s_setpc")):
             blocks.append(cur)
@@ -173,3 +181,52 @@ def check_function(lines):
             if hit:
                 violations.append(("VALU write of an MFMA source within 4 wait states", hit + " -> " + t))
     return n_asm, violations
+
+
+def _writes_m0(t):
+    ops = _operands(t)
+    return bool(ops) and ops[0] == "m0"
+
+
+def check_m0(lines):
+    """Return (number of inline-assembly LDS-DMA loads checked, list of
+    violations): M0 written outside inline assembly, or a load reached on
+    some path with no inline-assembly M0 write as the last write of M0."""
+    blocks, succ, pred = _blocks(lines, tag_asm=True)
+    violations, relying = [], 0
+
+    def step(k, ours, record):
+        nonlocal relying
+        for t in blocks[k][1]:
+            inl = t.startswith("INL ")
+            body = t[4:] if inl else t
+            if _writes_m0(body):
+                if not inl and record:
+                    violations.append(("M0 written outside inline assembly", body))
+                ours = inl
+                continue
+            if inl and re.match(r"(?:buffer|global)_load_\w+ .*\blds$", body):
+                if record:
+                    relying += 1
+                    if not ours:
+                        violations.append(("LDS-DMA load without an inline-assembly M0 write before it", body))
+        return ours
+
+    # forward dataflow: "the last M0 write on every path came from inline
+    # assembly"; false at the entry (M0 is undefined there)
+    state_in = [True] * len(blocks)
+    if blocks:
+        state_in[0] = False
+    changed = True
+    while changed:
+        changed = False
+        for k in range(len(blocks)):
+            inc = state_in[k] if k == 0 else all(step(p, state_in[p], False) for p in pred[k]) if pred[k] else state_in[k]
+            if k == 0:
+                inc = False
+            if inc != state_in[k]:
+                state_in[k] = inc
+                changed = True
+    for k in range(len(blocks)):
+        step(k, state_in[k], True)
+    return relying, violations

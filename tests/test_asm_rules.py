@@ -1,6 +1,7 @@
 """The inline-assembly MFMAs of gemm_m16_kernel against the rules its source
 states (no accumulator access next to an MFMA the compiler cannot see, no
-VALU-written MFMA operand without wait states), checked on the assembly of
+VALU-written MFMA operand without wait states), and its grouped LDS-DMA
+loads against theirs (M0 written only by inline assembly), checked on the assembly of
 gemm_mfma.hip compiled with the library's own flags.  Runs on the CPU
 (hipcc cross-compiles for gfx950); the checker itself is first tested on
 small hand-written listings."""
@@ -98,6 +99,63 @@ def test_checker_follows_branches():
     assert len(bad) == 1 and "after an MFMA" in bad[0][0]
 
 
+SETLOAD = (";;#ASMSTART\ns_mov_b32 m0, s4\ns_nop 0\nbuffer_load_dwordx4 v1, s[8:11], s5 offen offset:0 lds\n"
+           ";;#ASMEND")
+LOAD = ";;#ASMSTART\nbuffer_load_dwordx4 v2, s[8:11], s5 offen offset:0x400 lds\n;;#ASMEND"
+
+
+def _check_m0(body: str):
+    (_, lines), = list(asm_rules.functions(_listing(body)))
+    return asm_rules.check_m0(lines)
+
+
+def test_m0_checker_accepts_a_shared_write():
+    n, bad = _check_m0(f"""
+        {SETLOAD}
+        v_add_u32_e32 v3, v4, v5
+        {LOAD}
+        {LOAD}
+    """)
+    assert n == 3 and bad == []
+
+
+def test_m0_checker_rejects_a_compiler_write():
+    n, bad = _check_m0(f"""
+        {SETLOAD}
+        s_mov_b32 m0, s6
+        {LOAD}
+    """)
+    assert [v[0] for v in bad] == ["M0 written outside inline assembly",
+                                   "LDS-DMA load without an inline-assembly M0 write before it"]
+
+
+def test_m0_checker_rejects_a_load_with_no_write_before_it():
+    n, bad = _check_m0(f"""
+        {LOAD}
+        {SETLOAD}
+    """)
+    assert len(bad) == 1 and "without an inline-assembly M0 write" in bad[0][0]
+
+
+def test_m0_checker_follows_every_path():
+    # one path reaches the load through the inline-assembly write, the other
+    # does not write M0 at all
+    n, bad = _check_m0(f"""
+        s_cbranch_scc1 .LBB0_2
+        {SETLOAD}
+        .LBB0_2:
+        {LOAD}
+    """)
+    assert len(bad) == 1
+    n, bad = _check_m0(f"""
+        {SETLOAD}
+        .LBB0_1:
+        {LOAD}
+        s_cbranch_scc1 .LBB0_1
+    """)
+    assert bad == []
+
+
 @pytest.fixture(scope="module")
 def gemm_asm():
     try:
@@ -124,3 +182,16 @@ def test_mfma16_kernels_keep_the_inline_asm_rules(gemm_asm):
         assert bad == [], f"{sym}: {bad[:5]}"
         checked += n_asm
     assert checked > 0, "no inline-asm MFMA found: the check would be vacuous"
+
+
+def test_gemm_kernels_write_m0_only_in_inline_asm(gemm_asm):
+    """The grouped buffer loads of gemm_m16_kernel rely on the compiler never
+    writing M0: checked on every GEMM kernel of the library's build."""
+    checked = 0
+    for sym, lines in asm_rules.functions(gemm_asm):
+        if "gemm" not in sym:
+            continue
+        n, bad = asm_rules.check_m0(lines)
+        assert bad == [], f"{sym}: {bad[:5]}"
+        checked += n
+    assert checked > 0, "no LDS-DMA load found: the check would be vacuous"
