@@ -346,16 +346,18 @@ def test_workload_graph_of_calls_over_buffer_sets(wid):
         plan.close()
 
 
-def test_workload2_staged_one_call_graphs_over_buffer_sets():
-    """Workload 2 staged (pvalue 2, two slots) in the form its steps are
-    timed: one HIP graph per buffer set, each holding one staged call, the
-    graphs replayed in turn.  Every set has its own inputs; every replay of
-    every set matches the oracle and an eager call bit for bit."""
-    w = I.WORKLOADS[2]
+@pytest.mark.parametrize("wid", [2, 4])
+def test_staged_one_call_graphs_over_buffer_sets(wid):
+    """Workloads 2 and 4 staged (pvalue 2, two slots) in the form their
+    steps are timed: one HIP graph per buffer set, each holding one staged
+    call, the graphs replayed in turn.  Every set has its own inputs; every
+    replay of every set matches an eager call bit for bit, and the oracle
+    (workload 2 in full, workload 4 on two rows of every 256-row block)."""
+    w = I.WORKLOADS[wid]
     nsets = 4
     host, sets = [], []
     for i in range(nsets):
-        shards, B = I.make_inputs(w, seed_base=5100 + i)
+        shards, B = I.make_inputs(w, seed_base=5100 + 10 * wid + i)
         host.append((shards, B))
         sets.append(([to_device(x, w.dtype) for x in shards], to_device(B, w.dtype),
                      torch.empty((w.m, w.n_local), dtype=torch_dtype(w.dtype), device="cuda")))
@@ -385,7 +387,8 @@ def test_workload2_staged_one_call_graphs_over_buffer_sets():
             for i, ((shards, B), (_, _, C)) in enumerate(zip(host, sets)):
                 assert np.array_equal(to_bits(C), eager[i]), f"replay {rep}, set {i}"
                 if rep == 0:
-                    check_against_oracle(w, shards, B, C)
+                    check_against_oracle(w, shards, B, C,
+                                         rows=None if wid == 2 else block_rows(w.m, seed=i))
         del graphs
     finally:
         plan.close()
