@@ -976,8 +976,14 @@ int run_staged(agmm_plan* p, const Call& c, const void* const* shards, const voi
     if (err != hipSuccess) rc = hip_err(err, "hipStreamWaitEvent");
   }
   if (rc == AGMM_OK) rc = staged_chunks(p, c, shards, B, C, gathered, alt, local_first);
-  // join whatever was enqueued, also after an error
-  const int rj = join_from(c, p->copy_stream, p->ev_side);
+  // Join whatever was enqueued, also after an error.  After a complete chunk
+  // loop an eager call needs no join of the copy stream: its work is the
+  // chunk copies in order, and the last chunk's GEMM (on the caller's
+  // stream, or on the second GEMM stream joined below) waited for the last
+  // copy's `ready` event; one cross-stream wait fewer per call.  Under graph
+  // capture every forked stream is joined explicitly.
+  const bool copies_awaited = rc == AGMM_OK && p->L.num_chunks >= 1 && !c.capturing;
+  const int rj = copies_awaited ? AGMM_OK : join_from(c, p->copy_stream, p->ev_side);
   const int rj2 = alt ? join_from(c, p->compute2, p->ev_c2) : AGMM_OK;
   if (rc != AGMM_OK) return rc;
   return rj != AGMM_OK ? rj : rj2;
