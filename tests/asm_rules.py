@@ -205,7 +205,7 @@ def check_m0(lines):
                     violations.append(("M0 written outside inline assembly", body))
                 ours = inl
                 continue
-            if inl and re.match(r"(?:buffer|global)_load_\w+ .*\blds$", body):
+            if inl and re.match(r"(?:global_load_lds_\w+\s|buffer_load_\w+ .*\blds$)", body):
                 if record:
                     relying += 1
                     if not ours:

@@ -135,6 +135,13 @@ def test_m0_checker_rejects_a_load_with_no_write_before_it():
         {SETLOAD}
     """)
     assert len(bad) == 1 and "without an inline-assembly M0 write" in bad[0][0]
+    # the flat form of the DMA load too
+    n, bad = _check_m0("""
+        ;;#ASMSTART
+        global_load_lds_dwordx4 v[2:3], off offset:1024
+        ;;#ASMEND
+    """)
+    assert n == 1 and len(bad) == 1
 
 
 def test_m0_checker_follows_every_path():
@@ -156,21 +163,26 @@ def test_m0_checker_follows_every_path():
     assert bad == []
 
 
-@pytest.fixture(scope="module")
-def gemm_asm():
+def _device_asm(source):
     try:
         hipcc = _build.hipcc()
     except RuntimeError:
         pytest.skip("hipcc not available")
-    src = os.path.join(_build.CSRC, "gemm_mfma.hip")
+    src = os.path.join(_build.CSRC, source)
     with tempfile.TemporaryDirectory(prefix="agmm_asm_") as tmp:
-        out = os.path.join(tmp, "gemm_mfma.s")
-        cmd = [hipcc, *_build.COMMON, *_build.SOURCES["gemm_mfma.hip"], "--cuda-device-only", "-S",
+        out = os.path.join(tmp, os.path.splitext(source)[0] + ".s")
+        cmd = [hipcc, *_build.COMMON, *_build.SOURCES[source], "--cuda-device-only", "-S",
                "-o", out, src]
         res = subprocess.run(cmd, capture_output=True, text=True)
         assert res.returncode == 0, res.stderr[-2000:]
         with open(out) as f:
-            yield f.read()
+            return f.read()
+
+
+@pytest.fixture(scope="module")
+def gemm_asm():
+    return _device_asm("gemm_mfma.hip")
+
 
 
 def test_mfma16_kernels_keep_the_inline_asm_rules(gemm_asm):
@@ -195,3 +207,4 @@ def test_gemm_kernels_write_m0_only_in_inline_asm(gemm_asm):
         assert bad == [], f"{sym}: {bad[:5]}"
         checked += n
     assert checked > 0, "no LDS-DMA load found: the check would be vacuous"
+
