@@ -971,7 +971,11 @@ int run_staged(agmm_plan* p, const Call& c, const void* const* shards, const voi
   const bool alt = p->s.gemm_streams == 2 && p->L.splits_used == 1 && (p->L.num_chunks > 1 || local_first);
   int rc = fork_to(p, c, p->copy_stream);
   if (rc != AGMM_OK) return rc;
-  if (alt) {
+  // The second GEMM stream needs no wait on the call's entry in an eager
+  // call: each GEMM it runs first waits for its chunk's `ready` event, which
+  // the copy stream records after its own wait on the entry.  Under graph
+  // capture it is forked from the caller's stream explicitly.
+  if (alt && c.capturing) {
     const hipError_t err = hipStreamWaitEvent(p->compute2, p->ev_entry, 0);
     if (err != hipSuccess) rc = hip_err(err, "hipStreamWaitEvent");
   }
