@@ -149,3 +149,34 @@ def test_validate_follows_the_header_rules():
             assert agmm.agmm_last_error() == ""
 
     check()
+
+
+def test_status_is_per_thread():
+    """The header's status rule on the CPU: each host thread reads the
+    status and message of its own most recent call, whatever other threads
+    do meanwhile (8 threads alternating accepted and rejected problems)."""
+    import threading
+    lib = agmm.load_library()
+    errors = []
+    start = threading.Barrier(8)
+
+    def worker(i):
+        try:
+            start.wait()
+            for it in range(2000):
+                bad = (i + it) % 2 == 0
+                st = lib.agmm_plan_validate(2, 4, 8, 8, 7 if bad else 0, 0)
+                want = agmm.AGMM_ERR_INVALID_ARG if bad else agmm.AGMM_OK
+                got_st, got_msg = lib.agmm_last_status(), lib.agmm_last_error().decode()
+                if st != want or got_st != want or (bad != ("unknown dtype 7" in got_msg)) or (not bad and got_msg):
+                    errors.append((i, it, st, got_st, got_msg))
+                    return
+        except Exception as e:   # pragma: no cover - reported below
+            errors.append((i, repr(e)))
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(8)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert errors == []
